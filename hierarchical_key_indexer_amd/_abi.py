@@ -1,0 +1,167 @@
+"""ctypes binding of the LSA indexer's C ABI (include/lsa.h).
+
+Argument marshalling only: every step of the indexer runs in the HIP kernels
+of ``liblsa.so``.  PyTorch supplies device memory and streams.  If the shared
+library is missing, loading raises at once; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LSA_LIBRARY", os.path.join(HERE, "liblsa.so"))
+
+LSA_OK, LSA_ERR_INVALID_ARG, LSA_ERR_UNSUPPORTED, LSA_ERR_BUFFER_TOO_SMALL, LSA_ERR_BAD_INDEX, LSA_ERR_HIP = range(6)
+LSA_F32, LSA_BF16 = 0, 1
+LSA_BEAM_PER_PARENT, LSA_BEAM_GLOBAL = 0, 1
+DTYPES = {"f32": LSA_F32, "bf16": LSA_BF16}
+BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
+
+EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
+           "lsa_select_workspace_bytes", "lsa_select", "lsa_flat_workspace_bytes", "lsa_flat_select",
+           "lsa_last_error", "lsa_abi_version")
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("n_keys", ctypes.c_int64), ("n_kv_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("key_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32),
+                ("n_levels", ctypes.c_int32), ("fanout", ctypes.c_int32 * 4), ("kmeans_iters", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+    @staticmethod
+    def make(n_keys, n_kv_heads, d_head, d_latent, key_dtype, latent_dtype, fanout, kmeans_iters, seed):
+        f = list(fanout) + [0] * (4 - len(fanout))
+        return IndexDesc(n_keys, n_kv_heads, d_head, d_latent, DTYPES.get(key_dtype, key_dtype),
+                         DTYPES.get(latent_dtype, latent_dtype), len(fanout), (ctypes.c_int32 * 4)(*f),
+                         kmeans_iters, seed)
+
+    @staticmethod
+    def of(wl) -> "IndexDesc":
+        return IndexDesc.make(wl.n_keys, wl.n_kv_heads, wl.d_head, wl.d_latent, wl.key_dtype, wl.latent_dtype,
+                              wl.fanout, wl.kmeans_iters, wl.seed)
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int32), ("k", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("beam", ctypes.c_int32)]
+
+    @staticmethod
+    def make(b, k, sink, window, beam="per_parent"):
+        return SelectParams(b, k, sink, window, BEAMS.get(beam, beam))
+
+
+class LsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"lsa error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblsa.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with hierarchical_key_indexer_amd.build_lib.build()")
+    lib = ctypes.CDLL(path)
+    P, SZ, I32, VP = ctypes.POINTER, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p
+    D, S = P(IndexDesc), P(SelectParams)
+    lib.lsa_index_bytes.argtypes, lib.lsa_index_bytes.restype = [D], SZ
+    lib.lsa_build_workspace_bytes.argtypes, lib.lsa_build_workspace_bytes.restype = [D], SZ
+    lib.lsa_build_index.argtypes = [D, VP, VP, VP, SZ, VP, SZ, VP]
+    lib.lsa_build_index.restype = ctypes.c_int
+    lib.lsa_select_out_width.argtypes, lib.lsa_select_out_width.restype = [S], I32
+    lib.lsa_select_workspace_bytes.argtypes, lib.lsa_select_workspace_bytes.restype = [D, S, I32, I32], SZ
+    lib.lsa_flat_workspace_bytes.argtypes, lib.lsa_flat_workspace_bytes.restype = [D, S, I32, I32], SZ
+    lib.lsa_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
+    lib.lsa_select.restype = ctypes.c_int
+    lib.lsa_flat_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, SZ, VP]
+    lib.lsa_flat_select.restype = ctypes.c_int
+    lib.lsa_last_error.argtypes, lib.lsa_last_error.restype = [], ctypes.c_char_p
+    lib.lsa_abi_version.argtypes, lib.lsa_abi_version.restype = [], I32
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().lsa_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != LSA_OK:
+        raise LsaError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None stays NULL)."""
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---- size queries ------------------------------------------------------------
+
+def index_bytes(desc: IndexDesc) -> int:
+    n = load().lsa_index_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def build_workspace_bytes(desc: IndexDesc) -> int:
+    n = load().lsa_build_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def select_out_width(params: SelectParams) -> int:
+    return load().lsa_select_out_width(ctypes.byref(params))
+
+
+def select_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:
+    n = load().lsa_select_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), n_tokens, n_q_heads)
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def flat_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:
+    n = load().lsa_flat_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), n_tokens, n_q_heads)
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+# ---- entry points (raw pointers) --------------------------------------------
+
+def lsa_build_index(desc, keys, W, index, workspace, stream=None) -> None:
+    """keys [N, Hkv, d] (fp32 or bf16), W [Hkv, d, dl] fp32, index/workspace
+    uint8 tensors on the GPU."""
+    _check(load().lsa_build_index(ctypes.byref(desc), _ptr(keys), _ptr(W), _ptr(index), index.numel(),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def lsa_select(desc, index, queries, q_pos, params, out_idx, out_scores=None, out_leaves=None, workspace=None,
+               stream=None) -> None:
+    t, hq = queries.shape[0], queries.shape[1]
+    _check(load().lsa_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
+                             ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(out_leaves),
+                             _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def lsa_flat_select(desc, index, queries, q_pos, params, out_idx, out_scores=None, workspace=None,
+                    stream=None) -> None:
+    t, hq = queries.shape[0], queries.shape[1]
+    _check(load().lsa_flat_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
+                                  ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream(stream)))

@@ -1,0 +1,185 @@
+// The C ABI of include/lsa.h: argument validation (always before any HIP
+// call), workspace sizing and dispatch to the build / select launchers.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "lsa_internal.h"
+
+namespace lsa {
+size_t build_workspace_bytes(const lsa_index_desc& d);
+}
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+int check_desc(const lsa_index_desc* d) {
+  if (!d) return fail(LSA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->n_keys < 1 || d->n_keys >= (int64_t(1) << 31))
+    return fail(LSA_ERR_UNSUPPORTED, "n_keys = %lld outside [1, 2^31)", (long long)d->n_keys);
+  if (d->n_kv_heads < 1 || d->n_kv_heads > 1024)
+    return fail(LSA_ERR_UNSUPPORTED, "n_kv_heads = %d outside [1, 1024]", d->n_kv_heads);
+  if (d->d_head != 64 && d->d_head != 128 && d->d_head != 256)
+    return fail(LSA_ERR_UNSUPPORTED, "d_head = %d not in {64, 128, 256}", d->d_head);
+  if (d->d_latent != 32 && d->d_latent != 64)
+    return fail(LSA_ERR_UNSUPPORTED, "d_latent = %d not in {32, 64}", d->d_latent);
+  if ((d->key_dtype != LSA_F32 && d->key_dtype != LSA_BF16) ||
+      (d->latent_dtype != LSA_F32 && d->latent_dtype != LSA_BF16))
+    return fail(LSA_ERR_UNSUPPORTED, "dtype codes must be LSA_F32 or LSA_BF16");
+  if (d->n_levels < 1 || d->n_levels > 4) return fail(LSA_ERR_UNSUPPORTED, "n_levels = %d outside [1, 4]", d->n_levels);
+  int64_t prod = 1;
+  for (int l = 0; l < d->n_levels; ++l) {
+    if (d->fanout[l] < 2 || d->fanout[l] > 256)
+      return fail(LSA_ERR_UNSUPPORTED, "fanout[%d] = %d outside [2, 256]", l, d->fanout[l]);
+    if (l == d->n_levels - 1 && prod > 65535)
+      return fail(LSA_ERR_UNSUPPORTED, "more than 65535 nodes above the leaf level");
+    prod *= d->fanout[l];
+    if (prod > (int64_t(1) << 22)) return fail(LSA_ERR_UNSUPPORTED, "product of fanouts exceeds 2^22");
+  }
+  if (d->kmeans_iters < 0 || d->kmeans_iters > 1000)
+    return fail(LSA_ERR_UNSUPPORTED, "kmeans_iters = %d outside [0, 1000]", d->kmeans_iters);
+  const double bytes = (double)d->n_keys * d->n_kv_heads * d->d_head * 4.0;
+  if (bytes > 4.0e12) return fail(LSA_ERR_UNSUPPORTED, "index too large");
+  return LSA_OK;
+}
+
+int check_params(const lsa_index_desc* d, const lsa_select_params* p, bool flat) {
+  if (!p) return fail(LSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->k < 1 || p->k > lsa::kMaxK) return fail(LSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", p->k, lsa::kMaxK);
+  if (p->sink < 0 || p->window < 0) return fail(LSA_ERR_INVALID_ARG, "sink and window must be >= 0");
+  if ((int64_t)p->sink + p->k + p->window > (int64_t(1) << 30)) return fail(LSA_ERR_UNSUPPORTED, "row width too large");
+  if (flat) return LSA_OK;
+  if (p->beam != LSA_BEAM_PER_PARENT && p->beam != LSA_BEAM_GLOBAL)
+    return fail(LSA_ERR_INVALID_ARG, "beam = %d is not an lsa_beam", p->beam);
+  if (p->b < 1) return fail(LSA_ERR_INVALID_ARG, "b = %d must be >= 1", p->b);
+  if (p->beam == LSA_BEAM_PER_PARENT) {
+    int64_t cap = 1;
+    for (int l = 0; l < d->n_levels; ++l) {
+      if (p->b > d->fanout[l]) return fail(LSA_ERR_UNSUPPORTED, "b = %d exceeds fanout[%d] = %d", p->b, l, d->fanout[l]);
+      cap *= p->b;
+    }
+    if (cap > lsa::kMaxLeaves) return fail(LSA_ERR_UNSUPPORTED, "b^n_levels = %lld exceeds %d", (long long)cap, lsa::kMaxLeaves);
+  } else if (p->b > 64) {
+    return fail(LSA_ERR_UNSUPPORTED, "global beam supports b <= 64");
+  }
+  return LSA_OK;
+}
+
+int check_shape(const lsa_index_desc* d, int32_t T, int32_t Hq, bool flat) {
+  if (T < 0) return fail(LSA_ERR_INVALID_ARG, "n_tokens = %d < 0", T);
+  if (Hq < 1 || Hq % d->n_kv_heads != 0)
+    return fail(LSA_ERR_INVALID_ARG, "n_q_heads = %d is not a positive multiple of n_kv_heads = %d", Hq, d->n_kv_heads);
+  const int G = Hq / d->n_kv_heads;
+  if (flat && G != 1 && G != 2 && G != 4)
+    return fail(LSA_ERR_UNSUPPORTED, "flat scan supports 1, 2 or 4 query heads per KV head (got %d)", G);
+  if (Hq > 65535) return fail(LSA_ERR_UNSUPPORTED, "n_q_heads = %d exceeds 65535", Hq);
+  if ((int64_t)T * Hq > (int64_t(1) << 30)) return fail(LSA_ERR_UNSUPPORTED, "too many query heads");
+  return LSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_last_error(void) { return g_err; }
+
+int32_t lsa_abi_version(void) { return 1; }
+
+size_t lsa_index_bytes(const lsa_index_desc* desc) {
+  clear_err();
+  if (check_desc(desc) != LSA_OK) return 0;
+  return lsa::compute_layout(*desc).total;
+}
+
+size_t lsa_build_workspace_bytes(const lsa_index_desc* desc) {
+  clear_err();
+  if (check_desc(desc) != LSA_OK) return 0;
+  return lsa::build_workspace_bytes(*desc);
+}
+
+int lsa_build_index(const lsa_index_desc* desc, const void* keys, const float* W, void* index, size_t index_bytes,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc != LSA_OK) return rc;
+  if (!keys || !W || !index || !workspace) return fail(LSA_ERR_INVALID_ARG, "keys, W, index and workspace must be non-NULL");
+  const size_t need_i = lsa::compute_layout(*desc).total;
+  if (index_bytes < need_i)
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "index buffer has %zu bytes, %zu needed", index_bytes, need_i);
+  const size_t need_w = lsa::build_workspace_bytes(*desc);
+  if (workspace_bytes < need_w)
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, need_w);
+  char err[256] = {0};
+  rc = lsa::launch_build(*desc, keys, W, index, workspace, (hipStream_t)stream, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
+int32_t lsa_select_out_width(const lsa_select_params* params) {
+  clear_err();
+  if (!params) return fail(LSA_ERR_INVALID_ARG, "params is NULL"), -1;
+  return params->sink + params->k + params->window;
+}
+
+size_t lsa_select_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                                  int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) || check_params(desc, params, false) || check_shape(desc, n_tokens, n_q_heads, false)) return 0;
+  return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false).bytes;
+}
+
+size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                                int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) || check_params(desc, params, true) || check_shape(desc, n_tokens, n_q_heads, true)) return 0;
+  return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, true).bytes;
+}
+
+static int select_common(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+                         int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+                         float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes,
+                         void* stream, bool flat) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc == LSA_OK) rc = check_params(desc, params, flat);
+  if (rc == LSA_OK) rc = check_shape(desc, n_tokens, n_q_heads, flat);
+  if (rc != LSA_OK) return rc;
+  if (n_tokens == 0) return LSA_OK;
+  if (!index || !queries || !q_pos || !out_idx || !workspace)
+    return fail(LSA_ERR_INVALID_ARG, "index, queries, q_pos, out_idx and workspace must be non-NULL");
+  const lsa::SelectPlan plan = lsa::plan_select(*desc, *params, n_tokens, n_q_heads, flat);
+  if (workspace_bytes < plan.bytes)
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
+  char err[256] = {0};
+  rc = lsa::launch_select(*desc, *params, plan, index, queries, q_pos, n_tokens, n_q_heads, out_idx, out_scores,
+                          out_leaves, workspace, (hipStream_t)stream, flat, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
+int lsa_select(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+               int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+               float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(desc, index, queries, q_pos, n_tokens, n_q_heads, params, out_idx, out_scores, out_leaves,
+                       workspace, workspace_bytes, stream, false);
+}
+
+int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+                    int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+                    float* out_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(desc, index, queries, q_pos, n_tokens, n_q_heads, params, out_idx, out_scores, nullptr,
+                       workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,277 @@
+// Device-side building blocks of the LSA indexer for gfx950 (wave64).
+//
+//  * number formats: bf16 <-> fp32 (round to nearest even), order-preserving
+//    uint32 image of an fp32 score;
+//  * rank keys: a 64-bit key (order(score) << 32 | ~index) whose unsigned
+//    order is "higher score first, then lower index first", so the best-k
+//    set is unique and a radix select over the keys reproduces the tie rule
+//    (score descending, index ascending);
+//  * block primitives (exclusive scan, the radix-select compaction of an LDS
+//    buffer to its k largest keys, bitonic sort);
+//  * the streaming top-k buffer used by the gather, merge and flat kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+typedef uint16_t bf16_t;
+typedef unsigned long long u64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float round_to_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
+
+// Unsigned image of an fp32 value that preserves order; -0 is folded into +0.
+__device__ __forceinline__ uint32_t order_u32(float s) {
+  uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_u32_to_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Valid rank keys are never 0 (order_u32 of any non-NaN float is > 0x007FFFFF),
+// so 0 marks an absent entry.
+__device__ __forceinline__ u64 rank_key(float s, int32_t idx) {
+  return ((u64)order_u32(s) << 32) | (u64)(~(uint32_t)idx);
+}
+__device__ __forceinline__ int32_t rank_key_index(u64 k) { return (int32_t)(~(uint32_t)k); }
+__device__ __forceinline__ float rank_key_score(u64 k) { return order_u32_to_f32((uint32_t)(k >> 32)); }
+
+// ---------------------------------------------------------------------------
+// latent rows: loads of 16 bytes and their dot product with a query slice
+// ---------------------------------------------------------------------------
+
+template <typename LT> struct Lat;
+template <> struct Lat<float> {
+  static constexpr int PER16 = 4;     // elements per 16 bytes
+  __device__ static __forceinline__ float dot16(const uint4& v, const float* q) {
+    float acc = __uint_as_float(v.x) * q[0];
+    acc = fmaf(__uint_as_float(v.y), q[1], acc);
+    acc = fmaf(__uint_as_float(v.z), q[2], acc);
+    acc = fmaf(__uint_as_float(v.w), q[3], acc);
+    return acc;
+  }
+  __device__ static __forceinline__ float get(const float* row, int i) { return row[i]; }
+};
+template <> struct Lat<bf16_t> {
+  static constexpr int PER16 = 8;
+  __device__ static __forceinline__ float dot16(const uint4& v, const float* q) {
+    float acc = __uint_as_float(v.x << 16) * q[0];
+    acc = fmaf(__uint_as_float(v.x & 0xFFFF0000u), q[1], acc);
+    acc = fmaf(__uint_as_float(v.y << 16), q[2], acc);
+    acc = fmaf(__uint_as_float(v.y & 0xFFFF0000u), q[3], acc);
+    acc = fmaf(__uint_as_float(v.z << 16), q[4], acc);
+    acc = fmaf(__uint_as_float(v.z & 0xFFFF0000u), q[5], acc);
+    acc = fmaf(__uint_as_float(v.w << 16), q[6], acc);
+    acc = fmaf(__uint_as_float(v.w & 0xFFFF0000u), q[7], acc);
+    return acc;
+  }
+  __device__ static __forceinline__ float get(const bf16_t* row, int i) { return bf16_to_f32(row[i]); }
+};
+
+// Sum over aligned groups of G lanes (G in {2,4,8,16,32}); every lane of the
+// group receives the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// wave / block primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ u64 wave_max_u64(u64 v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    u64 o = __shfl_xor(v, m, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t mbcnt64(u64 mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Exclusive prefix sum of one int per thread over the block; *total gets the
+// block sum.  `wsum` is LDS scratch of BLOCK/64 ints.  Contains barriers.
+template <int BLOCK>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < BLOCK / 64; ++i) {
+    int s = wsum[i];
+    base += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+// LDS scratch of the radix select.
+struct RadixScratch {
+  uint32_t hist[256];
+  int wsum[16];
+  int digit;
+  uint32_t above;
+  uint32_t hd;
+};
+
+// Keep the k largest nonzero keys of buf[0..n) (n <= BLOCK*M, k < n, keys
+// unique) in buf[0..k), in no particular order.  Returns a value t such that
+// every kept key is >= t and every dropped key is < t (so a future key can
+// only belong to the best k if it is > t).  MSB-first radix select, 8 bits
+// per pass, on keys held in registers.  All threads of the block must call.
+template <int BLOCK, int M>
+__device__ u64 topk_compact(u64* buf, int n, int k, RadixScratch* sc) {
+  u64 v[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int i = threadIdx.x + j * BLOCK;
+    v[j] = (i < n) ? buf[i] : 0ull;
+  }
+  u64 prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += BLOCK) sc->hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&sc->hist[(uint32_t)(v[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const uint32_t h0 = sc->hist[4 * l], h1 = sc->hist[4 * l + 1], h2 = sc->hist[4 * l + 2],
+                     h3 = sc->hist[4 * l + 3];
+      const uint32_t s = h0 + h1 + h2 + h3;
+      uint32_t incl = s;  // sum over lanes >= l
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        uint32_t o = __shfl_down(incl, off, 64);
+        if (l + off < 64) incl += o;
+      }
+      const uint32_t above = incl - s;
+      if (above < need && need <= incl) {
+        uint32_t acc = above;
+        int d;
+        uint32_t hd;
+        if (acc + h3 >= need) { d = 4 * l + 3; hd = h3; }
+        else if ((acc += h3) + h2 >= need) { d = 4 * l + 2; hd = h2; }
+        else if ((acc += h2) + h1 >= need) { d = 4 * l + 1; hd = h1; }
+        else { acc += h1; d = 4 * l; hd = h0; }
+        sc->digit = d;
+        sc->above = acc;
+        sc->hd = hd;
+      }
+    }
+    __syncthreads();
+    const int d = sc->digit;
+    need -= sc->above;
+    const uint32_t hd = sc->hd;
+    prefix |= (u64)d << shift;
+    mask |= 0xFFull << shift;
+    __syncthreads();
+    if (hd == need) break;
+  }
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) mine += (v[j] != 0ull && (v[j] & mask) >= prefix) ? 1 : 0;
+  int total;
+  int pos = block_exclusive_scan<BLOCK>(mine, sc->wsum, &total);
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+    if (v[j] != 0ull && (v[j] & mask) >= prefix) buf[pos++] = v[j];
+  __syncthreads();
+  return prefix;
+}
+
+// Sort buf[0..n) ascending (n <= cap, cap a power of two); slots n..cap-1 are
+// filled with ~0.  Block-wide bitonic sort in LDS.
+template <int BLOCK>
+__device__ void bitonic_sort_asc(u64* buf, int n, int cap) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  if (p > cap) p = cap;
+  for (int i = n + threadIdx.x; i < p; i += BLOCK) buf[i] = ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= p; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (p >> 1); t += BLOCK) {
+        const int i = 2 * stride * (t / stride) + (t % stride);
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const u64 a = buf[i], b = buf[j];
+        if ((a > b) == up) {
+          buf[i] = b;
+          buf[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Write one output row from the n (<= k) rank keys in buf: sink positions,
+// the keys in ascending index order with their scores, the window positions.
+// Uses buf as sort space (capacity cap >= next power of two of n).
+template <int BLOCK>
+__device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
+                                    int32_t* row, float* scores_row) {
+  // re-key as (index << 32 | order(score)) so an ascending sort orders by index
+  for (int i = threadIdx.x; i < n; i += BLOCK) {
+    const u64 key = buf[i];
+    buf[i] = ((u64)(uint32_t)rank_key_index(key) << 32) | (key >> 32);
+  }
+  __syncthreads();
+  bitonic_sort_asc<BLOCK>(buf, n, cap);
+  for (int i = threadIdx.x; i < k; i += BLOCK) {
+    if (i < n) {
+      const u64 key = buf[i];
+      row[sink + i] = (int32_t)(key >> 32);
+      if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
+    } else {
+      row[sink + i] = -1;
+      if (scores_row) scores_row[i] = -__builtin_huge_valf();
+    }
+  }
+  const int ns = min(sink, p + 1);
+  for (int i = threadIdx.x; i < sink; i += BLOCK) row[i] = i < ns ? i : -1;
+  const int w0 = max(sink, p - window + 1);
+  const int nw = p - w0 + 1;
+  for (int i = threadIdx.x; i < window; i += BLOCK) row[sink + k + i] = i < nw ? w0 + i : -1;
+}
+
+// A row for a query whose position is outside [0, N): all -1.
+template <int BLOCK>
+__device__ void write_invalid_row(int width, int k, int32_t* row, float* scores_row) {
+  for (int i = threadIdx.x; i < width; i += BLOCK) row[i] = -1;
+  if (scores_row)
+    for (int i = threadIdx.x; i < k; i += BLOCK) scores_row[i] = -__builtin_huge_valf();
+}
+
+}  // namespace lsa

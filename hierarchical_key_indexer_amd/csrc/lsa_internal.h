@@ -1,0 +1,90 @@
+// Host-side internals shared by the ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdio.h>
+#include <string.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+constexpr int kMaxLevels = 4;
+constexpr size_t kAlign = 256;
+constexpr int kMaxLeaves = 4096;   // b^L (or b) cap of a query's leaf list
+constexpr int kMaxK = 4096;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Byte offsets of the index blob sections (the layout lsa.h specifies).
+struct Layout {
+  size_t W = 0, perm = 0, latent = 0, total = 0;
+  size_t cent[kMaxLevels] = {0, 0, 0, 0};
+  size_t cscore[kMaxLevels] = {0, 0, 0, 0};
+  size_t offsets[kMaxLevels] = {0, 0, 0, 0};
+  int64_t nodes[kMaxLevels + 1] = {1, 0, 0, 0, 0};   // nodes[l] = P_l, nodes[0] = 1
+};
+
+inline int latent_elem_bytes(const lsa_index_desc& d) { return d.latent_dtype == LSA_BF16 ? 2 : 4; }
+inline int key_elem_bytes(const lsa_index_desc& d) { return d.key_dtype == LSA_BF16 ? 2 : 4; }
+
+inline Layout compute_layout(const lsa_index_desc& d) {
+  Layout L;
+  const int64_t hk = d.n_kv_heads, n = d.n_keys, dl = d.d_latent, dh = d.d_head;
+  const int ls = latent_elem_bytes(d);
+  for (int l = 1; l <= d.n_levels; ++l) L.nodes[l] = L.nodes[l - 1] * d.fanout[l - 1];
+  size_t cur = 256;
+  auto put = [&](size_t& off, size_t bytes) {
+    off = cur;
+    cur = align_up(cur + bytes);
+  };
+  put(L.W, (size_t)(hk * dh * dl * 4));
+  for (int l = 1; l <= d.n_levels; ++l) put(L.cent[l - 1], (size_t)(hk * L.nodes[l] * dl * 4));
+  for (int l = 1; l <= d.n_levels; ++l) put(L.cscore[l - 1], (size_t)(hk * L.nodes[l] * dl * ls));
+  for (int l = 1; l <= d.n_levels; ++l) put(L.offsets[l - 1], (size_t)(hk * (L.nodes[l] + 1) * 4));
+  put(L.perm, (size_t)(hk * n * 4));
+  put(L.latent, (size_t)(hk * n * dl * ls));
+  L.total = cur;
+  return L;
+}
+
+// The 256-byte header, passed by value to the kernel that writes it.
+struct BlobHeader {
+  uint32_t w[64];
+};
+
+// Bump allocator over a caller workspace; with base == nullptr it only sizes.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    size_t off = align_up(used);
+    used = off + count * sizeof(T);
+    return base ? (T*)(base + off) : nullptr;
+  }
+};
+
+// ---- build -----------------------------------------------------------------
+size_t build_workspace_bytes(const lsa_index_desc& d);
+int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void* index, void* ws,
+                 hipStream_t stream, char* err, size_t errlen);
+
+// ---- select ------------------------------------------------------------------
+struct SelectPlan {
+  int64_t qh;          // T * Hq
+  int nl_cap;          // leaf-list capacity per query head
+  int splits;          // workgroups per query head in the gather (1 = direct)
+  int flat_splits;     // workgroups per (token, KV head) in the flat scan
+  size_t bytes;        // workspace bytes
+};
+SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat);
+int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& plan,
+                  const void* index, const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq,
+                  int32_t* out_idx, float* out_scores, int32_t* out_leaves, void* ws, hipStream_t stream,
+                  bool flat, char* err, size_t errlen);
+
+}  // namespace lsa

@@ -1,0 +1,201 @@
+/*
+ * lsa.h -- C ABI of the Latent Sparse Attention (LSA) indexer for AMD MI355X
+ * (gfx950).
+ *
+ * The indexer picks, for every query head of every query token, the cached
+ * keys that sparse attention will read.  Keys are projected into a latent
+ * space and clustered into a bucket hierarchy; a query scores the bucket
+ * centroids level by level, descends into its best buckets, scores the member
+ * keys and keeps the best k, together with the attention-sink tokens and a
+ * local causal window.  (Page "Latent Sparse Attention (LSA): The 72.4x and
+ * 22.7x Speedups, and What They Compare Against", section "How does LSA
+ * work?", steps 1-3; page "Latent Sparse Attention: tree search over keys for
+ * 10M-token context", TL;DR and flowchart.)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers point to GPU memory owned by the
+ *    caller; the library never allocates or frees device memory and never
+ *    synchronises: every call only enqueues work on `stream` (a hipStream_t
+ *    passed as void*, NULL = the null stream) and returns.  Calls are
+ *    therefore capturable in a HIP graph.
+ *  - Every argument is validated on the host before anything is enqueued.
+ *    On any error nothing is enqueued, the status is returned and
+ *    lsa_last_error() describes it.  No call aborts, exits or throws.
+ *  - Status codes: lsa_status.  LSA_ERR_HIP reports a launch failure; faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - Query head hq reads KV head hq / G with G = n_q_heads / n_kv_heads.
+ *  - Dtypes: keys and queries are fp32 or bf16 (the same for both); the
+ *    latent store is fp32 or bf16.  All dot products accumulate in fp32.
+ *
+ * Limits (LSA_ERR_UNSUPPORTED otherwise): 1 <= n_keys < 2^31; n_kv_heads <=
+ * 1024; d_head in {64, 128, 256}; d_latent in {32, 64}; 1 <= n_levels <= 4;
+ * 2 <= fanout <= 256; at most 65535 nodes above the leaf level; product of
+ * fanouts <= 2^22; per-parent beam: b <= fanout at every level and
+ * b^n_levels <= 4096; global beam: b <= 64; 1 <= k <= 4096; n_q_heads <=
+ * 65535; the flat scan needs n_q_heads / n_kv_heads in {1, 2, 4}.  Latent
+ * values must stay below 256 in magnitude (the k-means centroid sums use
+ * 64-bit fixed point).
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSA_OK = 0,
+  LSA_ERR_INVALID_ARG = 1,      /* null pointer, negative size, inconsistent shapes */
+  LSA_ERR_UNSUPPORTED = 2,      /* outside the limits above                          */
+  LSA_ERR_BUFFER_TOO_SMALL = 3, /* index or workspace smaller than required          */
+  LSA_ERR_BAD_INDEX = 4,        /* descriptor does not describe a valid index        */
+  LSA_ERR_HIP = 5               /* a HIP launch failed                               */
+} lsa_status;
+
+typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
+
+/* Beam rule of the descent.  PER_PARENT: every kept node keeps its best b
+ * children (frontier b^l at level l).  GLOBAL: each level keeps the best b
+ * children over the whole frontier. */
+typedef enum { LSA_BEAM_PER_PARENT = 0, LSA_BEAM_GLOBAL = 1 } lsa_beam;
+
+/* Shape of an index.  Filled by the caller; the same descriptor must be
+ * passed to every call on that index (a copy is stored in the blob header). */
+typedef struct {
+  int64_t n_keys;       /* N: cached keys (token positions 0..N-1)               */
+  int32_t n_kv_heads;   /* Hkv                                                   */
+  int32_t d_head;       /* key / query width                                     */
+  int32_t d_latent;     /* latent width                                          */
+  int32_t key_dtype;    /* lsa_dtype of keys and queries                         */
+  int32_t latent_dtype; /* lsa_dtype of latent keys and of the scoring centroids */
+  int32_t n_levels;     /* L                                                     */
+  int32_t fanout[4];    /* F_1..F_L (children per node at each level)            */
+  int32_t kmeans_iters; /* Lloyd (assign, update) rounds per node                */
+  uint64_t seed;        /* seeds the k-means initial centroids                   */
+} lsa_index_desc;
+
+typedef struct {
+  int32_t b;      /* buckets kept per level (per parent, or globally)          */
+  int32_t k;      /* long-range keys kept per query head                       */
+  int32_t sink;   /* attention-sink positions 0..sink-1                        */
+  int32_t window; /* local window: the last `window` positions up to p         */
+  int32_t beam;   /* lsa_beam                                                  */
+} lsa_select_params;
+
+/* ------------------------------------------------------------------------
+ * The index blob: one caller-owned device buffer of lsa_index_bytes(desc)
+ * bytes, little-endian, every section aligned to 256 bytes.
+ *
+ *   header (256 bytes)
+ *     0  char[4]   "LSA1"            4  uint32  version = 1
+ *     8  int64     n_keys
+ *    16  int32     n_kv_heads, d_head, d_latent, key_dtype, latent_dtype,
+ *                  n_levels, fanout[4], kmeans_iters, 0
+ *    64  uint64    seed              72  uint64  total bytes
+ *    80  uint64    offset of W       88  uint64  offset of perm
+ *    96  uint64    offset of latent
+ *   104  uint64[4] offsets of centroids[l]   (0 for absent levels)
+ *   136  uint64[4] offsets of cscore[l]
+ *   168  uint64[4] offsets of offsets[l]
+ *   sections, in this order:
+ *     W            fp32   [Hkv][d_head][d_latent]        the latent map
+ *     centroids[l] fp32   [Hkv][P_l][d_latent]            P_l = F_1*...*F_l
+ *     cscore[l]    latent [Hkv][P_l][d_latent]            scoring copy (RNE)
+ *     offsets[l]   int32  [Hkv][P_l + 1]                  CSR row ranges
+ *     perm         int32  [Hkv][N]                        key index of CSR row
+ *     latent       latent [Hkv][N][d_latent]              row r = key perm[r]
+ *
+ * Node ids: child c of node p at level l has id p*F_l + c (the root is node
+ * 0 of level 0).  Rows [offsets[l][n], offsets[l][n+1]) of a head hold the
+ * keys of node n of level l, in ascending key index within each leaf; the
+ * ranges of a node's children tile the node's range.  A node with no member
+ * is empty: it is never selected.  A child that received no initial centroid
+ * (its parent had fewer members than the fanout) has zero centroids.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the index blob for `desc`; 0 if the descriptor is invalid (then
+ * lsa_last_error() says why). */
+size_t lsa_index_bytes(const lsa_index_desc* desc);
+
+/* Bytes of device workspace lsa_build_index needs; 0 if invalid. */
+size_t lsa_build_workspace_bytes(const lsa_index_desc* desc);
+
+/* Build the index (step 1 of "How does LSA work?": keys are clustered into a
+ * hierarchy of buckets in a latent space).
+ *   keys      device [N][Hkv][d_head], key_dtype (the KV cache's key layout)
+ *   W         device [Hkv][d_head][d_latent] fp32, latent map (copied into
+ *             the blob; queries use the same map)
+ *   index     device, index_bytes >= lsa_index_bytes(desc); fully written
+ *   workspace device, workspace_bytes >= lsa_build_workspace_bytes(desc);
+ *             scratch, contents undefined afterwards
+ * Latent keys are round(K.W) (fp32 accumulation, one RNE rounding to the
+ * latent dtype).  Level l splits every node of level l-1 into F_l children by
+ * Lloyd k-means on the node's own members: seeded initial centroids (distinct
+ * members drawn with splitmix64), kmeans_iters rounds of (assign to the
+ * nearest centroid, ties to the lowest child; move every non-empty centroid
+ * to its members' mean), then a final assignment against the stored
+ * centroids.  Deterministic: the same inputs give the same bytes. */
+int lsa_build_index(const lsa_index_desc* desc, const void* keys, const float* W, void* index,
+                    size_t index_bytes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Width of one output row: sink + k + window. */
+int32_t lsa_select_out_width(const lsa_select_params* params);
+
+/* Bytes of device workspace lsa_select needs for this shape; 0 if invalid. */
+size_t lsa_select_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
+                                  int32_t n_tokens, int32_t n_q_heads);
+
+/* Tree selection (steps 2 and 3 of "How does LSA work?").
+ *   index      device blob written by lsa_build_index (or to the same layout)
+ *   queries    device [T][Hq][d_head], key_dtype
+ *   q_pos      device int32 [T], position p of each query token, 0 <= p < N
+ *              (a row whose position is out of range is written as all -1)
+ *   out_idx    device int32 [T][Hq][sink + k + window]:
+ *                [0, sink)          positions 0..min(sink, p+1)-1, then -1
+ *                [sink, sink+k)     selected long-range keys, ascending, -1 padded
+ *                [sink+k, width)    positions max(sink, p-window+1)..p, then -1
+ *   out_scores device fp32 [T][Hq][k] or NULL: score of each selected key,
+ *              aligned with its slot, -inf padded
+ *   out_leaves device int32 [T][Hq][b^L] (b for GLOBAL) or NULL: the leaf
+ *              buckets the query descended into, -1 padded
+ * The query's latent is round(q.W_h).  Level by level the children of every
+ * kept node are scored by the inner product with their scoring centroid
+ * (empty children never kept) and the best b are kept (ties: lower id).  The
+ * members of the kept leaves whose index lies in [sink, p - window] are
+ * scored by the inner product of latents, and the best k (ties: lower index)
+ * are returned; fewer candidates than k return all of them. */
+int lsa_select(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+               int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+               float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Bytes of device workspace lsa_flat_select needs; 0 if invalid. */
+size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
+                                int32_t n_tokens, int32_t n_q_heads);
+
+/* Full-scan baseline: the indexer that scores every key ("old indexer" of
+ * the flowchart on "Latent Sparse Attention: tree search over keys for
+ * 10M-token context").  Same arguments and output rows as lsa_select, with
+ * every key in [sink, p - window] a candidate; params->b and ->beam are
+ * ignored.  Equal to lsa_select with b = fanout at every level. */
+int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* queries,
+                    const int32_t* q_pos, int32_t n_tokens, int32_t n_q_heads,
+                    const lsa_select_params* params, int32_t* out_idx, float* out_scores,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next lsa_* call on the same thread. */
+const char* lsa_last_error(void);
+
+/* ABI version (1). */
+int32_t lsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

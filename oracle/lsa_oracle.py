@@ -43,6 +43,7 @@ from __future__ import annotations
 import dataclasses
 
 import numpy as np
+import scipy.sparse
 
 # ----------------------------------------------------------------------------
 # number formats
@@ -162,19 +163,33 @@ def kmeans_init_positions(seed: int, head: int, level: int, node: int, m: int, f
 # ----------------------------------------------------------------------------
 
 
-def sq_dists(x: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """Squared Euclidean distances [m, F] in float64."""
-    xx = np.einsum("ij,ij->i", x, x)
-    cc = np.einsum("ij,ij->i", c, c)
-    return xx[:, None] - 2.0 * (x @ c.T) + cc[None, :]
+def sq_dists(x: np.ndarray, c: np.ndarray, xx: np.ndarray | None = None) -> np.ndarray:
+    """Squared Euclidean distances [m, F] in float64: |x|^2 - 2 x.c + |c|^2."""
+    if xx is None:
+        xx = np.einsum("ij,ij->i", x, x)
+    d = x @ c.T
+    d *= -2.0
+    d += np.einsum("ij,ij->i", c, c)[None, :]
+    d += xx[:, None]
+    return d
 
 
-def assign_nearest(x: np.ndarray, c: np.ndarray, chunk: int = 1 << 18) -> np.ndarray:
+def assign_nearest(x: np.ndarray, c: np.ndarray, xx: np.ndarray | None = None, chunk: int = 1 << 16) -> np.ndarray:
     """Index of the nearest centroid for every row; ties -> lowest index."""
+    if xx is None:
+        xx = np.einsum("ij,ij->i", x, x)
     out = np.empty(len(x), dtype=np.int64)
     for lo in range(0, len(x), chunk):
-        out[lo:lo + chunk] = np.argmin(sq_dists(x[lo:lo + chunk], c), axis=1)
+        out[lo:lo + chunk] = np.argmin(sq_dists(x[lo:lo + chunk], c, xx[lo:lo + chunk]), axis=1)
     return out
+
+
+def member_means(x: np.ndarray, a: np.ndarray, n: int):
+    """(counts [n], sums [n, d]) of the rows of x grouped by label a, as the
+    product of the n x m membership (one-hot) matrix with x, in float64."""
+    cnt = np.bincount(a, minlength=n)
+    member = scipy.sparse.csr_matrix((np.ones(len(a)), (a, np.arange(len(a)))), shape=(n, len(a)))
+    return cnt, np.asarray(member @ x)
 
 
 def lloyd(x: np.ndarray, f: int, iters: int, init_pos: list):
@@ -192,12 +207,13 @@ def lloyd(x: np.ndarray, f: int, iters: int, init_pos: list):
     if nv == 0:
         return cent, np.zeros(0, dtype=np.int64), 0
     cent[:nv] = round_f32(x[np.asarray(init_pos)])
+    xx = np.einsum("ij,ij->i", x, x)
     for _ in range(iters):
-        a = assign_nearest(x, cent[:nv])
-        cnt = np.bincount(a, minlength=nv)
-        for c in np.nonzero(cnt)[0]:
-            cent[c] = round_f32(x[a == c].sum(axis=0) / cnt[c])
-    return cent, assign_nearest(x, cent[:nv]), nv
+        a = assign_nearest(x, cent[:nv], xx)
+        cnt, sums = member_means(x, a, nv)
+        nz = cnt > 0
+        cent[:nv][nz] = round_f32(sums[nz] / cnt[nz, None])
+    return cent, assign_nearest(x, cent[:nv], xx), nv
 
 
 def lloyd_objective(x: np.ndarray, cent: np.ndarray, a: np.ndarray) -> float:
@@ -299,16 +315,28 @@ def build_head(lat: np.ndarray, w_h: np.ndarray, desc: IndexDesc, h: int) -> Hea
                      valid=valids, perm=perm, csr_latent=lat[perm], assign=assigns)
 
 
-def build_index(keys: np.ndarray, W: np.ndarray, desc: IndexDesc, heads=None, progress=None) -> OracleIndex:
+def build_index(keys: np.ndarray, W: np.ndarray, desc: IndexDesc, heads=None, progress=None,
+                workers: int = 1) -> OracleIndex:
     """Index of every KV head.  ``keys`` [N, Hkv, d] storage format,
     ``W`` [Hkv, d, d_latent] fp32.  ``heads`` restricts the build to some
-    heads (the others are left as None)."""
+    heads (the others are left as None); ``workers`` builds heads in threads
+    (the heads are independent)."""
     out = [None] * desc.n_kv_heads
-    for h in (range(desc.n_kv_heads) if heads is None else heads):
+    todo = list(range(desc.n_kv_heads) if heads is None else heads)
+
+    def one(h):
         lat = latent_keys(keys[:, h, :], W[h], desc.key_dtype, desc.latent_dtype)
         out[h] = build_head(lat, W[h], desc, h)
         if progress:
             progress(f"oracle index head {h} built")
+
+    if workers > 1 and len(todo) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(min(workers, len(todo))) as ex:
+            list(ex.map(one, todo))
+    else:
+        for h in todo:
+            one(h)
     return OracleIndex(desc=desc, heads=out)
 
 
@@ -384,13 +412,15 @@ def descend(hidx: HeadIndex, fanout: tuple, qlat: np.ndarray, b: int, beam: str)
     return frontier
 
 
-def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectParams, flat: bool = False) -> dict:
+def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectParams, flat: bool = False,
+               leaves=None) -> dict:
     """The whole selection of one query head at position p.
 
     Candidates are the members of the selected leaves (all keys when ``flat``)
     that fall in C(p); each is scored s_j = q~ . k~_j; the top-k by (s desc,
     j asc) are kept ("scores the keys within the selected clusters", Wink
-    Pings).  Fewer than k candidates: all of them.
+    Pings).  Fewer than k candidates: all of them.  ``leaves`` replaces the
+    descent by a given leaf set (the key stage alone).
     """
     hidx = idx.heads[h]
     _, _, (lo, hi) = segments(p, prm.sink, prm.window)
@@ -398,7 +428,9 @@ def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectPa
         leaves = None
         rows = np.arange(len(hidx.perm), dtype=np.int64)
     else:
-        leaves = descend(hidx, idx.desc.fanout, qlat, prm.b, prm.beam)
+        if leaves is None:
+            leaves = descend(hidx, idx.desc.fanout, qlat, prm.b, prm.beam)
+        leaves = np.asarray(leaves, dtype=np.int64)
         off = hidx.offsets[-1]
         rows = (np.concatenate([np.arange(off[c], off[c + 1]) for c in leaves])
                 if len(leaves) else np.zeros(0, dtype=np.int64))
@@ -409,8 +441,9 @@ def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectPa
     order = np.lexsort((j, -s))[:prm.k]
     top_j, top_s = j[order], s[order]
     asc = np.argsort(top_j, kind="stable")
-    return dict(leaves=leaves, cand_idx=j, cand_scores=s, top_idx=top_j[asc], top_scores=top_s[asc],
-                kth=(top_s[-1] if len(top_s) else -np.inf) if len(top_s) == min(prm.k, len(j)) else -np.inf)
+    return dict(leaves=leaves, cand_idx=j, cand_scores=s, cand_scale=dot_scale(qlat, hidx.csr_latent[rows]),
+                top_idx=top_j[asc], top_scores=top_s[asc],
+                kth=top_s[-1] if len(j) > prm.k else -np.inf)
 
 
 def _row(res: dict, p: int, prm: SelectParams):

@@ -1,0 +1,174 @@
+"""Comparison of the HIP path's outputs with the CPU oracle, to the stated
+tolerances.
+
+* scores: |s_gpu - s_ref| <= 1e-3 * sum_i |q~_i k~_i| (fp32 accumulation of a
+  64-term dot product errs by about 4e-6 of that scale, so a failure is a bug);
+* key sets: equal, except for swaps whose oracle score lies within
+  1e-3 * scale of the oracle's k-th score; sink and window segments exact;
+* leaf sets: the GPU's descent must be a valid top-b choice at every level
+  (every kept child scores >= every dropped sibling, up to the same
+  tolerance); key sets are then compared against the oracle's key stage run on
+  the GPU's leaves, so one legitimate near-tie swap cannot cascade.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import lsa_oracle as O
+
+TOL = 1e-3
+
+
+def log(msg: str) -> None:
+    """Progress line that names the running case (flushed at once)."""
+    print(msg, flush=True)
+
+
+def check_leaves(hidx, fanout, qlat, b, beam, gpu_leaves):
+    """The GPU leaf set is a valid descent (per-parent or global top-b at
+    every level, ties up to TOL of the score scale).  Returns the leaf list."""
+    leaves = np.array(sorted(int(x) for x in gpu_leaves if x >= 0), dtype=np.int64)
+    assert len(set(leaves.tolist())) == len(leaves), "duplicate leaves"
+    L = len(fanout)
+    # ancestors of the kept leaves at every level (level L = the leaves)
+    anc = [None] * (L + 1)
+    anc[L] = leaves
+    for lev in range(L - 1, -1, -1):
+        anc[lev] = np.unique(anc[lev + 1] // fanout[lev])
+    assert anc[0].tolist() in ([0], []), "leaves from more than one root"
+    for lev in range(1, L + 1):
+        f = fanout[lev - 1]
+        cnt = np.diff(hidx.offsets[lev - 1])
+        kept = set(anc[lev].tolist())
+        parents = anc[lev - 1]
+        groups = [parents] if beam == "global" else [[p] for p in parents]
+        for grp in groups:
+            kids = np.concatenate([np.arange(p * f, (p + 1) * f) for p in grp])
+            kids = kids[cnt[kids] > 0]
+            sc = hidx.cscore[lev - 1][kids] @ qlat
+            scale = O.dot_scale(qlat, hidx.cscore[lev - 1][kids])
+            mine = np.array([k in kept for k in kids])
+            assert mine.sum() == min(b, len(kids)), f"level {lev}: kept {mine.sum()} of {len(kids)} children, b={b}"
+            if mine.all() or not mine.any():
+                continue
+            worst_kept = np.min(sc[mine] + TOL * scale[mine])
+            best_dropped = np.max(sc[~mine] - TOL * scale[~mine])
+            assert worst_kept >= best_dropped, f"level {lev}: a dropped child beats a kept one beyond tolerance"
+    return leaves
+
+
+def check_row(gpu_row, gpu_scores, res, p, prm: O.SelectParams, what=""):
+    """One output row (and its scores) against the oracle's per-query result
+    ``res`` (from O.select_one on the same leaf set)."""
+    sink, k, window = prm.sink, prm.k, prm.window
+    s, w, _ = O.segments(p, sink, window)
+    assert gpu_row[:sink].tolist() == s + [-1] * (sink - len(s)), f"{what}: sink segment"
+    assert gpu_row[sink + k:].tolist() == w + [-1] * (window - len(w)), f"{what}: window segment"
+    top = np.asarray(gpu_row[sink:sink + k])
+    n_ref = len(res["top_idx"])
+    valid = top[top >= 0]
+    assert len(valid) == n_ref, f"{what}: {len(valid)} selected, oracle {n_ref}"
+    assert np.all(top[n_ref:] == -1), f"{what}: padding"
+    assert np.all(np.diff(valid) > 0), f"{what}: not ascending / duplicates"
+    cand = dict(zip(res["cand_idx"].tolist(), range(len(res["cand_idx"]))))
+    missing = [j for j in valid.tolist() if j not in cand]
+    assert not missing, f"{what}: selected keys outside the candidate set: {missing[:5]}"
+    ci = np.array([cand[j] for j in valid.tolist()], dtype=np.int64)
+    ref_s = res["cand_scores"][ci]
+    scale = res["cand_scale"][ci]
+    if gpu_scores is not None:
+        gs = np.asarray(gpu_scores[:len(valid)], dtype=np.float64)
+        bad = np.abs(gs - ref_s) > TOL * scale
+        assert not bad.any(), f"{what}: {bad.sum()} scores off, e.g. gpu {gs[bad][:3]} ref {ref_s[bad][:3]}"
+        assert np.all(np.isneginf(np.asarray(gpu_scores[len(valid):]))), f"{what}: score padding"
+    g, o = set(valid.tolist()), set(res["top_idx"].tolist())
+    if g != o:
+        tau = res["kth"]
+        assert np.isfinite(tau), f"{what}: sets differ with fewer candidates than k"
+        for j in g ^ o:
+            c = cand[j]
+            assert abs(res["cand_scores"][c] - tau) <= TOL * res["cand_scale"][c], \
+                f"{what}: key {j} differs (score {res['cand_scores'][c]}, k-th {tau})"
+    return len(g ^ o)
+
+
+def compare_select(oidx, queries, q_pos, prm, gpu_idx, gpu_scores, gpu_leaves=None, pairs=None, flat=False,
+                   log=None):
+    """Compare GPU rows with the oracle for the given (t, hq) pairs (all by
+    default).  Returns the number of tolerated near-tie swaps."""
+    desc = oidx.desc
+    T, Hq = queries.shape[0], queries.shape[1]
+    g = Hq // desc.n_kv_heads
+    pairs = pairs if pairs is not None else [(t, hq) for t in range(T) for hq in range(Hq)]
+    swaps = 0
+    for (t, hq) in pairs:
+        h = hq // g
+        p = int(q_pos[t])
+        qlat = O.query_latent(queries[t, hq], oidx.heads[h], desc.key_dtype, desc.latent_dtype)
+        leaves = None
+        if not flat:
+            if gpu_leaves is not None:
+                leaves = check_leaves(oidx.heads[h], desc.fanout, qlat, prm.b, prm.beam, gpu_leaves[t, hq])
+            else:
+                leaves = None
+        res = O.select_one(oidx, h, qlat, p, prm, flat=flat, leaves=leaves)
+        swaps += check_row(gpu_idx[t, hq], None if gpu_scores is None else gpu_scores[t, hq], res, p, prm,
+                           what=f"(t={t}, hq={hq}, p={p})")
+    if log:
+        log(f"compared {len(pairs)} query heads, {swaps} near-tie swaps")
+    return swaps
+
+
+def csr_from_assignment(leaf_of_key: np.ndarray, n_leaves: int):
+    """CSR of an assignment, by definition: counts, offsets, stable order."""
+    counts = np.bincount(leaf_of_key, minlength=n_leaves)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    perm = np.argsort(leaf_of_key, kind="stable")
+    return offsets, perm
+
+
+def check_build(gidx, keys, W, desc: O.IndexDesc, sample=None, log=None):
+    """Properties of a GPU-built index (read back from its blob) that must
+    hold whatever the k-means trajectory: latent within 1 ulp of the oracle's
+    projection, CSR bit-exact from the GPU's own assignment, every key at its
+    nearest centroid (GPU centroids, float64 distances) within 1e-4."""
+    rng = np.random.default_rng(123)
+    for h, hh in enumerate(gidx.heads):
+        n = desc.n_keys
+        assert np.array_equal(np.sort(hh.perm), np.arange(n)), "perm is not a bijection"
+        rows = np.arange(n) if sample is None or sample >= n else np.sort(rng.choice(n, sample, replace=False))
+        keys_h = keys[hh.perm[rows], h, :]
+        ref = O.latent_keys(keys_h, W[h], desc.key_dtype, desc.latent_dtype)
+        got = hh.csr_latent[rows]
+        if desc.latent_dtype == "bf16":
+            ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+            assert np.all(np.abs(got - ref) <= ulp * 1.0000001), "latent beyond 1 bf16 ulp"
+        else:
+            sc = np.abs(O.stored_to_f64(keys_h, desc.key_dtype)) @ np.abs(W[h].astype(np.float64))
+            assert np.all(np.abs(got - ref) <= 1e-5 * sc + 1e-30), "fp32 latent beyond tolerance"
+        lat = np.empty_like(hh.csr_latent)
+        lat[hh.perm] = hh.csr_latent
+        for lev in range(desc.n_levels):
+            nodes = desc.nodes(lev + 1)
+            off, perm = csr_from_assignment(hh.assign[lev], nodes)
+            assert np.array_equal(off, hh.offsets[lev]), f"head {h} level {lev + 1}: offsets"
+            if lev == desc.n_levels - 1:
+                assert np.array_equal(perm, hh.perm), f"head {h}: perm is not the stable CSR order"
+            f = desc.fanout[lev]
+            mcount = np.array([n]) if lev == 0 else np.diff(hh.offsets[lev - 1])
+            cent = hh.centroids[lev].reshape(-1, f, lat.shape[1])
+            ks = np.arange(n) if sample is None or sample >= n else np.sort(rng.choice(n, sample, replace=False))
+            for c0 in range(0, len(ks), 2048):
+                kk = ks[c0:c0 + 2048]
+                x = lat[kk]
+                node = hh.assign[lev][kk]
+                pk = node // f
+                nv = np.minimum(mcount[pk], f)
+                d2 = ((x[:, None, :] - cent[pk]) ** 2).sum(-1)               # [m, F]
+                d2[np.arange(f)[None, :] >= nv[:, None]] = np.inf
+                best = d2.min(axis=1)
+                mine = d2[np.arange(len(kk)), node % f]
+                ok = mine <= best * (1 + 1e-4) + 1e-6 * (x * x).sum(-1)
+                assert ok.all(), f"head {h} level {lev + 1}: {np.sum(~ok)} keys not at their nearest centroid"
+    if log:
+        log("build properties hold")

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Select is tested on oracle-built index blobs, which isolates it from the GPU
+build; the GPU build is tested by the properties its final state must have
+(latent within 1 ulp, nearest-centroid assignments, stable nested CSR) and by
+its agreement with the oracle's build on the same inputs."""
+import numpy as np
+import pytest
+
+from oracle import lsa_oracle as O
+from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
+from tests.parity import check_build, compare_select, log
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_key_indexer_amd import _abi
+    _abi.load()
+
+
+def _abi():
+    from hierarchical_key_indexer_amd import _abi as A
+    return A
+
+
+def _li(desc_o: O.IndexDesc, blob=None):
+    from hierarchical_key_indexer_amd.indexer import LatentIndex
+    A = _abi()
+    d = A.IndexDesc.make(desc_o.n_keys, desc_o.n_kv_heads, desc_o.d_head, desc_o.d_latent, desc_o.key_dtype,
+                         desc_o.latent_dtype, desc_o.fanout, desc_o.kmeans_iters, desc_o.seed)
+    li = LatentIndex(d)
+    if blob is not None:
+        assert li.index.numel() == blob.size
+        li.index.copy_(torch.from_numpy(blob))
+    return li
+
+
+def _dev(arr):
+    from hierarchical_key_indexer_amd.indexer import keys_to_device
+    return keys_to_device(arr)
+
+
+def _params(prm: O.SelectParams):
+    return _abi().SelectParams.make(prm.b, prm.k, prm.sink, prm.window, prm.beam)
+
+
+def gpu_select(li, queries, pos, prm, flat=False, leaves=True):
+    q = _dev(queries)
+    p = torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).cuda()
+    if flat:
+        idx, sc, lv = li.flat_select(q, p, _params(prm))
+    else:
+        idx, sc, lv = li.select(q, p, _params(prm), leaves=leaves)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy(), (None if lv is None else lv.cpu().numpy())
+
+
+def gpu_build(desc_o, keys, W):
+    li = _li(desc_o)
+    li.build(_dev(keys), torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    return li
+
+
+def _blob_of(li):
+    return li.index.cpu().numpy()
+
+
+def _small(name="decode_1m", **kw):
+    base = dict(n_keys=3000, n_kv_heads=2, group=2, d_latent=64, n_centers=60, n_tokens=6, kmeans_iters=4,
+                fanout=(8, 8), b=3, k=50, sink=4, window=32)
+    base.update(kw)
+    return get_workload(name).scaled(**base)
+
+
+SMALL_CASES = {
+    "2lvl_bf16_g2": _small(),
+    "1lvl_f32_dl32": _small("tiny_flat_65k", n_keys=5000, n_kv_heads=1, group=1, d_latent=32, fanout=(64,), b=5,
+                            k=100, n_centers=50),
+    "3lvl_bf16_g4": _small(n_keys=20000, n_kv_heads=2, group=4, fanout=(4, 5, 6), b=2, k=64, window=100),
+    "2lvl_f32_keys_bf16_lat": _small(key_dtype="f32", n_keys=4097, fanout=(16, 4), b=4, k=33, sink=0, window=0),
+    "2lvl_tiny_nodes": _small(n_keys=300, fanout=(16, 16), b=4, k=20),          # many nodes with < fanout members
+    "ragged_k_gt_cands": _small(n_keys=777, fanout=(4, 4), b=1, k=300, window=7),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL_CASES))
+def test_small_select_and_flat_on_oracle_index(case):
+    wl = SMALL_CASES[case]
+    log(f"[small select] case={case} N={wl.n_keys} fanout={wl.fanout} b={wl.b} k={wl.k}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    queries = gen_queries(wl, keys)
+    # positions: the tail plus edge positions around sink / window
+    pos = np.array([0, 1, wl.sink, wl.sink + wl.window, wl.sink + wl.window + 1, wl.n_keys - 1][:wl.n_tokens],
+                   dtype=np.int32)
+    li = _li(desc, O.index_blob(oidx))
+    for beam in ("per_parent", "global"):
+        prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window, beam)
+        gi, gs, gl = gpu_select(li, queries, pos, prm)
+        compare_select(oidx, queries, pos, prm, gi, gs, gl, log=log)
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, flat=True, log=log)
+
+
+@pytest.mark.parametrize("case", ["2lvl_bf16_g2", "1lvl_f32_dl32", "3lvl_bf16_g4", "2lvl_tiny_nodes"])
+def test_small_build_properties_and_agreement(case):
+    wl = SMALL_CASES[case]
+    log(f"[small build] case={case}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    li = gpu_build(desc, keys, W)
+    blob = _blob_of(li)
+    gidx = O.index_from_blob(blob, desc)
+    check_build(gidx, keys, W, desc, log=log)
+    oidx = O.build_index(keys, W, desc)
+    oblob = O.index_blob(oidx)
+    assert np.array_equal(blob[:64], oblob[:64]) and np.array_equal(blob[64:200], oblob[64:200]), "header"
+    agree = [np.mean(gidx.heads[h].assign[-1] == oidx.heads[h].assign[-1]) for h in range(desc.n_kv_heads)]
+    log(f"leaf agreement with the oracle build: {agree}")
+    assert min(agree) >= 0.99
+    li2 = gpu_build(desc, keys, W)
+    assert np.array_equal(blob, _blob_of(li2)), "build is not deterministic"
+
+
+def test_tree_with_all_buckets_equals_flat_gpu():
+    # b equal to every level's fanout: the descent keeps every non-empty bucket
+    wl = _small(n_keys=5000, fanout=(8, 8), b=8, k=77)
+    keys, W = gen_keys(wl), gen_W(wl)
+    li = gpu_build(O.IndexDesc.of(wl), keys, W)
+    q, p = gen_queries(wl, keys), gen_positions(wl)
+    prm = O.SelectParams(8, 77, wl.sink, wl.window)
+    ti, ts, _ = gpu_select(li, q, p, prm)
+    fi, fs, _ = gpu_select(li, q, p, prm, flat=True)
+    assert np.array_equal(ti, fi) and np.array_equal(ts, fs)
+
+
+def test_edge_positions_and_invalid_rows():
+    wl = _small(n_keys=2000, n_tokens=8, fanout=(8, 8), b=2, k=40, sink=4, window=16)
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    li = _li(desc, O.index_blob(oidx))
+    queries = gen_queries(wl, keys)
+    pos = np.array([0, 3, 4, 19, 20, 21, -1, 2000], dtype=np.int32)
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    for flat in (False, True):
+        gi, gs, gl = gpu_select(li, queries, pos, prm, flat=flat)
+        ok = [(t, hq) for t in range(6) for hq in range(wl.n_q_heads)]
+        compare_select(oidx, queries, pos, prm, gi, gs, gl, pairs=ok, flat=flat, log=log)
+        assert np.all(gi[6:] == -1) and np.all(np.isneginf(gs[6:]))
+
+
+def test_zero_tokens_is_a_no_op():
+    A = _abi()
+    wl = _small(n_keys=500)
+    desc = O.IndexDesc.of(wl)
+    li = _li(desc)
+    q = torch.zeros((0, wl.n_q_heads, wl.d_head), dtype=torch.bfloat16, device="cuda")
+    p = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    prm = A.SelectParams.make(wl.b, wl.k, wl.sink, wl.window)
+    out = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ws = torch.zeros((256,), dtype=torch.uint8, device="cuda")
+    A.lsa_select(li.desc, li.index, q, p, prm, out, None, None, ws)
+    A.lsa_flat_select(li.desc, li.index, q, p, prm, out, None, ws)
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+def test_tiny_flat_65k_build_and_select():
+    wl = get_workload("tiny_flat_65k")
+    log(f"[tiny_flat_65k] N={wl.n_keys}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    queries, pos = gen_queries(wl, keys), gen_positions(wl)
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    li = _li(desc, O.index_blob(oidx))
+    gi, gs, gl = gpu_select(li, queries, pos, prm)
+    compare_select(oidx, queries, pos, prm, gi, gs, gl, log=log)
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, flat=True, log=log)
+    # tree with b = 256 (every bucket) equals flat exactly
+    prm_all = O.SelectParams(256, wl.k, wl.sink, wl.window)
+    ai, as_, _ = gpu_select(li, queries, pos, prm_all)
+    assert np.array_equal(ai, fi) and np.array_equal(as_, fs)
+    # GPU build
+    lb = gpu_build(desc, keys, W)
+    blob = _blob_of(lb)
+    gidx = O.index_from_blob(blob, desc)
+    check_build(gidx, keys, W, desc, log=log)
+    agree = np.mean(gidx.heads[0].assign[0] == oidx.heads[0].assign[0])
+    log(f"tiny_flat_65k leaf agreement with the oracle build: {agree:.6f}")
+    assert agree >= 0.99
+    assert np.array_equal(blob, _blob_of(gpu_build(desc, keys, W)))
+
+
+@pytest.fixture(scope="module")
+def c1():
+    wl = get_workload("decode_1m")
+    log("[decode_1m] generating keys")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    log("[decode_1m] oracle index build (8 heads)")
+    oidx = O.build_index(keys, W, desc, progress=log, workers=8)
+    return wl, keys, W, desc, oidx
+
+
+def test_decode_1m_select_parity(c1):
+    wl, keys, W, desc, oidx = c1
+    queries, pos = gen_queries(wl, keys), gen_positions(wl)
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    li = _li(desc, O.index_blob(oidx))
+    log("[decode_1m] GPU tree select")
+    gi, gs, gl = gpu_select(li, queries, pos, prm)
+    compare_select(oidx, queries, pos, prm, gi, gs, gl, log=log)
+    log("[decode_1m] GPU flat select")
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, flat=True, log=log)
+    # repeat-run equality
+    gi2, gs2, _ = gpu_select(li, queries, pos, prm)
+    assert np.array_equal(gi, gi2) and np.array_equal(gs, gs2)
+
+
+def test_prefill_1m_select_sampled(c1):
+    wl, keys, W, desc, oidx = c1
+    wl2 = get_workload("prefill_1m")
+    queries, pos = gen_queries(wl2, keys), gen_positions(wl2)
+    prm = O.SelectParams(wl2.b, wl2.k, wl2.sink, wl2.window)
+    li = _li(desc, O.index_blob(oidx))
+    log("[prefill_1m] GPU tree select, 4096 tokens x 32 heads")
+    gi, gs, gl = gpu_select(li, queries, pos, prm)
+    rng = np.random.default_rng(5)
+    pairs = [(int(t), int(h)) for t, h in zip(rng.integers(0, wl2.n_tokens, 96), rng.integers(0, 32, 96))]
+    pairs += [(0, 0), (wl2.n_tokens - 1, 31)]
+    compare_select(oidx, queries, pos, prm, gi, gs, gl, pairs=pairs, log=log)
+
+
+def test_decode_1m_gpu_build(c1):
+    wl, keys, W, desc, oidx = c1
+    log("[decode_1m] GPU build")
+    li = gpu_build(desc, keys, W)
+    blob = _blob_of(li)
+    gidx = O.index_from_blob(blob, desc)
+    check_build(gidx, keys, W, desc, sample=20000, log=log)
+    for h in range(desc.n_kv_heads):
+        agree = np.mean(gidx.heads[h].assign[-1] == oidx.heads[h].assign[-1])
+        log(f"head {h}: leaf agreement with the oracle build {agree:.5f}")
+        assert agree >= 0.95
+    li2 = gpu_build(desc, keys, W)
+    assert torch.equal(li.index, li2.index), "build is not deterministic"
