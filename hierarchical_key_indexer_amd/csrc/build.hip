@@ -520,6 +520,12 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
   const int DL = d.d_latent;
   const bool lat_bf16 = d.latent_dtype == LSA_BF16;
 
+  // every byte of the blob is defined (section padding included)
+  {
+    const int64_t nb = (int64_t)(L.total / 4);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(nb)), dim3(256), 0, st, (uint32_t*)blob, 0u, nb);
+    LSA_LAUNCH_CHECK();
+  }
   // latent keys [Hkv][N][DL]
   {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)hk);
