@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA indexer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_1m]
+
+A step is one ``lsa_select`` call over the workload's batch of query heads
+(query projection, centroid descent, gather-and-score, top-k, assembly), with
+the key cache and its index already resident in HBM.  The index build and the
+full-scan baseline (``lsa_flat_select``) are timed in the same run and
+reported beside it, together with tree-vs-flat recall.
+
+Prints one JSON line.  ``roofline`` describes the dominant kernel of the step
+(the gather-and-score): algorithmic bytes per launch (keys scored x bytes per
+key row) over its average duration, measured with HIP events that the library
+records on its own launch stream.  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer query-heads/s and keys-scored/s at 1M/10M keys; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_key_indexer_amd", "csrc", f)
+                  for f in ("select.hip", "lsa_device.h")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (the library records them on
+    the stream it launches on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        assert self.hip.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed_steps(fn, steps, hip, stage, abi):
+    """Run fn() `steps` times; return (wall ms per step, stage ms per step)."""
+    import torch
+    starts, stops = hip.create(steps), hip.create(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        abi.set_profile_events(stage, starts[i], stops[i])
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    abi.set_profile_events(stage, None, None)
+    stage_ms = sum(hip.elapsed_ms(a, b) for a, b in zip(starts, stops)) / steps
+    hip.destroy(starts + stops)
+    return wall, stage_ms
+
+
+def cpu_baseline(wl, keys, W, queries, pos):
+    """The CPU oracle, untuned, on KV head 0 of the workload: its index build
+    (reported, not in the value) and the selection of that head's G query
+    heads for every token (sampled to at most 64 query heads)."""
+    import numpy as np
+    from oracle import lsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    desc = O.IndexDesc.of(wl)
+    t = time.perf_counter()
+    oidx = O.build_index(keys, W, desc, heads=[0])
+    build_s = time.perf_counter() - t
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    pairs = [(tt, hq) for tt in range(wl.n_tokens) for hq in range(wl.group)]
+    if len(pairs) > 64:
+        rng = np.random.default_rng(0)
+        pairs = [pairs[i] for i in sorted(rng.choice(len(pairs), 64, replace=False))]
+    t = time.perf_counter()
+    O.select(oidx, queries, pos, prm, pairs=pairs)
+    sel_s = time.perf_counter() - t
+    return {
+        "value": len(pairs) / sel_s, "unit": "query-heads/s", "cores": blas_threads, "kind": "oracle",
+        "sample": (f"KV head 0 of {wl.name} (N={wl.n_keys}): oracle select of {len(pairs)} query heads "
+                   f"in {sel_s:.2f} s on the oracle's own index of that head (index build {build_s:.1f} s, "
+                   f"not in the value); float64 numpy, BLAS threads={blas_threads}, host cpus={os.cpu_count()}"),
+        "build_s_one_head": build_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_1m")
+    ap.add_argument("--flat-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flat", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the indexer shards by KV head "
+              f"with no exchange, and multi-GPU runs are not part of this build.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hierarchical_key_indexer_amd import _abi
+    from hierarchical_key_indexer_amd.indexer import LatentIndex, keys_to_device
+    from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _abi.load()
+    hip = HipEvents()
+    wl = get_workload(args.workload)
+    log(f"workload {wl.name}: generating inputs")
+    t = time.perf_counter()
+    keys, W = gen_keys(wl), gen_W(wl)
+    queries, pos = gen_queries(wl, keys), gen_positions(wl)
+    log(f"inputs ready in {time.perf_counter() - t:.1f} s")
+    kd, Wd = keys_to_device(keys), torch.from_numpy(W).cuda()
+    qd, pd = keys_to_device(queries), torch.from_numpy(pos).cuda()
+    desc = _abi.IndexDesc.of(wl)
+    li = LatentIndex(desc)
+    # index build (not part of the step): first call warms up, then timed
+    li.build(kd, Wd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    li.build(kd, Wd)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    li.release_build_workspace()
+    log(f"index build {build_ms:.1f} ms")
+
+    prm = _abi.SelectParams.make(wl.b, wl.k, wl.sink, wl.window)
+    out = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, leaves=True)
+    li.select(qd, pd, prm, leaves=True, out=out)
+    torch.cuda.synchronize()
+    # keys scored per call: members of every selected leaf
+    counts = li.leaf_counts()
+    leaves = out[2].cpu().numpy()
+    heads_of = np.arange(wl.n_q_heads) // wl.group
+    keys_scored = int(sum(counts[heads_of[hq]][leaves[t_, hq][leaves[t_, hq] >= 0]].sum()
+                          for t_ in range(wl.n_tokens) for hq in range(wl.n_q_heads)))
+    row_bytes = wl.d_latent * (2 if wl.latent_dtype == "bf16" else 4) + 4
+
+    for _ in range(args.warmup):
+        li.select(qd, pd, prm, leaves=False, out=(out[0], out[1], None))
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} select steps")
+    ms_step, gather_ms = timed_steps(lambda: li.select(qd, pd, prm, leaves=False, out=(out[0], out[1], None)),
+                                     args.steps, hip, _abi.STAGE_GATHER, _abi)
+    qheads = wl.n_tokens * wl.n_q_heads
+    tree_idx = out[0].cpu().numpy()
+
+    gather_bytes = keys_scored * row_bytes
+    roof = {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(wl.name, "gather")
+    roof["kernel"] = "gather_kernel"
+    roof["algorithmic_bytes_per_launch"] = gather_bytes
+    roof["kernel_ms"] = gather_ms
+
+    result = {
+        "metric": METRIC, "value": qheads / (ms_step * 1e-3), "unit": "query-heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.latent_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; keys around Gaussian centers, queries = noisy cached keys)",
+        "config": {"workload": wl.name, "n_keys": wl.n_keys, "kv_heads": wl.n_kv_heads, "q_heads": wl.n_q_heads,
+                   "tokens": wl.n_tokens, "d_head": wl.d_head, "d_latent": wl.d_latent, "fanout": list(wl.fanout),
+                   "b": wl.b, "k": wl.k, "sink": wl.sink, "window": wl.window},
+        "keys_scored_per_s": keys_scored / (ms_step * 1e-3),
+        "keys_scored_per_step": keys_scored,
+        "roofline": roof,
+        "build_ms": build_ms,
+    }
+
+    if not args.no_flat:
+        fsteps = args.flat_steps or max(5, min(args.steps, 50))
+        fout = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, flat=True)
+        for _ in range(3):
+            li.flat_select(qd, pd, prm, out=fout)
+        flat_ms, flat_kernel_ms = timed_steps(lambda: li.flat_select(qd, pd, prm, out=fout), fsteps, hip,
+                                              _abi.STAGE_FLAT, _abi)
+        flat_idx = fout[0].cpu().numpy()
+        s0, k = wl.sink, wl.k
+        rec = []
+        for t_ in range(wl.n_tokens):
+            for hq in range(wl.n_q_heads):
+                a = tree_idx[t_, hq, s0:s0 + k]
+                b = flat_idx[t_, hq, s0:s0 + k]
+                a, b = set(a[a >= 0].tolist()), set(b[b >= 0].tolist())
+                rec.append(len(a & b) / max(1, len(b)))
+        flat_bytes = wl.n_tokens * wl.n_kv_heads * wl.n_keys * row_bytes
+        result["flat"] = {
+            "ms_per_call": flat_ms, "query_heads_per_s": qheads / (flat_ms * 1e-3),
+            "keys_scored_per_s": qheads * wl.n_keys / (flat_ms * 1e-3),
+            "kernel": "flat_kernel", "kernel_ms": flat_kernel_ms,
+            "achieved_GBs": flat_bytes / (flat_kernel_ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": flat_bytes / (flat_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": load_traffic(wl.name, "flat"),
+        }
+        result["recall_at_k_vs_flat"] = {"mean": float(np.mean(rec)), "p5": float(np.percentile(rec, 5))}
+        result["speedup_vs_flat"] = flat_ms / ms_step
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 1 << 30
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, keys, W, queries, pos)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

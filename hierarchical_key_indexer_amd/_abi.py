@@ -20,7 +20,8 @@ BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
 
 EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
            "lsa_select_workspace_bytes", "lsa_select", "lsa_flat_workspace_bytes", "lsa_flat_select",
-           "lsa_last_error", "lsa_abi_version")
+           "lsa_last_error", "lsa_abi_version", "lsa_set_profile_events")
+STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT = 1, 2, 3, 4, 5
 
 
 class IndexDesc(ctypes.Structure):
@@ -83,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_flat_select.restype = ctypes.c_int
     lib.lsa_last_error.argtypes, lib.lsa_last_error.restype = [], ctypes.c_char_p
     lib.lsa_abi_version.argtypes, lib.lsa_abi_version.restype = [], I32
+    lib.lsa_set_profile_events.argtypes, lib.lsa_set_profile_events.restype = [I32, VP, VP], ctypes.c_int
     _lib = lib
     return lib
 
@@ -165,3 +167,9 @@ def lsa_flat_select(desc, index, queries, q_pos, params, out_idx, out_scores=Non
     _check(load().lsa_flat_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
                                   ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(workspace),
                                   0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def set_profile_events(stage: int, start, stop) -> None:
+    """Record raw hipEvent_t handles around one stage of later select calls
+    (None, None switches it off)."""
+    _check(load().lsa_set_profile_events(stage, start, stop))

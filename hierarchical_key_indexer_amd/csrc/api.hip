@@ -8,7 +8,22 @@
 
 namespace lsa {
 size_t build_workspace_bytes(const lsa_index_desc& d);
+
+namespace {
+struct StageEvents {
+  void* start = nullptr;
+  void* stop = nullptr;
+};
+thread_local StageEvents g_stage[8];
+}  // namespace
+
+void prof_begin(int stage, hipStream_t st) {
+  if (g_stage[stage].start) (void)hipEventRecord((hipEvent_t)g_stage[stage].start, st);
 }
+void prof_end(int stage, hipStream_t st) {
+  if (g_stage[stage].stop) (void)hipEventRecord((hipEvent_t)g_stage[stage].stop, st);
+}
+}  // namespace lsa
 
 namespace {
 
@@ -95,6 +110,15 @@ extern "C" {
 const char* lsa_last_error(void) { return g_err; }
 
 int32_t lsa_abi_version(void) { return 1; }
+
+int lsa_set_profile_events(int32_t stage, void* start, void* stop) {
+  clear_err();
+  if (stage < LSA_STAGE_PROJECT || stage > LSA_STAGE_FLAT) return fail(LSA_ERR_INVALID_ARG, "unknown stage %d", stage);
+  if ((start == nullptr) != (stop == nullptr)) return fail(LSA_ERR_INVALID_ARG, "start and stop must both be set or both NULL");
+  lsa::g_stage[stage].start = start;
+  lsa::g_stage[stage].stop = stop;
+  return LSA_OK;
+}
 
 size_t lsa_index_bytes(const lsa_index_desc* desc) {
   clear_err();

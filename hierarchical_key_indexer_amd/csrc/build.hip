@@ -28,14 +28,6 @@ namespace lsa {
 // projection: out = round(X . W) for 64 rows x one head per workgroup
 // ---------------------------------------------------------------------------
 
-template <typename KT> struct KeyLoad;
-template <> struct KeyLoad<float> {
-  __device__ static __forceinline__ float get(const float* p, int i) { return p[i]; }
-};
-template <> struct KeyLoad<bf16_t> {
-  __device__ static __forceinline__ float get(const bf16_t* p, int i) { return bf16_to_f32(p[i]); }
-};
-
 // X [nrows][nheads][dh]; W [heads/group][dh][DL]; the output row of (row, head)
 // is out + ((head_major ? head * nrows + row : row * nheads + head) * DL).
 // OUT_BF16: store bf16 bits (uint16) of the RNE rounding; otherwise store

@@ -64,6 +64,33 @@ template <> struct Lat<float> {
   }
   __device__ static __forceinline__ float get(const float* row, int i) { return row[i]; }
 };
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+
+// 8 bf16 latents . 8 bf16 query values (two per dword), fp32 accumulation with
+// the packed dot2 instruction (bf16 x bf16 products are exact in fp32).
+__device__ __forceinline__ float dot16_bf16x2(const uint4& v, const uint4& q) {
+  float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s16, v.x), __builtin_bit_cast(v2s16, q.x), 0.f, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s16, v.y), __builtin_bit_cast(v2s16, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s16, v.z), __builtin_bit_cast(v2s16, q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2s16, v.w), __builtin_bit_cast(v2s16, q.w), acc, false);
+  return acc;
+}
+
+// Query slice held as the operand the row dot products want: packed bf16
+// pairs for a bf16 latent store (the query latent is bf16-valued there), fp32
+// values for an fp32 store.
+template <typename LT> struct QSlice;
+template <> struct QSlice<bf16_t> {
+  uint4 q;
+  __device__ __forceinline__ void load(const float* src) {   // 8 bf16-valued floats
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(src[2 * i]) >> 16) | (__float_as_uint(src[2 * i + 1]) & 0xFFFF0000u);
+    q = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ __forceinline__ float dot(const uint4& v) const { return dot16_bf16x2(v, q); }
+};
+
 template <> struct Lat<bf16_t> {
   static constexpr int PER16 = 8;
   __device__ static __forceinline__ float dot16(const uint4& v, const float* q) {
@@ -80,12 +107,35 @@ template <> struct Lat<bf16_t> {
   __device__ static __forceinline__ float get(const bf16_t* row, int i) { return bf16_to_f32(row[i]); }
 };
 
-// Sum over aligned groups of G lanes (G in {2,4,8,16,32}); every lane of the
-// group receives the group's sum.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
+// Keys / queries in their storage format, widened to fp32.
+template <typename KT> struct KeyLoad;
+template <> struct KeyLoad<float> {
+  __device__ static __forceinline__ float get(const float* p, int i) { return p[i]; }
+};
+template <> struct KeyLoad<bf16_t> {
+  __device__ static __forceinline__ float get(const bf16_t* p, int i) { return bf16_to_f32(p[i]); }
+};
+
+template <> struct QSlice<float> {
+  float q[4];
+  __device__ __forceinline__ void load(const float* src) {
 #pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+    for (int i = 0; i < 4; ++i) q[i] = src[i];
+  }
+  __device__ __forceinline__ float dot(const uint4& v) const { return Lat<float>::dot16(v, q); }
+};
+
+// Sum over aligned groups of G lanes (G in {1,2,4,8,16}) with DPP moves; the
+// first lane of every group (lane % G == 0) receives the group's sum (other
+// lanes hold partial sums).  xor-1 and xor-2 quad permutations, then row
+// shifts left by 4 and by 8 (lane i reads lane i+4 / i+8 of its 16-lane row).
+template <int G>
+__device__ __forceinline__ float group_sum_lead(float v) {
+  if (G >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  if (G >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  if (G >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, true));
+  if (G >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xF, 0xF, true));
+  static_assert(G <= 16, "groups wider than a DPP row");
   return v;
 }
 
@@ -133,36 +183,98 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wsum, int* total
   return base + incl - x;
 }
 
+// Exclusive prefix sum in reversed thread order: thread t gets the sum of x
+// over threads t+1 .. BLOCK-1.  Contains barriers.
+template <int BLOCK>
+__device__ __forceinline__ int block_exclusive_scan_rev(int x, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = x;   // sum over lanes >= lane within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_down(incl, off, 64);
+    if (lane + off < 64) incl += o;
+  }
+  if (lane == 0) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < BLOCK / 64; ++i) {
+    int s = wsum[i];
+    base += (i > w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
 // LDS scratch of the radix select.
 struct RadixScratch {
   uint32_t hist[256];
   int wsum[16];
+  u64 wmin[16], wmax[16];
   int digit;
   uint32_t above;
   uint32_t hd;
 };
 
+__device__ __forceinline__ u64 wave_min_u64(u64 v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    u64 o = __shfl_xor(v, m, 64);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
 // Keep the k largest nonzero keys of buf[0..n) (n <= BLOCK*M, k < n, keys
 // unique) in buf[0..k), in no particular order.  Returns a value t such that
 // every kept key is >= t and every dropped key is < t (so a future key can
-// only belong to the best k if it is > t).  MSB-first radix select, 8 bits
-// per pass, on keys held in registers.  All threads of the block must call.
+// only belong to the best k if it is > t).  MSB-first radix select on keys
+// held in registers: the bits the smallest and largest key share are common
+// to all keys and skipped, then 8-bit digits from the highest bit where they
+// differ (so the first histogram is spread, not piled into one bin).  All
+// threads of the block must call.
 template <int BLOCK, int M>
 __device__ u64 topk_compact(u64* buf, int n, int k, RadixScratch* sc) {
+  constexpr int NW = BLOCK / 64;
   u64 v[M];
+  u64 lo = ~0ull, hi = 0ull;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const int i = threadIdx.x + j * BLOCK;
     v[j] = (i < n) ? buf[i] : 0ull;
+    if (v[j] != 0ull) {
+      lo = v[j] < lo ? v[j] : lo;
+      hi = v[j] > hi ? v[j] : hi;
+    }
   }
-  u64 prefix = 0, mask = 0;
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if ((threadIdx.x & 63) == 0) {
+    sc->wmin[threadIdx.x >> 6] = lo;
+    sc->wmax[threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  lo = sc->wmin[0];
+  hi = sc->wmax[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    lo = sc->wmin[i] < lo ? sc->wmin[i] : lo;
+    hi = sc->wmax[i] > hi ? sc->wmax[i] : hi;
+  }
+  const int top = (lo == hi) ? 0 : 64 - __clzll(lo ^ hi);     // bits [0, top) vary
+  u64 mask = top >= 64 ? 0ull : (~0ull << top);
+  u64 prefix = lo & mask;
   uint32_t need = (uint32_t)k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int hb = top; hb > 0;) {
+    const int lb = hb > 8 ? hb - 8 : 0;
+    const u64 dmask = ((1ull << (hb - lb)) - 1ull);
     for (int i = threadIdx.x; i < 256; i += BLOCK) sc->hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < M; ++j)
-      if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&sc->hist[(uint32_t)(v[j] >> shift) & 255u], 1u);
+      if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&sc->hist[(uint32_t)((v[j] >> lb) & dmask)], 1u);
     __syncthreads();
     if (threadIdx.x < 64) {
       const int l = threadIdx.x;
@@ -192,11 +304,12 @@ __device__ u64 topk_compact(u64* buf, int n, int k, RadixScratch* sc) {
     __syncthreads();
     const int d = sc->digit;
     need -= sc->above;
-    const uint32_t hd = sc->hd;
-    prefix |= (u64)d << shift;
-    mask |= 0xFFull << shift;
+    const uint32_t hdv = sc->hd;
+    prefix |= (u64)d << lb;
+    mask |= dmask << lb;
     __syncthreads();
-    if (hd == need) break;
+    if (hdv == need) break;
+    hb = lb;
   }
   int mine = 0;
 #pragma unroll
@@ -236,22 +349,110 @@ __device__ void bitonic_sort_asc(u64* buf, int n, int cap) {
   }
 }
 
+// LDS scratch of the bucket sort by key index.
+constexpr int kSortBuckets = 1024;
+struct SortScratch {
+  uint32_t cnt[kSortBuckets];
+  int wsum[16];
+  u64 wmin[16], wmax[16];
+  int big;
+};
+
+// Sort the n unique keys buf[0..n) (index in the high 32 bits) ascending
+// into out[0..n): bucket by index over [min, max] (histogram, scan,
+// scatter), then an insertion sort inside every bucket.  A bucket of more
+// than 64 keys (a very uneven index spread) sends the whole set to the
+// bitonic sort instead.  Returns the array holding the sorted keys.
+template <int BLOCK>
+__device__ u64* sort_by_index(u64* buf, u64* out, int n, int cap, SortScratch* sc) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int NB = kSortBuckets;
+  u64 lo = ~0ull, hi = 0ull;
+  for (int i = threadIdx.x; i < n; i += BLOCK) {
+    lo = buf[i] < lo ? buf[i] : lo;
+    hi = buf[i] > hi ? buf[i] : hi;
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if ((threadIdx.x & 63) == 0) {
+    sc->wmin[threadIdx.x >> 6] = lo;
+    sc->wmax[threadIdx.x >> 6] = hi;
+  }
+  for (int b = threadIdx.x; b < NB; b += BLOCK) sc->cnt[b] = 0u;
+  if (threadIdx.x == 0) sc->big = 0;
+  __syncthreads();
+  lo = sc->wmin[0];
+  hi = sc->wmax[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    lo = sc->wmin[i] < lo ? sc->wmin[i] : lo;
+    hi = sc->wmax[i] > hi ? sc->wmax[i] : hi;
+  }
+  const uint64_t ilo = lo >> 32, span = (hi >> 32) - ilo + 1;
+  auto bucket = [&](u64 key) { return (int)((((key >> 32) - ilo) * (uint64_t)NB) / span); };
+  for (int i = threadIdx.x; i < n; i += BLOCK) atomicAdd(&sc->cnt[bucket(buf[i])], 1u);
+  __syncthreads();
+  constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
+  int mine = 0, mx = 0;
+  if ((int)threadIdx.x * PER < NB)
+    for (int j = 0; j < PER; ++j) {
+      const int c = (int)sc->cnt[threadIdx.x * PER + j];
+      mine += c;
+      mx = c > mx ? c : mx;
+    }
+  if (mx > 64) sc->big = 1;
+  int total;
+  int run = block_exclusive_scan<BLOCK>(mine, sc->wsum, &total);
+  if ((int)threadIdx.x * PER < NB)
+    for (int j = 0; j < PER; ++j) {
+      const int c = (int)sc->cnt[threadIdx.x * PER + j];
+      sc->cnt[threadIdx.x * PER + j] = (uint32_t)run;
+      run += c;
+    }
+  __syncthreads();
+  if (sc->big) {
+    bitonic_sort_asc<BLOCK>(buf, n, cap);
+    return buf;
+  }
+  for (int i = threadIdx.x; i < n; i += BLOCK) {
+    const u64 key = buf[i];
+    out[atomicAdd(&sc->cnt[bucket(key)], 1u)] = key;
+  }
+  __syncthreads();
+  // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
+  for (int b = threadIdx.x; b < NB; b += BLOCK) {
+    const int e = (int)sc->cnt[b], st = b == 0 ? 0 : (int)sc->cnt[b - 1];
+    for (int i = st + 1; i < e; ++i) {
+      const u64 x = out[i];
+      int j = i - 1;
+      while (j >= st && out[j] > x) {
+        out[j + 1] = out[j];
+        --j;
+      }
+      out[j + 1] = x;
+    }
+  }
+  __syncthreads();
+  return out;
+}
+
 // Write one output row from the n (<= k) rank keys in buf: sink positions,
 // the keys in ascending index order with their scores, the window positions.
-// Uses buf as sort space (capacity cap >= next power of two of n).
+// buf[0..cap) is sort space; n <= cap / 2.
 template <int BLOCK>
 __device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
                                     int32_t* row, float* scores_row) {
+  __shared__ SortScratch ss;
   // re-key as (index << 32 | order(score)) so an ascending sort orders by index
   for (int i = threadIdx.x; i < n; i += BLOCK) {
     const u64 key = buf[i];
     buf[i] = ((u64)(uint32_t)rank_key_index(key) << 32) | (key >> 32);
   }
   __syncthreads();
-  bitonic_sort_asc<BLOCK>(buf, n, cap);
+  u64* sorted = n > 1 ? sort_by_index<BLOCK>(buf, buf + cap / 2, n, cap, &ss) : buf;
   for (int i = threadIdx.x; i < k; i += BLOCK) {
     if (i < n) {
-      const u64 key = buf[i];
+      const u64 key = sorted[i];
       row[sink + i] = (int32_t)(key >> 32);
       if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
     } else {

@@ -73,6 +73,10 @@ size_t build_workspace_bytes(const lsa_index_desc& d);
 int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void* index, void* ws,
                  hipStream_t stream, char* err, size_t errlen);
 
+// ---- instrumentation ---------------------------------------------------------
+void prof_begin(int stage, hipStream_t st);
+void prof_end(int stage, hipStream_t st);
+
 // ---- select ------------------------------------------------------------------
 struct SelectPlan {
   int64_t qh;          // T * Hq

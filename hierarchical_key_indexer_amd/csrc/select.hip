@@ -8,14 +8,19 @@
 // window.  The full scan is the "old indexer" of the flowchart on "Latent
 // Sparse Attention: tree search over keys for 10M-token context".
 //
-//   descend_kernel   one workgroup per query head: level-by-level centroid
-//                    dot products, wave-wide top-b per parent; leaf list with
-//                    CSR row starts and candidate prefix counts
+//   descend_kernel   one workgroup per query head: the query's latent
+//                    (round(q.W_h)), then level by level the children of every
+//                    kept node are scored (one lane per child) and ranked
+//                    within the wave (readlane compares); leaf list with CSR
+//                    row starts and candidate prefix counts
 //   gather_kernel    a query head's candidates split evenly over S
 //                    workgroups; 16-byte lane loads of latent rows (a row is
-//                    LPK lanes), fp32 dot, causal/sink/window mask, streaming
-//                    top-k in LDS (radix-select compaction)
-//   merge_kernel     top-k over the S partial lists, then the output row
+//                    LPK lanes, reduced with DPP), fp32 dot, causal / sink /
+//                    window mask, streaming top-k in LDS (radix-select
+//                    compaction); with S > 1 the local lists are appended to
+//                    one per-query-head array
+//   merge_kernel     streaming top-k over that array, then the output row
+//   qproj_kernel     query latents for the flat scan
 //   flat_kernel      full scan of one KV head's rows for its G query heads
 //                    (each row read once for G heads), streaming top-k each
 #include "lsa_device.h"
@@ -27,8 +32,10 @@ struct SelArgs {
   const void* lat;             // [Hkv][N][DL] CSR latent
   const int* perm;             // [Hkv][N]
   int64_t N;
-  int Hkv, G, Hq, T;
-  const float* qlat;           // [T*Hq][DL]
+  int Hkv, G, Hq, T, d_head;
+  const void* queries;         // [T][Hq][d_head] key dtype
+  const float* W;              // [Hkv][d_head][DL]
+  float* qlat;                 // [T*Hq][DL]
   const int* q_pos;            // [T]
   int sink, window, k, width;
   const void* cscore[kMaxLevels];
@@ -41,8 +48,10 @@ struct SelArgs {
   int* nleaf;                  // [QH]
   int* out_leaves;             // [QH][nl_cap] or null
   int S;                       // workgroups per query head (gather) or per (t, KV head) (flat)
-  unsigned long long* part_keys;  // [QH][S][k]
-  int* part_cnt;               // [QH][S]
+  unsigned long long* part_keys;  // [QH][part_cap] appended local top-k lists
+  unsigned int* part_n;        // [QH] entries appended
+  int64_t part_cap;
+  unsigned long long* tau;     // [QH] sampled lower bound for the best k (0 = none)
   int32_t* out_idx;            // [QH][width]
   float* out_scores;           // [QH][k] or null
   int64_t qh0;                 // first query head of this launch
@@ -57,41 +66,95 @@ __device__ __forceinline__ float row_dot(const LT* row, const float* q) {
   return acc;
 }
 
+// q~ = round_latent(q . W_h) into q_out (LDS) and the workspace.  d_head is
+// cut into kQSlices slices; thread (slice, j) sums one slice of output j and
+// the slice sums are added in slice order, so every kernel that projects a
+// query gets the same bits (needs blockDim >= kQSlices * DL).  qin holds
+// d_head + kQSlices * DL floats of LDS.
+constexpr int kQSlices = 4;
+
+template <typename KT, typename LT, int DL>
+__device__ __forceinline__ void query_latent(const SelArgs& a, int64_t qh, int h, float* qin, float* q_out) {
+  const KT* qrow = (const KT*)a.queries + qh * a.d_head;
+  float* part = qin + a.d_head;
+  for (int i = threadIdx.x; i < a.d_head; i += blockDim.x) qin[i] = KeyLoad<KT>::get(qrow, i);
+  __syncthreads();
+  if (threadIdx.x < kQSlices * DL) {
+    const int j = threadIdx.x % DL, sl = threadIdx.x / DL;
+    const int per = a.d_head / kQSlices;
+    const float* Wh = a.W + (size_t)h * a.d_head * DL + j;
+    float acc = 0.f;
+    for (int i = sl * per; i < (sl + 1) * per; i += 8) {   // per is a multiple of 8
+      float wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) wv[u] = Wh[(size_t)(i + u) * DL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(qin[i + u], wv[u], acc);
+    }
+    part[sl * DL + j] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < DL) {
+    float v = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < kQSlices; ++k2) v += part[k2 * DL + threadIdx.x];
+    v = Lat<LT>::PER16 == 8 ? round_to_bf16(v) : v;
+    q_out[threadIdx.x] = v;
+    a.qlat[qh * DL + threadIdx.x] = v;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // descent
 // ---------------------------------------------------------------------------
 
 // Compact the non-negative entries of src[0..ns) into dst (order kept);
-// returns the count.  Block-wide, 256 threads.
+// returns the count.  Block-wide.
+template <int BLOCK>
 __device__ int compact_ids(const int* src, int ns, int* dst, int* wsum) {
-  const int per = (ns + 255) / 256;
+  const int per = (ns + BLOCK - 1) / BLOCK;
   const int i0 = min(ns, (int)threadIdx.x * per), i1 = min(ns, i0 + per);
   int c = 0;
   for (int i = i0; i < i1; ++i) c += src[i] >= 0;
   int total;
-  int pos = block_exclusive_scan<256>(c, wsum, &total);
+  int pos = block_exclusive_scan<BLOCK>(c, wsum, &total);
   for (int i = i0; i < i1; ++i)
     if (src[i] >= 0) dst[pos++] = src[i];
   __syncthreads();
   return total;
 }
 
-template <typename LT, int DL>
-__global__ __launch_bounds__(256) void descend_kernel(SelArgs a) {
+__device__ __forceinline__ u64 readlane_u64(u64 v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((u64)hi << 32) | lo;
+}
+
+template <typename KT, typename LT, int DL, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
+  constexpr int NW = BLOCK / 64;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float qin[256 + kQSlices * DL];
   __shared__ float q[DL];
-  __shared__ int wsum[4];
-  __shared__ unsigned long long wbest[4];
+  __shared__ int wsum[NW];
+  __shared__ unsigned long long wbest[NW];
+  __shared__ RadixScratch rs;
   int* fa = (int*)smem;                   // frontier
-  int* fb = fa + a.nl_cap;                // next frontier slots
-  unsigned long long* gk = (unsigned long long*)(fb + a.nl_cap + (a.nl_cap & 1));  // global beam keys
+  int* fb = fa + a.nl_cap;                // next frontier slots, then the leaf prefix counts
+  const size_t off_gk = ((size_t)(2 * a.nl_cap + 1) * 4 + 7) / 8 * 8;
+  unsigned long long* gk = (unsigned long long*)(smem + off_gk);                       // global beam keys
+  unsigned long long* sk = gk + (a.beam == LSA_BEAM_GLOBAL ? (size_t)a.b * 256 : 0);   // sample keys
 
   const int64_t qh = a.qh0 + blockIdx.x;
   const int hq = (int)(qh % a.Hq);
   const int h = hq / a.G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < DL; i += 256) q[i] = a.qlat[qh * DL + i];
-  if (threadIdx.x == 0) fa[0] = 0;
+  query_latent<KT, LT, DL>(a, qh, h, qin, q);
+  if (threadIdx.x == 0) {
+    fa[0] = 0;
+    if (a.part_n) a.part_n[qh] = 0u;
+  }
   __syncthreads();
   int nf = 1;
   for (int lev = 0; lev < a.L; ++lev) {
@@ -99,38 +162,43 @@ __global__ __launch_bounds__(256) void descend_kernel(SelArgs a) {
     const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
     const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
     if (a.beam == LSA_BEAM_PER_PARENT) {
+      const int NJ = (F + 63) / 64;
       const int bs = min(a.b, F);
-      for (int i = w; i < nf; i += 4) {
+      for (int i = w; i < nf; i += NW) {
         const int par = fa[i];
-        unsigned long long key[4];
+        u64 key[4];
+        int nne = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int c = j * 64 + lane;
           key[j] = 0ull;
           if (c < F) {
             const int64_t node = (int64_t)par * F + c;
-            if (off[node + 1] > off[node]) key[j] = rank_key(row_dot<LT, DL>(cs + node * DL, q), (int)node);
+            const int o0 = off[node], o1 = off[node + 1];
+            const float sc = row_dot<LT, DL>(cs + node * DL, q);   // loads issued with the offsets
+            if (o1 > o0) key[j] = rank_key(sc, (int)node);
+          }
+          nne += __popcll(__ballot(key[j] != 0ull));
+        }
+        // rank of each key among the parent's children (keys are unique)
+        int rank[4] = {0, 0, 0, 0};
+        for (int jj = 0; jj < NJ; ++jj) {
+          for (int src = 0; src < 64; ++src) {
+            const u64 other = readlane_u64(key[jj], src);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rank[j] += other > key[j] ? 1 : 0;
           }
         }
-        int r = 0;
-        for (; r < bs; ++r) {
-          unsigned long long best = key[0];
 #pragma unroll
-          for (int j = 1; j < 4; ++j) best = key[j] > best ? key[j] : best;
-          const unsigned long long wm = wave_max_u64(best);
-          if (wm == 0ull) break;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (key[j] == wm) key[j] = 0ull;
-          if (lane == 0) fb[i * bs + r] = rank_key_index(wm);
-        }
-        for (int rr = r + lane; rr < bs; rr += 64) fb[i * bs + rr] = -1;
+        for (int j = 0; j < 4; ++j)
+          if (key[j] != 0ull && rank[j] < bs) fb[i * bs + rank[j]] = rank_key_index(key[j]);
+        for (int r = min(nne, bs) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
       }
       __syncthreads();
-      nf = compact_ids(fb, nf * bs, fa, wsum);
+      nf = compact_ids<BLOCK>(fb, nf * bs, fa, wsum);
     } else {
       const int ns = nf * F;
-      for (int i = threadIdx.x; i < ns; i += 256) {
+      for (int i = threadIdx.x; i < ns; i += BLOCK) {
         const int par = fa[i / F], c = i % F;
         const int64_t node = (int64_t)par * F + c;
         gk[i] = off[node + 1] > off[node] ? rank_key(row_dot<LT, DL>(cs + node * DL, q), (int)node) : 0ull;
@@ -138,48 +206,94 @@ __global__ __launch_bounds__(256) void descend_kernel(SelArgs a) {
       __syncthreads();
       int r = 0;
       for (; r < a.b; ++r) {
-        unsigned long long best = 0ull;
-        for (int i = threadIdx.x; i < ns; i += 256) best = gk[i] > best ? gk[i] : best;
+        u64 best = 0ull;
+        for (int i = threadIdx.x; i < ns; i += BLOCK) best = gk[i] > best ? gk[i] : best;
         best = wave_max_u64(best);
         if (lane == 0) wbest[w] = best;
         __syncthreads();
-        unsigned long long bm = wbest[0];
-        for (int ww = 1; ww < 4; ++ww) bm = wbest[ww] > bm ? wbest[ww] : bm;
+        u64 bm = wbest[0];
+        for (int ww = 1; ww < NW; ++ww) bm = wbest[ww] > bm ? wbest[ww] : bm;
         if (bm == 0ull) break;                      // block-uniform
-        for (int i = threadIdx.x; i < ns; i += 256)
+        for (int i = threadIdx.x; i < ns; i += BLOCK)
           if (gk[i] == bm) gk[i] = 0ull;
         if (threadIdx.x == 0) fb[r] = rank_key_index(bm);
         __syncthreads();
       }
-      for (int rr = r + threadIdx.x; rr < a.b; rr += 256) fb[rr] = -1;
+      for (int rr = r + threadIdx.x; rr < a.b; rr += BLOCK) fb[rr] = -1;
       __syncthreads();
-      nf = compact_ids(fb, a.b, fa, wsum);
+      nf = compact_ids<BLOCK>(fb, a.b, fa, wsum);
     }
   }
   // leaf list: CSR row starts and exclusive prefix of member counts
   const int* offL = a.off[a.L - 1] + (size_t)h * (a.P[a.L - 1] + 1);
   int* lrow = a.leafrow + qh * a.nl_cap;
   int* lpre = a.leafpre + qh * (a.nl_cap + 1);
-  const int per = (nf + 255) / 256;
+  if (a.out_leaves) {
+    int* ol = a.out_leaves + qh * a.nl_cap;
+    for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) ol[i] = i < nf ? fa[i] : -1;
+  }
+  const int per = (nf + BLOCK - 1) / BLOCK;
   const int i0 = min(nf, (int)threadIdx.x * per), i1 = min(nf, i0 + per);
   int c = 0;
   for (int i = i0; i < i1; ++i) c += offL[fa[i] + 1] - offL[fa[i]];
   int total;
-  int run = block_exclusive_scan<256>(c, wsum, &total);
+  int run = block_exclusive_scan<BLOCK>(c, wsum, &total);
   for (int i = i0; i < i1; ++i) {
     const int leaf = fa[i];
-    lrow[i] = offL[leaf];
+    const int r0 = offL[leaf];
+    lrow[i] = r0;
     lpre[i] = run;
-    run += offL[leaf + 1] - offL[leaf];
+    fa[i] = r0;                 // from here on fa holds the leaves' first CSR rows
+    fb[i] = run;
+    run += offL[leaf + 1] - r0;
   }
   if (threadIdx.x == 0) {
     lpre[nf] = total;
+    fb[nf] = total;
     a.nleaf[qh] = nf;
   }
-  if (a.out_leaves) {
-    int* ol = a.out_leaves + qh * a.nl_cap;
-    for (int i = threadIdx.x; i < a.nl_cap; i += 256) ol[i] = i < nf ? fa[i] : -1;
+  if (!a.tau) return;
+  // Sampled threshold: score NS candidates spread evenly over the leaf list
+  // and keep the r-th best sample key, r chosen so that about 3k candidates
+  // are expected above it.  The gather appends only keys above this value;
+  // a query head that ends with fewer than k such keys is redone without it.
+  __syncthreads();
+  const int t = (int)(qh / a.Hq);
+  const int p = a.q_pos[t];
+  u64 tau = 0ull;
+  if (p >= 0 && (int64_t)p < a.N && (int64_t)total > 4 * (int64_t)a.k) {
+    const int NS = total < BLOCK ? total : BLOCK;
+    const int r = (int)((3LL * a.k * NS + total - 1) / total);
+    u64 key = 0ull;
+    if ((int)threadIdx.x < NS) {
+      const int64_t o = (int64_t)threadIdx.x * total / NS;
+      int lo_i = 0, hi_i = nf;   // fb[lo_i] <= o < fb[hi_i]
+      while (hi_i - lo_i > 1) {
+        const int mid = (lo_i + hi_i) >> 1;
+        if (fb[mid] <= o) lo_i = mid; else hi_i = mid;
+      }
+      const int64_t row = fa[lo_i] + (o - fb[lo_i]);
+      const int j = a.perm[(size_t)h * a.N + row];
+      if (j >= a.sink && j <= p - a.window)
+        key = rank_key(row_dot<LT, DL>((const LT*)a.lat + ((size_t)h * a.N + row) * DL, q), j);
+    }
+    sk[threadIdx.x] = key;
+    int nvalid;
+    block_exclusive_scan<BLOCK>(key != 0ull ? 1 : 0, wsum, &nvalid);
+    if (r < nvalid) tau = topk_compact<BLOCK, 1>(sk, BLOCK, r, &rs);
   }
+  if (threadIdx.x == 0) a.tau[qh] = tau;
+}
+
+// query latents (and a cleared append counter) for the flat scan
+template <typename KT, typename LT, int DL>
+__global__ __launch_bounds__(256) void qproj_kernel(SelArgs a) {
+  __shared__ float qin[256 + kQSlices * DL];
+  __shared__ float q[DL];
+  const int64_t qh = a.qh0 + blockIdx.x;
+  const int h = (int)(qh % a.Hq) / a.G;
+  query_latent<KT, LT, DL>(a, qh, h, qin, q);
+  if (threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -187,8 +301,8 @@ __global__ __launch_bounds__(256) void descend_kernel(SelArgs a) {
 // ---------------------------------------------------------------------------
 
 // Append the keys with pred set to the LDS buffer (one LDS atomic per wave).
-__device__ __forceinline__ void wave_append(bool pred, unsigned long long key, unsigned long long* buf, int* n) {
-  const uint64_t bal = __ballot(pred);
+__device__ __forceinline__ void wave_append(bool pred, u64 key, u64* buf, int* n) {
+  const u64 bal = __ballot(pred);
   if (bal == 0ull) return;
   int base = 0;
   if (lane_id() == 0) base = atomicAdd(n, __popcll(bal));
@@ -196,56 +310,72 @@ __device__ __forceinline__ void wave_append(bool pred, unsigned long long key, u
   if (pred) buf[base + mbcnt64(bal)] = key;
 }
 
+// Append the keys with pred[u] set (up to U <= 15 per lane) with one LDS
+// atomic per wave: the lane's exclusive offset comes from bit-plane ballots
+// of its count.
+template <int U>
+__device__ __forceinline__ void wave_append_many(const bool* pred, const u64* key, u64* buf, int* n) {
+  static_assert(U <= 15, "four bit planes");
+  constexpr int PL = U < 2 ? 1 : U < 4 ? 2 : U < 8 ? 3 : 4;
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) c += pred[u] ? 1 : 0;
+  int tot = 0, pre = 0;
+#pragma unroll
+  for (int b = 0; b < PL; ++b) {
+    const u64 bb = __ballot((c >> b) & 1);
+    tot += __popcll(bb) << b;
+    pre += (int)mbcnt64(bb) << b;
+  }
+  if (tot == 0) return;
+  int base = 0;
+  if (lane_id() == 0) base = atomicAdd(n, tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+  int pos = base + pre;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (pred[u]) buf[pos++] = key[u];
+}
+
+// Append this workgroup's n local keys to the query head's array.
+template <int BLOCK>
+__device__ void append_part(const SelArgs& a, int64_t qh, const u64* buf, int n, int* base_sh) {
+  if (threadIdx.x == 0) *base_sh = (int)atomicAdd(&a.part_n[qh], (unsigned)n);
+  __syncthreads();
+  u64* dst = a.part_keys + qh * a.part_cap + *base_sh;
+  for (int i = threadIdx.x; i < n; i += BLOCK) dst[i] = buf[i];
+}
+
 // ---------------------------------------------------------------------------
 // gather-and-score
 // ---------------------------------------------------------------------------
 
-template <typename LT, int DL, int M, int U>
-__global__ __launch_bounds__(256) void gather_kernel(SelArgs a) {
-  constexpr int BLOCK = 256;
+// Score candidates [lo, hi) of a query head's leaf list (CSR rows of KV head
+// h; lpre / lrow in LDS) and append the rank keys above thr to buf, keeping
+// at most the best k when the buffer fills (streaming radix-select
+// compaction).  Returns the number of keys left in buf.  Block-wide.
+template <typename LT, int DL, int M, int U, int BLOCK>
+__device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int chi, const int* lpre,
+                             const int* lrow, int nl, int64_t lo, int64_t hi, u64 thr, u64* buf, int* n_sh,
+                             RadixScratch* rs) {
+  constexpr int NW = BLOCK / 64;
   constexpr int CAP = M * BLOCK;
   constexpr int E = Lat<LT>::PER16;              // latent elements per lane load
   constexpr int LPK = DL / E;                    // lanes per key
   constexpr int KPW = 64 / LPK;                  // keys per wave per load
-  constexpr int ROUND = 4 * KPW * U;             // candidates per round
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ RadixScratch rs;
-  __shared__ int n_sh;
-  unsigned long long* buf = (unsigned long long*)smem;
-  int* lpre = (int*)(buf + CAP);
-  int* lrow = lpre + a.nl_cap + 1;
-
-  const int64_t qh = a.qh0 + blockIdx.y;
-  const int s = blockIdx.x;
-  const int t = (int)(qh / a.Hq), hq = (int)(qh % a.Hq), h = hq / a.G;
-  const int p = a.q_pos[t];
-  if (p < 0 || (int64_t)p >= a.N) {
-    if (a.S > 1) {
-      if (threadIdx.x == 0) a.part_cnt[qh * a.S + s] = 0;
-    } else {
-      write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
-    }
-    return;
-  }
-  const int clo = a.sink, chi = p - a.window;
-  const int nl = a.nleaf[qh];
-  for (int i = threadIdx.x; i <= nl; i += BLOCK) lpre[i] = a.leafpre[qh * (a.nl_cap + 1) + i];
-  for (int i = threadIdx.x; i < nl; i += BLOCK) lrow[i] = a.leafrow[qh * a.nl_cap + i];
-  if (threadIdx.x == 0) n_sh = 0;
-  __syncthreads();
-  const int64_t total = lpre[nl];
-  const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
+  constexpr int ROUND = NW * KPW * U;            // candidates per round
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lig = lane % LPK, g = lane / LPK;
-  const int64_t wlen = (hi - lo + 3) / 4;
+  if (threadIdx.x == 0) *n_sh = 0;
+  __syncthreads();
+  const int64_t wlen = (hi - lo + NW - 1) / NW;
   const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
-  float qv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) qv[e] = a.qlat[qh * DL + lig * E + e];
+  QSlice<LT> qv;
+  qv.load(a.qlat + qh * DL + lig * E);
   // first leaf of this wave's range (largest i with lpre[i] <= wlo)
   int cur = 0;
   {
-    int lo_i = 0, hi_i = nl;   // lpre[lo_i] <= wlo < lpre[hi_i]
+    int lo_i = 0, hi_i = nl;
     while (hi_i - lo_i > 1) {
       const int mid = (lo_i + hi_i) >> 1;
       if (lpre[mid] <= wlo) lo_i = mid; else hi_i = mid;
@@ -254,51 +384,93 @@ __global__ __launch_bounds__(256) void gather_kernel(SelArgs a) {
   }
   const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
   const int* permb = a.perm + (size_t)h * a.N;
-  unsigned long long thr = 0ull;
   const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
-  for (int64_t r = 0; r < rounds; ++r) {
-    uint4 v[U];
-    int idx[U];
-    bool ok[U];
+  const bool fits = hi - lo <= CAP;
+  uint4 v[U], vn[U];
+  int idx[U], idxn[U];
+  auto fetch = [&](int64_t r, uint4* vv, int* ii) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t o = wlo + (r * U + u) * KPW + g;
-      ok[u] = o < whi;
-      v[u] = make_uint4(0u, 0u, 0u, 0u);
-      idx[u] = -1;
-      if (ok[u]) {
+      vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      ii[u] = -1;
+      if (o < whi) {
         while (lpre[cur + 1] <= o) ++cur;
         const int64_t row = lrow[cur] + (o - lpre[cur]);
-        v[u] = *(const uint4*)(latb + row * DL + lig * E);
-        idx[u] = permb[row];
+        vv[u] = *(const uint4*)(latb + row * DL + lig * E);
+        ii[u] = permb[row];
       }
     }
+  };
+  if (rounds > 0) fetch(0, v, idx);
+  for (int64_t r = 0; r < rounds; ++r) {
+    if (r + 1 < rounds) fetch(r + 1, vn, idxn);
+    bool pr[U];
+    u64 ky[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float sc = group_sum<LPK>(Lat<LT>::dot16(v[u], qv));
-      const bool cand = ok[u] && lig == LPK - 1 && idx[u] >= clo && idx[u] <= chi;
-      const unsigned long long key = cand ? rank_key(sc, idx[u]) : 0ull;
-      wave_append(cand && key > thr, key, buf, &n_sh);
+      const float sc = group_sum_lead<LPK>(qv.dot(v[u]));
+      const bool cand = lig == 0 && idx[u] >= clo && idx[u] <= chi;
+      ky[u] = cand ? rank_key(sc, idx[u]) : 0ull;
+      pr[u] = cand && ky[u] > thr;
     }
+    wave_append_many<U>(pr, ky, buf, n_sh);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = vn[u];
+      idx[u] = idxn[u];
+    }
+    if (fits) continue;          // every candidate of the range fits: no compaction
     __syncthreads();
-    if (n_sh + ROUND > CAP) {
-      const int n = n_sh;
-      const unsigned long long t2 = topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-      if (threadIdx.x == 0) n_sh = a.k;
-      thr = t2;
+    if (*n_sh + ROUND > CAP) {
+      const int n = *n_sh;
+      thr = topk_compact<BLOCK, M>(buf, n, a.k, rs);
+      if (threadIdx.x == 0) *n_sh = a.k;
       __syncthreads();
     }
   }
   __syncthreads();
-  int n = n_sh;
+  return *n_sh;
+}
+
+template <typename LT, int DL, int M, int U, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
+  constexpr int CAP = M * BLOCK;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ RadixScratch rs;
+  __shared__ int n_sh, base_sh;
+  u64* buf = (u64*)smem;
+  int* lpre = (int*)(buf + CAP);
+  int* lrow = lpre + a.nl_cap + 1;
+
+  const int64_t qh = a.qh0 + blockIdx.y;
+  const int s = blockIdx.x;
+  const int t = (int)(qh / a.Hq), hq = (int)(qh % a.Hq), h = hq / a.G;
+  const int p = a.q_pos[t];
+  if (p < 0 || (int64_t)p >= a.N) {
+    if (a.S == 1)
+      write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    return;
+  }
+  const int clo = a.sink, chi = p - a.window;
+  const int nl = a.nleaf[qh];
+  for (int i = threadIdx.x; i <= nl; i += BLOCK) lpre[i] = a.leafpre[qh * (a.nl_cap + 1) + i];
+  for (int i = threadIdx.x; i < nl; i += BLOCK) lrow[i] = a.leafrow[qh * a.nl_cap + i];
+  __syncthreads();
+  const int64_t total = lpre[nl];
+  const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
+  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
+  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs);
+  if (a.S == 1 && n < a.k && thr0 != 0ull) {
+    // the sampled threshold let fewer than k keys through: redo without it
+    n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs);
+  }
   if (n > a.k) {
     topk_compact<BLOCK, M>(buf, n, a.k, &rs);
     n = a.k;
   }
   if (a.S > 1) {
-    unsigned long long* dst = a.part_keys + (qh * a.S + s) * (int64_t)a.k;
-    for (int i = threadIdx.x; i < n; i += BLOCK) dst[i] = buf[i];
-    if (threadIdx.x == 0) a.part_cnt[qh * a.S + s] = n;
+    append_part<BLOCK>(a, qh, buf, n, &base_sh);
   } else {
     write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
                                a.out_scores ? a.out_scores + qh * a.k : nullptr);
@@ -306,17 +478,57 @@ __global__ __launch_bounds__(256) void gather_kernel(SelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// merge of the S partial lists of one query head
+// merge: streaming top-k over a query head's appended local lists
 // ---------------------------------------------------------------------------
 
-template <int M>
-__global__ __launch_bounds__(256) void merge_kernel(SelArgs a) {
-  constexpr int BLOCK = 256;
+// Two histogram passes over the keys (12-bit digits of the rank key, from the
+// top) find a prefix that every key of the best k reaches; one more pass
+// appends only the keys at or above it, and the streaming compaction picks
+// the exact best k among them.
+template <int BLOCK>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, int* wsum, int* d_out,
+                                           uint32_t* above_out, uint32_t* hd_out) {
+  // thread t owns bins [4t, 4t+4); counts above a bin come from a scan that
+  // runs from the highest thread down
+  constexpr int PER = 4096 / BLOCK;
+  const int t = threadIdx.x;
+  uint32_t hb[PER];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hb[i] = hist[t * PER + i];
+    s += hb[i];
+  }
+  int total;
+  // exclusive scan in reversed thread order = keys in bins of higher threads
+  const int rev_t = BLOCK - 1 - t;
+  (void)rev_t;
+  const uint32_t above_t = (uint32_t)block_exclusive_scan_rev<BLOCK>((int)s, wsum, &total);
+  if (above_t < need && need <= above_t + s) {
+    uint32_t acc = above_t;
+    for (int i = PER - 1; i >= 0; --i) {
+      if (acc + hb[i] >= need) {
+        *d_out = t * PER + i;
+        *above_out = acc;
+        *hd_out = hb[i];
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  __syncthreads();
+}
+
+template <typename LT, int DL, int BLOCK, int M>
+__global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   constexpr int CAP = M * BLOCK;
+  constexpr int R = 8;                       // loads in flight per thread
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ RadixScratch rs;
-  __shared__ int n_sh;
-  unsigned long long* buf = (unsigned long long*)smem;
+  __shared__ uint32_t hist[4096];
+  __shared__ int n_sh, d_sh;
+  __shared__ uint32_t above_sh, hd_sh;
+  u64* buf = (u64*)smem;
   const int64_t qh = a.qh0 + blockIdx.x;
   const int t = (int)(qh / a.Hq);
   const int p = a.q_pos[t];
@@ -324,24 +536,83 @@ __global__ __launch_bounds__(256) void merge_kernel(SelArgs a) {
     write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
   }
+  const int n_in = (int)a.part_n[qh];
+  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
+  if (n_in < a.k && thr0 != 0ull && a.nleaf) {
+    // the sampled threshold let fewer than k keys through: score every
+    // candidate of this query head here, without it
+    int* lpre = (int*)(buf + CAP);
+    int* lrow = lpre + a.nl_cap + 1;
+    const int nl = a.nleaf[qh];
+    for (int i = threadIdx.x; i <= nl; i += BLOCK) lpre[i] = a.leafpre[qh * (a.nl_cap + 1) + i];
+    for (int i = threadIdx.x; i < nl; i += BLOCK) lrow[i] = a.leafrow[qh * a.nl_cap + i];
+    __syncthreads();
+    const int h = (int)(qh % a.Hq) / a.G;
+    int n = gather_stream<LT, DL, M, 4, BLOCK>(a, qh, h, a.sink, p - a.window, lpre, lrow, nl, 0, lpre[nl], 0ull,
+                                               buf, &n_sh, &rs);
+    if (n > a.k) {
+      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+      n = a.k;
+    }
+    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
+                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    return;
+  }
+  const u64* src = a.part_keys + qh * a.part_cap;
+  u64 lowest = 0ull;                         // keys below this are never needed
+  if (n_in > 8 * a.k) {
+    uint32_t need = (uint32_t)a.k;
+    u64 prefix = 0ull;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = 52 - 12 * pass;
+      const u64 pmask = pass == 0 ? 0ull : (0xFFFull << 52);
+      for (int i = threadIdx.x; i < 4096; i += BLOCK) hist[i] = 0u;
+      __syncthreads();
+      for (int base = 0; base < n_in; base += BLOCK * R) {
+        u64 v[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int e = base + j * BLOCK + threadIdx.x;
+          v[j] = e < n_in ? src[e] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (v[j] != 0ull && (v[j] & pmask) == prefix) atomicAdd(&hist[(uint32_t)(v[j] >> shift) & 0xFFFu], 1u);
+      }
+      __syncthreads();
+      find_digit<BLOCK>(hist, need, rs.wsum, &d_sh, &above_sh, &hd_sh);
+      prefix |= (u64)d_sh << shift;
+      need -= above_sh;
+      const bool done = hd_sh == need;
+      __syncthreads();
+      if (done || pass == 1) break;
+    }
+    lowest = prefix;                         // the best k all have key >= prefix
+  }
   if (threadIdx.x == 0) n_sh = 0;
   __syncthreads();
-  unsigned long long thr = 0ull;
-  for (int s = 0; s < a.S; ++s) {
-    const int cnt = a.part_cnt[qh * a.S + s];
-    if (n_sh + cnt > CAP) {           // block-uniform (n_sh read after a barrier)
-      thr = topk_compact<BLOCK, M>(buf, n_sh, a.k, &rs);
-      if (threadIdx.x == 0) n_sh = a.k;
-      __syncthreads();
+  u64 thr = lowest == 0ull ? 0ull : lowest - 1ull;
+  for (int base = 0; base < n_in; base += BLOCK * R) {
+    u64 v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = base + j * BLOCK + threadIdx.x;
+      v[j] = e < n_in ? src[e] : 0ull;
     }
-    const unsigned long long* src = a.part_keys + (qh * a.S + s) * (int64_t)a.k;
-    for (int i0 = 0; i0 < cnt; i0 += BLOCK) {
-      const int i = i0 + threadIdx.x;
-      const unsigned long long key = i < cnt ? src[i] : 0ull;
-      wave_append(key > thr, key, buf, &n_sh);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      wave_append(v[j] > thr, v[j], buf, &n_sh);
+      if ((j & 1) == 1) {                    // room check every two appends
+        __syncthreads();
+        if (n_sh + 2 * BLOCK > CAP) {
+          thr = topk_compact<BLOCK, M>(buf, n_sh, a.k, &rs);
+          if (threadIdx.x == 0) n_sh = a.k;
+          __syncthreads();
+        }
+      }
     }
-    __syncthreads();
   }
+  __syncthreads();
   int n = n_sh;
   if (n > a.k) {
     topk_compact<BLOCK, M>(buf, n, a.k, &rs);
@@ -356,8 +627,8 @@ __global__ __launch_bounds__(256) void merge_kernel(SelArgs a) {
 // ---------------------------------------------------------------------------
 
 template <typename LT, int DL, int M, int U, int NQ>
-__global__ __launch_bounds__(512) void flat_kernel(SelArgs a) {
-  constexpr int BLOCK = 512, NW = BLOCK / 64;
+__global__ __launch_bounds__(1024) void flat_kernel(SelArgs a) {
+  constexpr int BLOCK = 1024, NW = BLOCK / 64;
   constexpr int CAP = M * BLOCK;
   constexpr int E = Lat<LT>::PER16;
   constexpr int LPK = DL / E;
@@ -366,31 +637,27 @@ __global__ __launch_bounds__(512) void flat_kernel(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ RadixScratch rs;
   __shared__ int n_sh[NQ];
-  unsigned long long* bufs = (unsigned long long*)smem;   // NQ x CAP
+  __shared__ int base_sh;
+  u64* bufs = (u64*)smem;   // NQ x CAP
 
   const int s = blockIdx.x;
   const int t = blockIdx.y / a.Hkv, h = blockIdx.y % a.Hkv;
   const int p = a.q_pos[t];
   const int64_t qh_base = (int64_t)t * a.Hq + (int64_t)h * a.G;
   if (p < 0 || (int64_t)p >= a.N) {
-    for (int j = 0; j < NQ; ++j) {
-      const int64_t qh = qh_base + j;
-      if (a.S > 1) {
-        if (threadIdx.x == 0) a.part_cnt[qh * a.S + s] = 0;
-      } else {
+    if (a.S == 1)
+      for (int j = 0; j < NQ; ++j) {
+        const int64_t qh = qh_base + j;
         write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
       }
-    }
     return;
   }
   const int clo = a.sink, chi = p - a.window;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lig = lane % LPK, g = lane / LPK;
-  float qv[NQ][E];
+  QSlice<LT> qv[NQ];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j)
-#pragma unroll
-    for (int e = 0; e < E; ++e) qv[j][e] = a.qlat[(qh_base + j) * DL + lig * E + e];
+  for (int j = 0; j < NQ; ++j) qv[j].load(a.qlat + (qh_base + j) * DL + lig * E);
   if (threadIdx.x < NQ) n_sh[threadIdx.x] = 0;
   __syncthreads();
   const int64_t lo = a.N * s / a.S, hi = a.N * (s + 1) / a.S;
@@ -398,34 +665,46 @@ __global__ __launch_bounds__(512) void flat_kernel(SelArgs a) {
   const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
   const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
   const int* permb = a.perm + (size_t)h * a.N;
-  unsigned long long thr[NQ];
+  u64 thr[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) thr[j] = 0ull;
   const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
-  for (int64_t r = 0; r < rounds; ++r) {
-    uint4 v[U];
-    int idx[U];
-    bool ok[U];
+  uint4 v[U], vn[U];
+  int idx[U], idxn[U];
+  auto fetch = [&](int64_t r, uint4* vv, int* ii) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = wlo + (r * U + u) * KPW + g;
-      ok[u] = row < whi;
-      v[u] = make_uint4(0u, 0u, 0u, 0u);
-      idx[u] = -1;
-      if (ok[u]) {
-        v[u] = *(const uint4*)(latb + row * DL + lig * E);
-        idx[u] = permb[row];
+      vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      ii[u] = -1;
+      if (row < whi) {
+        vv[u] = *(const uint4*)(latb + row * DL + lig * E);
+        ii[u] = permb[row];
       }
+    }
+  };
+  if (rounds > 0) fetch(0, v, idx);
+  for (int64_t r = 0; r < rounds; ++r) {
+    if (r + 1 < rounds) fetch(r + 1, vn, idxn);
+    bool cand[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cand[u] = lig == 0 && idx[u] >= clo && idx[u] <= chi;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      bool pr[U];
+      u64 ky[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float sc = group_sum_lead<LPK>(qv[j].dot(v[u]));
+        ky[u] = cand[u] ? rank_key(sc, idx[u]) : 0ull;
+        pr[u] = cand[u] && ky[u] > thr[j];
+      }
+      wave_append_many<U>(pr, ky, bufs + j * CAP, &n_sh[j]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool cand = ok[u] && lig == LPK - 1 && idx[u] >= clo && idx[u] <= chi;
-#pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        const float sc = group_sum<LPK>(Lat<LT>::dot16(v[u], qv[j]));
-        const unsigned long long key = cand ? rank_key(sc, idx[u]) : 0ull;
-        wave_append(cand && key > thr[j], key, bufs + j * CAP, &n_sh[j]);
-      }
+      v[u] = vn[u];
+      idx[u] = idxn[u];
     }
     __syncthreads();
 #pragma unroll
@@ -441,16 +720,14 @@ __global__ __launch_bounds__(512) void flat_kernel(SelArgs a) {
   __syncthreads();
   for (int j = 0; j < NQ; ++j) {
     const int64_t qh = qh_base + j;
-    unsigned long long* buf = bufs + j * CAP;
+    u64* buf = bufs + j * CAP;
     int n = n_sh[j];
     if (n > a.k) {
       topk_compact<BLOCK, M>(buf, n, a.k, &rs);
       n = a.k;
     }
     if (a.S > 1) {
-      unsigned long long* dst = a.part_keys + (qh * a.S + s) * (int64_t)a.k;
-      for (int i = threadIdx.x; i < n; i += BLOCK) dst[i] = buf[i];
-      if (threadIdx.x == 0) a.part_cnt[qh * a.S + s] = n;
+      append_part<BLOCK>(a, qh, buf, n, &base_sh);
     } else {
       write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
                                  a.out_scores ? a.out_scores + qh * a.k : nullptr);
@@ -463,9 +740,6 @@ __global__ __launch_bounds__(512) void flat_kernel(SelArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 
-int launch_project_queries(const lsa_index_desc& d, const void* queries, int32_t T, int32_t Hq, const float* W,
-                           float* out, hipStream_t st);
-
 namespace {
 
 int ipow(int b, int e) {
@@ -474,12 +748,16 @@ int ipow(int b, int e) {
   return r;
 }
 
-// entries per thread of the streaming buffer: capacity >= 2k
-int pick_m(int k, int block) {
+// entries per thread of a streaming buffer whose capacity must reach `need`
+int pick_m(int need, int block) {
   int m = 1;
-  while (m * block < 2 * k) m <<= 1;
+  while (m * block < need) m <<= 1;
   return m;
 }
+
+constexpr int kMergeBlock = 1024;
+constexpr int kSplitM = 8;                 // 1024-thread split buffer: 8192 keys
+constexpr int kFlatU = 4;
 
 struct SelWs {
   float* qlat;
@@ -487,7 +765,8 @@ struct SelWs {
   int* leafpre;
   int* nleaf;
   unsigned long long* part_keys;
-  int* part_cnt;
+  unsigned int* part_n;
+  unsigned long long* tau;
 };
 
 size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& pl, int32_t T,
@@ -501,13 +780,16 @@ size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const S
     w.leafrow = c.take<int>((size_t)(qh * pl.nl_cap));
     w.leafpre = c.take<int>((size_t)(qh * (pl.nl_cap + 1)));
     w.nleaf = c.take<int>((size_t)qh);
+    w.tau = c.take<unsigned long long>((size_t)qh);
+  } else {
+    w.tau = nullptr;
   }
   const int S = flat ? pl.flat_splits : pl.splits;
   w.part_keys = nullptr;
-  w.part_cnt = nullptr;
+  w.part_n = nullptr;
   if (S > 1) {
     w.part_keys = c.take<unsigned long long>((size_t)(qh * S * p.k));
-    w.part_cnt = c.take<int>((size_t)(qh * S));
+    w.part_n = c.take<unsigned int>((size_t)qh);
   }
   if (out) *out = w;
   return align_up(c.used);
@@ -518,7 +800,27 @@ void allow_lds(KERNEL* k, size_t bytes) {
   if (bytes > 64 * 1024) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+template <typename LT, int DL, int M>
+void launch_merge(SelArgs a, int64_t QH, int64_t chunk, hipStream_t st) {
+  auto mk = merge_kernel<LT, DL, kMergeBlock, M>;
+  const size_t mlds = (size_t)M * kMergeBlock * 8 + ((size_t)a.nl_cap * 2 + 2) * 4;
+  allow_lds(mk, mlds);
+  for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
+    a.qh0 = q0;
+    const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
+    hipLaunchKernelGGL(mk, dim3((unsigned)nq), dim3(kMergeBlock), mlds, st, a);
+  }
+}
+
+// capacity >= k + four appends' room, and >= 2k so the final sort fits
 template <typename LT, int DL>
+void merge_all(const SelArgs& a, int k, int64_t QH, int64_t chunk, hipStream_t st) {
+  const int need = k + 4 * kMergeBlock > 2 * k ? k + 4 * kMergeBlock : 2 * k;
+  if (pick_m(need, kMergeBlock) <= 8) launch_merge<LT, DL, 8>(a, QH, chunk, st);
+  else launch_merge<LT, DL, 16>(a, QH, chunk, st);
+}
+
+template <typename KT, typename LT, int DL>
 int run_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& pl, const void* index,
                const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, bool flat, char* err,
@@ -527,11 +829,6 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   const char* blob = (const char*)index;
   SelWs w;
   carve_select(d, p, pl, T, Hq, flat, ws, &w);
-  int rc = launch_project_queries(d, queries, T, Hq, (const float*)(blob + L.W), w.qlat, st);
-  if (rc != LSA_OK) {
-    snprintf(err, errlen, "query projection launch failed");
-    return rc;
-  }
   SelArgs a;
   memset(&a, 0, sizeof(a));
   a.lat = blob + L.latent;
@@ -541,6 +838,9 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   a.G = Hq / d.n_kv_heads;
   a.Hq = Hq;
   a.T = T;
+  a.d_head = d.d_head;
+  a.queries = queries;
+  a.W = (const float*)(blob + L.W);
   a.qlat = w.qlat;
   a.q_pos = q_pos;
   a.sink = p.sink;
@@ -562,12 +862,12 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   a.nleaf = w.nleaf;
   a.out_leaves = out_leaves;
   a.part_keys = w.part_keys;
-  a.part_cnt = w.part_cnt;
+  a.part_n = w.part_n;
+  a.tau = w.tau;
   a.out_idx = out_idx;
   a.out_scores = out_scores;
   a.qh0 = 0;
   const int64_t QH = (int64_t)T * Hq;
-  const int M = pick_m(p.k, 256);
 
 #define LSA_CHECK(what)                                                              \
   do {                                                                               \
@@ -581,71 +881,101 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   const int64_t chunk = 32768;   // query heads per grid (grid.y limit)
   if (!flat) {
     a.S = pl.splits;
-    const size_t dlds = align_up((size_t)pl.nl_cap * 2 * 4 + 8, 16) +
-                        (p.beam == LSA_BEAM_GLOBAL ? (size_t)p.b * 256 * 8 : 0);
-    auto dk = descend_kernel<LT, DL>;
+    a.part_cap = (int64_t)a.S * p.k;
+    constexpr int DB = 1024;
+    const size_t dlds = ((size_t)(2 * pl.nl_cap + 1) * 4 + 7) / 8 * 8 +
+                        (p.beam == LSA_BEAM_GLOBAL ? (size_t)p.b * 256 * 8 : 0) + (size_t)DB * 8;
+    auto dk = descend_kernel<KT, LT, DL, DB>;
     allow_lds(dk, dlds);
+    prof_begin(LSA_STAGE_DESCEND, st);
     for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
       a.qh0 = q0;
       const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
-      hipLaunchKernelGGL(dk, dim3((unsigned)nq), dim3(256), dlds, st, a);
+      hipLaunchKernelGGL(dk, dim3((unsigned)nq), dim3(DB), dlds, st, a);
     }
+    prof_end(LSA_STAGE_DESCEND, st);
     LSA_CHECK("descend");
-    constexpr int U = 4;
-#define LSA_GATHER(MV)                                                                          \
+    constexpr int U = 8;
+    const int GB = 256;
+    const int KPWG = 64 / (DL * (int)sizeof(LT) / 16);
+    const int needg = p.k + (GB / 64) * KPWG * U > 2 * p.k ? p.k + (GB / 64) * KPWG * U : 2 * p.k;
+    const int M = pick_m(needg, GB);
+#define LSA_GATHER(MV, BV)                                                                      \
   {                                                                                             \
-    auto gk = gather_kernel<LT, DL, MV, U>;                                                     \
-    const size_t glds = (size_t)MV * 256 * 8 + ((size_t)pl.nl_cap * 2 + 2) * 4;                 \
+    auto gk = gather_kernel<LT, DL, MV, U, BV>;                                                 \
+    const size_t glds = (size_t)MV * BV * 8 + ((size_t)pl.nl_cap * 2 + 2) * 4;                  \
     allow_lds(gk, glds);                                                                        \
+    prof_begin(LSA_STAGE_GATHER, st);                                                           \
     for (int64_t q0 = 0; q0 < QH; q0 += chunk) {                                                \
       a.qh0 = q0;                                                                               \
       const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;                                     \
-      hipLaunchKernelGGL(gk, dim3((unsigned)a.S, (unsigned)nq), dim3(256), glds, st, a);        \
+      hipLaunchKernelGGL(gk, dim3((unsigned)a.S, (unsigned)nq), dim3(BV), glds, st, a);         \
     }                                                                                           \
-    if (a.S > 1) {                                                                              \
-      auto mk = merge_kernel<MV>;                                                               \
-      const size_t mlds = (size_t)MV * 256 * 8;                                                 \
-      allow_lds(mk, mlds);                                                                      \
-      for (int64_t q0 = 0; q0 < QH; q0 += chunk) {                                              \
-        a.qh0 = q0;                                                                             \
-        const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;                                   \
-        hipLaunchKernelGGL(mk, dim3((unsigned)nq), dim3(256), mlds, st, a);                     \
-      }                                                                                         \
-    }                                                                                           \
+    prof_end(LSA_STAGE_GATHER, st);                                                             \
   }
-    switch (M) {
-      case 1: case 2: LSA_GATHER(2) break;
-      case 4: LSA_GATHER(4) break;
-      case 8: LSA_GATHER(8) break;
-      case 16: LSA_GATHER(16) break;
-      default: LSA_GATHER(32) break;
+    if (GB == 1024) {
+      switch (M) {
+        case 1: case 2: LSA_GATHER(2, 1024) break;
+        case 4: LSA_GATHER(4, 1024) break;
+        default: LSA_GATHER(8, 1024) break;
+      }
+    } else {
+      switch (M) {
+        case 1: case 2: LSA_GATHER(2, 256) break;
+        case 4: LSA_GATHER(4, 256) break;
+        case 8: LSA_GATHER(8, 256) break;
+        case 16: LSA_GATHER(16, 256) break;
+        default: LSA_GATHER(32, 256) break;
+      }
     }
 #undef LSA_GATHER
     LSA_CHECK("gather");
+    if (a.S > 1) {
+      prof_begin(LSA_STAGE_MERGE, st);
+      merge_all<LT, DL>(a, p.k, QH, chunk, st);
+      prof_end(LSA_STAGE_MERGE, st);
+      LSA_CHECK("merge");
+    }
     return LSA_OK;
   }
   // flat
   a.S = pl.flat_splits;
+  a.part_cap = (int64_t)a.S * p.k;
   const int G = a.G;
-  const int MF = pick_m(p.k, 512);
+  prof_begin(LSA_STAGE_PROJECT, st);
+  for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
+    a.qh0 = q0;
+    const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
+    hipLaunchKernelGGL((qproj_kernel<KT, LT, DL>), dim3((unsigned)nq), dim3(256), 0, st, a);
+  }
+  prof_end(LSA_STAGE_PROJECT, st);
+  a.qh0 = 0;
+  LSA_CHECK("query projection");
+  const int KPWF = 64 / (DL * (int)sizeof(LT) / 16);
+  const int needf = p.k + 16 * KPWF * kFlatU > 2 * p.k ? p.k + 16 * KPWF * kFlatU : 2 * p.k;
+  const int MF = pick_m(needf, 1024);
   const int64_t TH = (int64_t)T * d.n_kv_heads;
   const int64_t fchunk = (chunk / d.n_kv_heads) * d.n_kv_heads;   // whole tokens per grid
-  constexpr int UF = 4;
 #define LSA_FLAT(MV, NQV)                                                                         \
   {                                                                                               \
-    auto fk = flat_kernel<LT, DL, MV, UF, NQV>;                                                   \
-    const size_t flds = (size_t)NQV * MV * 512 * 8;                                               \
+    auto fk = flat_kernel<LT, DL, MV, kFlatU, NQV>;                                               \
+    const size_t flds = (size_t)NQV * MV * 1024 * 8;                                              \
+    if (flds > 160 * 1024) {                                                                      \
+      snprintf(err, errlen, "flat scan: k = %d with %d query heads per KV head exceeds LDS", p.k, NQV); \
+      return LSA_ERR_UNSUPPORTED;                                                                 \
+    }                                                                                             \
     allow_lds(fk, flds);                                                                          \
     for (int64_t r0 = 0; r0 < TH; r0 += fchunk) {                                                 \
       const int64_t nr = TH - r0 < fchunk ? TH - r0 : fchunk;                                     \
       SelArgs b2 = a;                                                                             \
-      b2.q_pos = a.q_pos + r0 / d.n_kv_heads;                                                     \
-      b2.qlat = a.qlat + (r0 / d.n_kv_heads) * (int64_t)Hq * DL;                                  \
-      b2.out_idx = a.out_idx + (r0 / d.n_kv_heads) * (int64_t)Hq * a.width;                       \
-      b2.out_scores = a.out_scores ? a.out_scores + (r0 / d.n_kv_heads) * (int64_t)Hq * a.k : nullptr; \
-      b2.part_keys = a.part_keys ? a.part_keys + (r0 / d.n_kv_heads) * (int64_t)Hq * a.S * a.k : nullptr; \
-      b2.part_cnt = a.part_cnt ? a.part_cnt + (r0 / d.n_kv_heads) * (int64_t)Hq * a.S : nullptr;  \
-      hipLaunchKernelGGL(fk, dim3((unsigned)a.S, (unsigned)nr), dim3(512), flds, st, b2);         \
+      const int64_t t0 = r0 / d.n_kv_heads;                                                       \
+      b2.q_pos = a.q_pos + t0;                                                                    \
+      b2.qlat = a.qlat + t0 * (int64_t)Hq * DL;                                                   \
+      b2.out_idx = a.out_idx + t0 * (int64_t)Hq * a.width;                                        \
+      b2.out_scores = a.out_scores ? a.out_scores + t0 * (int64_t)Hq * a.k : nullptr;             \
+      b2.part_keys = a.part_keys ? a.part_keys + t0 * (int64_t)Hq * a.part_cap : nullptr;         \
+      b2.part_n = a.part_n ? a.part_n + t0 * (int64_t)Hq : nullptr;                               \
+      hipLaunchKernelGGL(fk, dim3((unsigned)a.S, (unsigned)nr), dim3(1024), flds, st, b2);        \
     }                                                                                             \
   }
 #define LSA_FLAT_NQ(MV)                                                        \
@@ -655,35 +985,21 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
     case 4: LSA_FLAT(MV, 4) break;                                             \
     default: snprintf(err, errlen, "flat scan supports 1, 2 or 4 query heads per KV head"); return LSA_ERR_UNSUPPORTED; \
   }
+  prof_begin(LSA_STAGE_FLAT, st);
   switch (MF) {
     case 1: LSA_FLAT_NQ(1) break;
     case 2: LSA_FLAT_NQ(2) break;
     case 4: LSA_FLAT_NQ(4) break;
     default: LSA_FLAT_NQ(8) break;
   }
+  prof_end(LSA_STAGE_FLAT, st);
 #undef LSA_FLAT_NQ
 #undef LSA_FLAT
   LSA_CHECK("flat scan");
   if (a.S > 1) {
-#define LSA_MERGE(MV)                                                                   \
-  {                                                                                     \
-    auto mk = merge_kernel<MV>;                                                         \
-    const size_t mlds = (size_t)MV * 256 * 8;                                           \
-    allow_lds(mk, mlds);                                                                \
-    for (int64_t q0 = 0; q0 < QH; q0 += chunk) {                                        \
-      a.qh0 = q0;                                                                       \
-      const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;                             \
-      hipLaunchKernelGGL(mk, dim3((unsigned)nq), dim3(256), mlds, st, a);               \
-    }                                                                                   \
-  }
-    switch (M) {
-      case 1: case 2: LSA_MERGE(2) break;
-      case 4: LSA_MERGE(4) break;
-      case 8: LSA_MERGE(8) break;
-      case 16: LSA_MERGE(16) break;
-      default: LSA_MERGE(32) break;
-    }
-#undef LSA_MERGE
+    prof_begin(LSA_STAGE_MERGE, st);
+    merge_all<LT, DL>(a, p.k, QH, chunk, st);
+    prof_end(LSA_STAGE_MERGE, st);
     LSA_CHECK("merge");
   }
   return LSA_OK;
@@ -699,17 +1015,23 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   const Layout L = compute_layout(d);
   const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
   const double expect = avg_leaf * pl.nl_cap;
+  // a few query heads: split each over S workgroups so the chip fills; a
+  // split should hold >= 2k candidates (its local top-k then shrinks the
+  // merge input) and, on average, fit the split buffer with room to spare
+  // few query heads: split each over S workgroups so the chip fills (a few
+  // workgroups per CU); the sampled threshold keeps every split's append
+  // list short
   int S = 1;
-  if (pl.qh < 2048) {
-    S = (int)((2048 + pl.qh - 1) / pl.qh);
-    const int by_work = (int)(expect / 512.0);
+  if (pl.qh < 1024) {
+    S = (int)((1024 + pl.qh - 1) / pl.qh);
+    const int by_work = (int)(expect / 1024.0);
     S = S < by_work ? S : by_work;
-    S = S < 1 ? 1 : (S > 256 ? 256 : S);
+    S = S < 1 ? 1 : (S > 64 ? 64 : S);
   }
   pl.splits = S;
   const int64_t th = (int64_t)T * d.n_kv_heads;
-  int64_t sf = (512 + th - 1) / th;
-  const int64_t by_rows = d.n_keys / 4096;
+  int64_t sf = (256 + th - 1) / th;
+  const int64_t by_rows = d.n_keys / 8192;
   sf = sf < by_rows ? sf : by_rows;
   sf = sf < 1 ? 1 : (sf > 1024 ? 1024 : sf);
   pl.flat_splits = (int)sf;
@@ -721,13 +1043,20 @@ int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const Sel
                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                   float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, bool flat, char* err,
                   size_t errlen) {
-  const bool lb = d.latent_dtype == LSA_BF16;
+  const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
+#define LSA_RUN(KT, LT, DLV) \
+  return run_select<KT, LT, DLV>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen)
   if (d.d_latent == 64) {
-    if (lb) return run_select<bf16_t, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen);
-    return run_select<float, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen);
+    if (kb && lb) LSA_RUN(bf16_t, bf16_t, 64);
+    if (kb) LSA_RUN(bf16_t, float, 64);
+    if (lb) LSA_RUN(float, bf16_t, 64);
+    LSA_RUN(float, float, 64);
   }
-  if (lb) return run_select<bf16_t, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen);
-  return run_select<float, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen);
+  if (kb && lb) LSA_RUN(bf16_t, bf16_t, 32);
+  if (kb) LSA_RUN(bf16_t, float, 32);
+  if (lb) LSA_RUN(float, bf16_t, 32);
+  LSA_RUN(float, float, 32);
+#undef LSA_RUN
 }
 
 }  // namespace lsa

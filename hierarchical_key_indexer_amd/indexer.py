@@ -49,6 +49,18 @@ class LatentIndex:
             lv = torch.empty((t, hq, nl), dtype=torch.int32, device=self.device)
         return idx, sc, lv
 
+    def leaf_counts(self):
+        """Members of every leaf bucket, [Hkv, P_L] int64 (host), read from the
+        blob: the header holds the byte offset of each level's CSR offsets."""
+        import numpy as np
+        L = self.desc.n_levels
+        hdr = self.index[:256].cpu().numpy()
+        off = int(hdr[168 + 8 * (L - 1):176 + 8 * (L - 1)].view(np.uint64)[0])
+        nodes = int(np.prod([self.desc.fanout[i] for i in range(L)]))
+        hk = self.desc.n_kv_heads
+        sec = self.index[off:off + hk * (nodes + 1) * 4].view(torch.int32).view(hk, nodes + 1)
+        return np.diff(sec.cpu().numpy().astype(np.int64), axis=1)
+
     def flat_select(self, queries, q_pos, params, scores=True, out=None, stream=None):
         t, hq = queries.shape[0], queries.shape[1]
         ws = self.workspace("flat", _abi.flat_workspace_bytes(self.desc, params, t, hq))

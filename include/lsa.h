@@ -187,6 +187,22 @@ int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* q
                     const lsa_select_params* params, int32_t* out_idx, float* out_scores,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Stages of a select call that can be timed by the caller. */
+typedef enum {
+  LSA_STAGE_PROJECT = 1, /* query latent projection                         */
+  LSA_STAGE_DESCEND = 2, /* centroid scoring and descent                    */
+  LSA_STAGE_GATHER = 3,  /* gather-and-score with top-k (lsa_select)       */
+  LSA_STAGE_MERGE = 4,   /* merge of split top-k lists                      */
+  LSA_STAGE_FLAT = 5     /* full scan with top-k (lsa_flat_select)         */
+} lsa_stage;
+
+/* Instrumentation: until reset, every lsa_select / lsa_flat_select call on
+ * this thread records `start` (a hipEvent_t) on its stream before the first
+ * kernel of `stage` and `stop` after the last one.  NULL events switch the
+ * stage off.  Nothing is allocated and nothing synchronises; the caller owns
+ * the events. */
+int lsa_set_profile_events(int32_t stage, void* start, void* stop);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next lsa_* call on the same thread. */
 const char* lsa_last_error(void);
