@@ -125,10 +125,50 @@ __device__ int compact_ids(const int* src, int ns, int* dst, int* wsum) {
   return total;
 }
 
-__device__ __forceinline__ u64 readlane_u64(u64 v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((u64)hi << 32) | lo;
+// Mark the `need` largest of the unique nonzero keys the wave holds (J per
+// lane): bit-serial radix select with ballots, from the top bit down, until
+// the undecided keys are exactly the ones still needed.  in[j] gets the
+// selected lanes of slot j.
+template <int J>
+__device__ __forceinline__ void wave_select_top(const u64* key, int need, u64* in) {
+  u64 cand[J];
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    cand[j] = __ballot(key[j] != 0ull);
+    in[j] = 0ull;
+    ncand += __popcll(cand[j]);
+  }
+  if (ncand <= need) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) in[j] = cand[j];
+    return;
+  }
+  int remaining = need;
+  for (int bit = 63; bit >= 0; --bit) {
+    u64 ones[J];
+    int c1 = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      ones[j] = __ballot((key[j] >> bit) & 1ull) & cand[j];
+      c1 += __popcll(ones[j]);
+    }
+    ncand = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (c1 >= remaining) {
+        cand[j] = ones[j];                   // the best `remaining` all have this bit
+      } else {
+        in[j] |= ones[j];                    // all of these are in
+        cand[j] &= ~ones[j];
+      }
+      ncand += __popcll(cand[j]);
+    }
+    if (c1 < remaining) remaining -= c1;
+    if (ncand == remaining) break;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) in[j] |= cand[j];
 }
 
 template <typename KT, typename LT, int DL, int BLOCK>
@@ -180,19 +220,17 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
           }
           nne += __popcll(__ballot(key[j] != 0ull));
         }
-        // rank of each key among the parent's children (keys are unique)
-        int rank[4] = {0, 0, 0, 0};
-        for (int jj = 0; jj < NJ; ++jj) {
-          for (int src = 0; src < 64; ++src) {
-            const u64 other = readlane_u64(key[jj], src);
+        // the parent's best bs children (keys are unique), kept in child order
+        u64 in[4];
+        wave_select_top<4>(key, bs, in);
+        int slot = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) rank[j] += other > key[j] ? 1 : 0;
-          }
+        for (int j = 0; j < 4; ++j) {
+          if ((in[j] >> lane) & 1ull) fb[i * bs + slot + (int)mbcnt64(in[j])] = rank_key_index(key[j]);
+          slot += __popcll(in[j]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (key[j] != 0ull && rank[j] < bs) fb[i * bs + rank[j]] = rank_key_index(key[j]);
         for (int r = min(nne, bs) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
+        (void)NJ;
       }
       __syncthreads();
       nf = compact_ids<BLOCK>(fb, nf * bs, fa, wsum);
@@ -262,25 +300,41 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   const int p = a.q_pos[t];
   u64 tau = 0ull;
   if (p >= 0 && (int64_t)p < a.N && (int64_t)total > 4 * (int64_t)a.k) {
-    const int NS = total < BLOCK ? total : BLOCK;
-    const int r = (int)((3LL * a.k * NS + total - 1) / total);
-    u64 key = 0ull;
-    if ((int)threadIdx.x < NS) {
-      const int64_t o = (int64_t)threadIdx.x * total / NS;
-      int lo_i = 0, hi_i = nf;   // fb[lo_i] <= o < fb[hi_i]
-      while (hi_i - lo_i > 1) {
-        const int mid = (lo_i + hi_i) >> 1;
-        if (fb[mid] <= o) lo_i = mid; else hi_i = mid;
-      }
-      const int64_t row = fa[lo_i] + (o - fb[lo_i]);
-      const int j = a.perm[(size_t)h * a.N + row];
-      if (j >= a.sink && j <= p - a.window)
-        key = rank_key(row_dot<LT, DL>((const LT*)a.lat + ((size_t)h * a.N + row) * DL, q), j);
+    // every wave scores 64 of BLOCK evenly spaced candidates and keeps its
+    // r-th best (r = expected share of 3k); tau is the median wave value
+    const int64_t NS = BLOCK;
+    const int r = (int)((3LL * a.k * 64 + total - 1) / total);
+    const int64_t o = (int64_t)threadIdx.x * total / NS;
+    int lo_i = 0, hi_i = nf;   // fb[lo_i] <= o < fb[hi_i]
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (fb[mid] <= o) lo_i = mid; else hi_i = mid;
     }
-    sk[threadIdx.x] = key;
-    int nvalid;
-    block_exclusive_scan<BLOCK>(key != 0ull ? 1 : 0, wsum, &nvalid);
-    if (r < nvalid) tau = topk_compact<BLOCK, 1>(sk, BLOCK, r, &rs);
+    const int64_t row = fa[lo_i] + (o - fb[lo_i]);
+    const int j = a.perm[(size_t)h * a.N + row];
+    const float sc = row_dot<LT, DL>((const LT*)a.lat + ((size_t)h * a.N + row) * DL, q);
+    u64 key[1] = {(j >= a.sink && j <= p - a.window) ? rank_key(sc, j) : 0ull};
+    const int nvalid = __popcll(__ballot(key[0] != 0ull));
+    u64 wt = 0ull;
+    if (r < nvalid) {
+      u64 in[1];
+      wave_select_top<1>(key, r, in);
+      wt = wave_min_u64(((in[0] >> lane) & 1ull) ? key[0] : ~0ull);
+    }
+    if (lane == 0) sk[w] = wt;
+    __syncthreads();
+    if (w == 0) {
+      // median of the NW wave values: lane i ranks value i (ties by lane)
+      const u64 x = lane < NW ? sk[lane] : ~0ull;
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const u64 o = __shfl(x, i, 64);
+        rank += (o < x || (o == x && i < lane)) ? 1 : 0;
+      }
+      if (lane < NW && rank == (NW - 1) / 2) a.tau[qh] = x;
+    }
+    return;
   }
   if (threadIdx.x == 0) a.tau[qh] = tau;
 }

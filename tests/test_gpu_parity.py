@@ -9,6 +9,7 @@ import pytest
 
 from oracle import lsa_oracle as O
 from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
+from tests.gpu_helpers import _abi, _blob_of, _dev, _li, gpu_build, gpu_select
 from tests.parity import check_build, compare_select, log
 
 pytestmark = pytest.mark.gpu
@@ -21,54 +22,6 @@ def _gpu():
         pytest.skip("no GPU")
     from hierarchical_key_indexer_amd import _abi
     _abi.load()
-
-
-def _abi():
-    from hierarchical_key_indexer_amd import _abi as A
-    return A
-
-
-def _li(desc_o: O.IndexDesc, blob=None):
-    from hierarchical_key_indexer_amd.indexer import LatentIndex
-    A = _abi()
-    d = A.IndexDesc.make(desc_o.n_keys, desc_o.n_kv_heads, desc_o.d_head, desc_o.d_latent, desc_o.key_dtype,
-                         desc_o.latent_dtype, desc_o.fanout, desc_o.kmeans_iters, desc_o.seed)
-    li = LatentIndex(d)
-    if blob is not None:
-        assert li.index.numel() == blob.size
-        li.index.copy_(torch.from_numpy(blob))
-    return li
-
-
-def _dev(arr):
-    from hierarchical_key_indexer_amd.indexer import keys_to_device
-    return keys_to_device(arr)
-
-
-def _params(prm: O.SelectParams):
-    return _abi().SelectParams.make(prm.b, prm.k, prm.sink, prm.window, prm.beam)
-
-
-def gpu_select(li, queries, pos, prm, flat=False, leaves=True):
-    q = _dev(queries)
-    p = torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).cuda()
-    if flat:
-        idx, sc, lv = li.flat_select(q, p, _params(prm))
-    else:
-        idx, sc, lv = li.select(q, p, _params(prm), leaves=leaves)
-    torch.cuda.synchronize()
-    return idx.cpu().numpy(), sc.cpu().numpy(), (None if lv is None else lv.cpu().numpy())
-
-
-def gpu_build(desc_o, keys, W):
-    li = _li(desc_o)
-    li.build(_dev(keys), torch.from_numpy(W).cuda())
-    torch.cuda.synchronize()
-    return li
-
-
-def _blob_of(li):
-    return li.index.cpu().numpy()
 
 
 def _small(name="decode_1m", **kw):
