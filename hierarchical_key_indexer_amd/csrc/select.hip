@@ -5,8 +5,8 @@
 // The 72.4x and 22.7x Speedups, and What They Compare Against"): a query
 // scores the bucket centroids first, drills into the selected buckets, and
 // attends to the selected long-range keys plus the attention sink and a local
-// window.  The full scan is the "old indexer" of the flowchart on "Latent
-// Sparse Attention: tree search over keys for 10M-token context".
+// window.  The full scan is the dashed, quadratic path of the flowchart on
+// "Latent Sparse Attention: tree search over keys for 10M-token context".
 //
 //   descend_kernel   one workgroup per query head: the query's latent
 //                    (round(q.W_h)), then level by level the children of every

@@ -177,8 +177,8 @@ int lsa_select(const lsa_index_desc* desc, const void* index, const void* querie
 size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
                                 int32_t n_tokens, int32_t n_q_heads);
 
-/* Full-scan baseline: the indexer that scores every key ("old indexer" of
- * the flowchart on "Latent Sparse Attention: tree search over keys for
+/* Full-scan baseline: the indexer that scores every key (the dashed, quadratic
+ * path of the flowchart on "Latent Sparse Attention: tree search over keys for
  * 10M-token context").  Same arguments and output rows as lsa_select, with
  * every key in [sink, p - window] a candidate; params->b and ->beam are
  * ignored.  Equal to lsa_select with b = fanout at every level. */

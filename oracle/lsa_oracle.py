@@ -157,9 +157,9 @@ def kmeans_init_positions(seed: int, head: int, level: int, node: int, m: int, f
 
 
 # ----------------------------------------------------------------------------
-# Lloyd k-means (the clustering that forms the buckets; the pages say keys are
-# "clustered into buckets ... organized as a hierarchy", "How does LSA work?"
-# step 1, and name no algorithm; Lloyd's two-step iteration is the reading)
+# Lloyd k-means (the clustering that forms the buckets: step 1 of "How does
+# LSA work?" groups keys into a hierarchy of buckets in latent space but names
+# no algorithm; Lloyd's two-step iteration is the reading)
 # ----------------------------------------------------------------------------
 
 
@@ -418,8 +418,8 @@ def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectPa
 
     Candidates are the members of the selected leaves (all keys when ``flat``)
     that fall in C(p); each is scored s_j = q~ . k~_j; the top-k by (s desc,
-    j asc) are kept ("scores the keys within the selected clusters", Wink
-    Pings).  Fewer than k candidates: all of them.  ``leaves`` replaces the
+    j asc) are kept (Wink Pings: after the clusters are scored, only the keys
+    inside the chosen clusters are scored).  Fewer than k candidates: all of them.  ``leaves`` replaces the
     descent by a given leaf set (the key stage alone).
     """
     hidx = idx.heads[h]
@@ -483,8 +483,8 @@ def select(idx: OracleIndex, queries: np.ndarray, q_pos: np.ndarray, prm: Select
 
 
 def flat_select(idx: OracleIndex, queries, q_pos, prm: SelectParams, pairs=None):
-    """Full-scan indexer: every key of C(p) is a candidate (the "old indexer"
-    that scores every key, bayesiansapien flowchart)."""
+    """Full-scan indexer: every key of C(p) is a candidate (the quadratic path
+    that scores every key, drawn dashed in the bayesiansapien flowchart)."""
     return select(idx, queries, q_pos, prm, flat=True, pairs=pairs)
 
 
