@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdio.h>
 #include <string.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/lsa.h"
@@ -78,12 +79,33 @@ void prof_begin(int stage, hipStream_t st);
 void prof_end(int stage, hipStream_t st);
 
 // ---- select ------------------------------------------------------------------
+
+// Node-major prefill path (prefill.hip): taken for large query batches when
+// the latent is bf16, the beam is per parent and the tree shape fits.
+struct PfPlan {
+  bool ok;                     // the path applies
+  int be[kMaxLevels];          // children kept per parent at each level
+  int nl[kMaxLevels + 1];      // slots per query head at each depth (nl[0] = 1)
+  int nl_out;                  // out_leaves row width, b^L
+  int spl;                     // samples per (query head, leaf)
+  int64_t cap;                 // appended keys per query head
+  int merge_m;                 // merge buffer entries per thread
+  int ch[kMaxLevels];          // workgroups per parent at each level
+  int chg;                     // workgroups per parent in the gather
+  size_t bytes;                // workspace bytes
+};
+PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq);
+int launch_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPlan& pl, const void* index,
+                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                   float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, char* err, size_t errlen);
+
 struct SelectPlan {
   int64_t qh;          // T * Hq
   int nl_cap;          // leaf-list capacity per query head
   int splits;          // workgroups per query head in the gather (1 = direct)
   int flat_splits;     // workgroups per (token, KV head) in the flat scan
   size_t bytes;        // workspace bytes
+  PfPlan pf;           // node-major prefill path (pf.ok)
 };
 SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat);
 int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& plan,

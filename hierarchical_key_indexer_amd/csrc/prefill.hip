@@ -1,0 +1,898 @@
+// Node-major selection for large query batches (prefill chunks) on gfx950.
+//
+// Same result as the per-query-head path of select.hip (steps 2 and 3 of "How
+// does LSA work?" on the page "Latent Sparse Attention (LSA): The 72.4x and
+// 22.7x Speedups, and What They Compare Against": score the bucket centroids,
+// keep the best buckets level by level, score the keys of the kept leaves,
+// keep the best k), computed the other way round: every tree node is visited
+// once per call with all the query heads that kept its parent, so a node's
+// children (and a leaf's keys) are read once per batch instead of once per
+// query head, and the scores come from bf16 matrix-core tiles.
+//
+//   pf_qproj_kernel     query latents, fp32 and bf16 copies
+//   pf_level_count      one level of the descent: a workgroup takes one parent
+//                       node and the query heads ("rows") that kept it; the
+//                       parent's children are the A operand of a 32x32x16 bf16
+//                       MFMA, 32 rows the B operand; every row keeps its best
+//                       b children (insertion network over the lane's 32
+//                       scores, merged with the partner lane); per-child
+//                       counts are added to global counters
+//   pf_level_scatter    the rows of every kept child are written to the
+//                       child's list (the next level's groups); at the last
+//                       level also the per-row leaf slots
+//   pf_gather           leaf-major scoring: one item is (leaf, 32 rows), the
+//                       rows' latents are the A operand, 32 keys of the leaf
+//                       the B operand.  Sample mode keeps the first s scores of
+//                       every (row, leaf); main mode appends the keys at or
+//                       above the row's threshold to the row's list
+//   pf_tau_kernel       per row, a threshold from the weighted samples such
+//                       that about 1.5k candidates are expected above it
+//   pf_merge_kernel     per row, the exact best k of the appended keys and the
+//                       output row; a row whose threshold let fewer than k keys
+//                       through (or whose list overflowed) is scored again in
+//                       full from its leaf list
+#include "select_device.h"
+
+namespace lsa {
+
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kPfBlock = 256;        // level and gather workgroups: 4 waves
+constexpr int kPfNW = kPfBlock / 64;
+constexpr int kPfMergeBlock = 512;
+constexpr int kPfMinRows = 256;      // query heads per KV head for this path
+constexpr int kPfMaxB = 16;
+constexpr int kPfMaxF = 64;
+constexpr float kPfTarget = 1.5f;    // expected appended keys per row, in units of k
+constexpr int kPfSampleR = 200;      // samples expected above the threshold
+
+struct PfArgs {
+  SelArgs s;                   // index, queries, outputs; s.qlat fp32 latents; s.part_keys / part_n appends
+  uint16_t* qlat16;            // [R][DL] bf16 bits of the query latents
+  int64_t R;                   // rows = T * Hq
+  int TG;                      // rows per KV head = T * G
+  // level being scored: lev = e - 1 indexes cscore / off / F / P; parents at depth e - 1
+  int lev;
+  int be;                      // children kept per parent at this level, min(b, F_e)
+  int sub;                     // leaf slots under one depth-e slot
+  int CH;                      // workgroups per parent
+  int64_t P_par;               // parents per KV head, P_{e-1}
+  const uint32_t* pstart;      // [Hkv * P_{e-1}] list starts in the parents' entries (null: root)
+  const uint32_t* pcnt;        // [Hkv * P_{e-1}] list lengths (null: root)
+  const int2* Eprev;           // parents' entries (row, slot) (null: root)
+  int2* Enext;                 // children's entries
+  u64* mask;                   // per parent entry: the children kept (bit c)
+  uint32_t* ccnt;              // [Hkv * P_e] child list lengths
+  uint32_t* cfill;             // [Hkv * P_e] fill counters
+  uint32_t* cstart;            // [Hkv * P_e] child list starts
+  int32_t* lf;                 // [R][nl] leaf of every slot, -1 for none
+  int nl;                      // leaf slots per row, prod of the be
+  // gather
+  int spl;                     // samples per (row, leaf)
+  uint16_t* smp;               // [R][nl][spl] top 16 bits of order(score), 0 = not a candidate
+  float* tauf;                 // [R] score threshold, -inf = none
+  int64_t cap;                 // append capacity per row
+};
+
+__device__ __forceinline__ int2 pf_entry(const PfArgs& a, int64_t pos, int h) {
+  if (a.Eprev) return a.Eprev[pos];
+  const int64_t i = pos - (int64_t)h * a.TG;
+  return make_int2((int)((i / a.s.G) * a.s.Hq + (int64_t)h * a.s.G + i % a.s.G), 0);
+}
+
+// the parent's list: [start, start + n) of the parents' entries
+__device__ __forceinline__ void pf_parent(const PfArgs& a, int64_t gp, int h, int64_t* start, int* n) {
+  if (a.pstart) {
+    *start = a.pstart[gp];
+    *n = (int)a.pcnt[gp];
+  } else {
+    *start = (int64_t)h * a.TG;
+    *n = a.TG;
+  }
+}
+
+__device__ __forceinline__ v8s as_v8s(const uint4& u) { return __builtin_bit_cast(v8s, u); }
+
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((u64)hi << 32) | lo;
+}
+
+// ---------------------------------------------------------------------------
+// query latents
+// ---------------------------------------------------------------------------
+
+template <typename KT, int DL>
+__global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
+  __shared__ float qin[256 + kQSlices * DL];
+  __shared__ float q[DL];
+  const int64_t row = blockIdx.x;
+  const int h = (int)(row % a.s.Hq) / a.s.G;
+  query_latent<KT, bf16_t, DL>(a.s, row, h, qin, q);
+  if (threadIdx.x < DL) a.qlat16[row * DL + threadIdx.x] = (uint16_t)(__float_as_uint(q[threadIdx.x]) >> 16);
+  if (threadIdx.x == 0) a.s.part_n[row] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// descent, one level
+// ---------------------------------------------------------------------------
+
+// t[0..B) holds the B largest values seen so far, descending (with repeats).
+template <int B>
+__device__ __forceinline__ void topb_insert(uint32_t (&t)[B], uint32_t v) {
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const uint32_t hi = t[j] > v ? t[j] : v;
+    v = t[j] > v ? v : t[j];
+    t[j] = hi;
+  }
+}
+
+template <int DL, int NT, int BMAX>
+__global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
+  constexpr int KS = DL / 16;                    // k-steps of 16 latent dims
+  __shared__ uint32_t lcnt[kPfMaxF];
+  const int64_t gp = blockIdx.x / a.CH;
+  const int ch = (int)(blockIdx.x % a.CH);
+  const int h = (int)(gp / a.P_par);
+  const int64_t par = gp % a.P_par;
+  const int F = a.s.F[a.lev];
+  const int64_t Pe = a.s.P[a.lev];
+  int64_t start;
+  int n;
+  pf_parent(a, gp, h, &start, &n);
+  const int ntiles = (n + 31) / 32;
+  if (ch * kPfNW >= ntiles) return;              // workgroup-uniform
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  if (threadIdx.x < kPfMaxF) lcnt[threadIdx.x] = 0u;
+  // children of the parent: non-empty mask and the A operand
+  const int64_t child0 = par * F;
+  const int* off = a.s.off[a.lev] + (size_t)h * (Pe + 1);
+  bool ne = false;
+  if (lane < F) ne = off[child0 + lane + 1] > off[child0 + lane];
+  const u64 ne_mask = __ballot(ne);
+  const bf16_t* cs = (const bf16_t*)a.s.cscore[a.lev] + ((size_t)h * Pe + child0) * DL;
+  v8s A[NT][KS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = 32 * t + l32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (c < F) u = *(const uint4*)(cs + (size_t)c * DL + 16 * s + 8 * half);
+      A[t][s] = as_v8s(u);
+    }
+  }
+  __syncthreads();
+  for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
+    const int r_in = ti * 32 + l32;
+    const bool valid = r_in < n;
+    const int64_t pos = start + r_in;
+    const int row = valid ? pf_entry(a, pos, h).x : -1;
+    v16f acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (valid) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+      const v8s Bv = as_v8s(u);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[t][s], Bv, acc[t], 0, 0, 0);
+    }
+    // lane holds row l32 against children 32t + 8(i/4) + 4 half + i%4
+    uint32_t key[NT][16];
+    uint32_t top[BMAX];
+#pragma unroll
+    for (int j = 0; j < BMAX; ++j) top[j] = 0u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
+        key[t][i] = ((ne_mask >> c) & 1ull) ? order_u32(acc[t][i]) : 0u;
+        topb_insert<BMAX>(top, key[t][i]);
+      }
+    // the partner lane (lane ^ 32) holds the other children of the row
+    uint32_t cm[BMAX];
+#pragma unroll
+    for (int j = 0; j < BMAX; ++j) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)top[BMAX - 1 - j], 32, 64);
+      cm[j] = top[j] > o ? top[j] : o;
+    }
+#pragma unroll
+    for (int hs = BMAX / 2; hs >= 1; hs >>= 1)
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j)
+        if ((j & hs) == 0) {
+          const uint32_t x = cm[j], y = cm[j + hs];
+          cm[j] = x > y ? x : y;
+          cm[j + hs] = x > y ? y : x;
+        }
+    uint32_t theta = 0u;
+#pragma unroll
+    for (int j = 0; j < BMAX; ++j)
+      if (j == a.be - 1) theta = cm[j];
+    u64 gt = 0ull, eq = 0ull;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u64 bit = 1ull << (32 * t + 8 * (i >> 2) + 4 * half + (i & 3));
+        gt |= key[t][i] > theta ? bit : 0ull;
+        eq |= key[t][i] == theta ? bit : 0ull;
+      }
+    gt |= shfl_xor_u64(gt, 32);
+    eq |= shfl_xor_u64(eq, 32);
+    u64 sel = gt;
+    if (theta != 0u) {
+      // ties at the b-th score: the lowest child ids
+      int need = a.be - __popcll(gt);
+      while (need > 0 && eq != 0ull) {
+        const u64 low = eq & (~eq + 1ull);
+        sel |= low;
+        eq ^= low;
+        --need;
+      }
+    }
+    if (half == 0 && valid) {
+      a.mask[pos] = sel;
+      u64 m = sel;
+      while (m != 0ull) {
+        const int c = __ffsll((long long)m) - 1;
+        atomicAdd(&lcnt[c], 1u);
+        m &= m - 1ull;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < F && lcnt[threadIdx.x] != 0u)
+    atomicAdd(&a.ccnt[(size_t)h * Pe + child0 + threadIdx.x], lcnt[threadIdx.x]);
+}
+
+__global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
+  __shared__ uint32_t lcnt[kPfMaxF], lbase[kPfMaxF], lfill[kPfMaxF], cst[kPfMaxF];
+  const int64_t gp = blockIdx.x / a.CH;
+  const int ch = (int)(blockIdx.x % a.CH);
+  const int h = (int)(gp / a.P_par);
+  const int64_t par = gp % a.P_par;
+  const int F = a.s.F[a.lev];
+  const int64_t Pe = a.s.P[a.lev];
+  int64_t start;
+  int n;
+  pf_parent(a, gp, h, &start, &n);
+  const int ntiles = (n + 31) / 32;
+  const int64_t cbase = (int64_t)h * Pe + par * F;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (ch == 0 && ntiles == 0) {
+    // a parent nobody kept: its children's lists are empty
+    if (threadIdx.x < F) a.cstart[cbase + threadIdx.x] = (uint32_t)(a.be * start);
+    return;
+  }
+  if (ch * kPfNW >= ntiles) return;              // workgroup-uniform
+  if (w == 0) {
+    const uint32_t c = lane < F ? a.ccnt[cbase + lane] : 0u;
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = (uint32_t)__shfl_up((int)incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    if (lane < kPfMaxF) {
+      cst[lane] = (uint32_t)(a.be * start) + incl - c;
+      lcnt[lane] = 0u;
+      lfill[lane] = 0u;
+    }
+    if (ch == 0 && lane < F) a.cstart[cbase + lane] = (uint32_t)(a.be * start) + incl - c;
+  }
+  __syncthreads();
+  for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
+    const int r_in = ti * 32 + lane;
+    if (lane < 32 && r_in < n) {
+      u64 m = a.mask[start + r_in];
+      while (m != 0ull) {
+        atomicAdd(&lcnt[__ffsll((long long)m) - 1], 1u);
+        m &= m - 1ull;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < F && lcnt[threadIdx.x] != 0u) lbase[threadIdx.x] = atomicAdd(&a.cfill[cbase + threadIdx.x], lcnt[threadIdx.x]);
+  __syncthreads();
+  const bool last = a.lev == a.s.L - 1;
+  for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
+    const int r_in = ti * 32 + lane;
+    if (lane < 32 && r_in < n) {
+      const int64_t pos = start + r_in;
+      const int2 e = pf_entry(a, pos, h);
+      u64 m = a.mask[pos];
+      int j = 0;
+      int32_t* lfr = a.lf + (size_t)e.x * a.nl;
+      while (m != 0ull) {
+        const int c = __ffsll((long long)m) - 1;
+        m &= m - 1ull;
+        const uint32_t slot = (uint32_t)e.y * a.be + j;
+        const uint32_t dst = cst[c] + lbase[c] + atomicAdd(&lfill[c], 1u);
+        a.Enext[dst] = make_int2(e.x, (int)slot);
+        if (last) lfr[slot] = (int32_t)(par * F + c);
+        ++j;
+      }
+      // slots left empty (fewer than be non-empty children) and their subtrees
+      for (; j < a.be; ++j) {
+        const int64_t s0 = ((int64_t)e.y * a.be + j) * a.sub;
+        for (int64_t q = 0; q < a.sub; ++q) lfr[s0 + q] = -1;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// leaf-major gather
+// ---------------------------------------------------------------------------
+
+// Items of a workgroup: (leaf c of the parent, tile i of 32 of the leaf's
+// rows); per item every 32-key tile of the leaf (sample mode: the first).
+template <int DL, bool SAMPLE>
+__global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
+  constexpr int KS = DL / 16;
+  __shared__ uint32_t tpre[kPfMaxF + 1];
+  __shared__ uint32_t lst[kPfMaxF], lcn[kPfMaxF];
+  __shared__ int o0s[kPfMaxF], o1s[kPfMaxF];
+  const int lev = a.s.L - 1;
+  const int64_t gp = blockIdx.x / a.CH;
+  const int ch = (int)(blockIdx.x % a.CH);
+  const int h = (int)(gp / a.P_par);
+  const int64_t par = gp % a.P_par;
+  const int F = a.s.F[lev];
+  const int64_t Pe = a.s.P[lev];
+  const int64_t cbase = (int64_t)h * Pe + par * F;
+  const int* offL = a.s.off[lev] + (size_t)h * (Pe + 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  if (w == 0) {
+    const uint32_t c = lane < F ? a.ccnt[cbase + lane] : 0u;
+    const uint32_t tl = (c + 31u) / 32u;
+    uint32_t incl = tl;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = (uint32_t)__shfl_up((int)incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    if (lane < F) {
+      tpre[lane + 1] = incl;
+      lst[lane] = a.cstart[cbase + lane];
+      lcn[lane] = c;
+      o0s[lane] = offL[par * F + lane];
+      o1s[lane] = offL[par * F + lane + 1];
+    }
+    if (lane == 0) tpre[0] = 0u;
+  }
+  __syncthreads();
+  const int items = (int)tpre[F];
+  const int sink = a.s.sink;
+  const bf16_t* latb = (const bf16_t*)a.s.lat + (size_t)h * a.s.N * DL;
+  const int* permb = a.s.perm + (size_t)h * a.s.N;
+  for (int it = ch * kPfNW + w; it < items; it += a.CH * kPfNW) {
+    int c = 0;
+    {
+      int lo = 0, hi = F;              // tpre[lo] <= it < tpre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)tpre[mid] <= it) lo = mid; else hi = mid;
+      }
+      c = lo;
+    }
+    const int i = it - (int)tpre[c];
+    // this lane's row of the tile (lanes l and l + 32 share row l % 32)
+    const int r_in = i * 32 + l32;
+    int row = -1, slot = 0, chi = -1;
+    float tau = 0.f;
+    if (r_in < (int)lcn[c]) {
+      const int2 e = a.Enext[lst[c] + r_in];
+      row = e.x;
+      slot = e.y;
+      const int p = a.s.q_pos[row / a.s.Hq];
+      chi = (p >= 0 && (int64_t)p < a.s.N) ? p - a.s.window : -1;
+      if (!SAMPLE) tau = a.tauf[row];
+    }
+    v8s Aq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+      Aq[s] = as_v8s(u);
+    }
+    // the 16 rows this lane's results belong to: m = 8(i/4) + 4 half + i%4
+    int rowm[16], chim[16], slotm[16];
+    float taum[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+      rowm[r] = __shfl(row, m, 64);
+      chim[r] = __shfl(chi, m, 64);
+      if (SAMPLE) slotm[r] = __shfl(slot, m, 64);
+      else taum[r] = __shfl(tau, m, 64);
+    }
+    const int o0 = o0s[c], o1 = o1s[c];
+    const int nkt = SAMPLE ? (o1 > o0 ? 1 : 0) : (o1 - o0 + 31) / 32;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int krow = o0 + 32 * kt + l32;
+      const bool kv = krow < o1;
+      int j = -1;
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (kv) u = *(const uint4*)(latb + (size_t)krow * DL + 16 * s + 8 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq[s], as_v8s(u), acc, 0, 0, 0);
+      }
+      if (kv) j = permb[krow];
+      const bool jc = kv && j >= sink;
+      if (SAMPLE) {
+        if (l32 < a.spl) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (rowm[r] < 0) continue;
+            const bool cand = jc && j <= chim[r];
+            const uint16_t v = cand ? (uint16_t)(order_u32(acc[r]) >> 16) : (uint16_t)0;
+            a.smp[((size_t)rowm[r] * a.nl + slotm[r]) * a.spl + l32] = v;
+          }
+        }
+      } else {
+        u64 bal[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bal[r] = __ballot(jc && j <= chim[r] && acc[r] >= taum[r]);
+        uint32_t base[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t cnt = (uint32_t)__popcll(half ? (bal[r] >> 32) : (bal[r] & 0xFFFFFFFFull));
+          base[r] = 0u;
+          if (l32 == 0 && cnt != 0u) base[r] = atomicAdd(&a.s.part_n[rowm[r]], cnt);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (bal[r] == 0ull) continue;
+          const uint32_t b0 = (uint32_t)__shfl((int)base[r], lane & 32, 64);
+          const uint32_t below = (uint32_t)__popcll(bal[r] & ((1ull << lane) - 1ull) & (half ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull));
+          const uint64_t pos = (uint64_t)b0 + below;
+          if (((bal[r] >> lane) & 1ull) && pos < (uint64_t)a.cap)
+            a.s.part_keys[(size_t)rowm[r] * a.cap + pos] = rank_key(acc[r], j);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-row threshold from the samples
+// ---------------------------------------------------------------------------
+
+// Over a 256-bin histogram (lane l owns bins 4l..4l+3), the bin that holds
+// the need-th unit of weight counted from the top, and in *above the weight of
+// the bins above it; -1 if the histogram holds less than need.  Wave-wide.
+__device__ __forceinline__ int wave_find_bin(const u64* hist, u64 need, u64* above_out) {
+  const int lane = threadIdx.x & 63;
+  u64 hb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
+  const u64 sum = hb[0] + hb[1] + hb[2] + hb[3];
+  u64 incl = sum;   // over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 x = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += x;
+  }
+  const u64 above = incl - sum;
+  const bool mine = above < need && need <= incl;
+  int d = -1;
+  u64 ab = 0ull;
+  if (mine) {
+    u64 acc = above;
+    for (int i = 3; i >= 0; --i) {
+      if (acc + hb[i] >= need) {
+        d = 4 * lane + i;
+        ab = acc;
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  const u64 bal = __ballot(mine);
+  if (bal == 0ull) return -1;
+  const int src = __ffsll((long long)bal) - 1;
+  *above_out = __shfl(ab, src, 64);
+  return __shfl(d, src, 64);
+}
+
+// One wave per row.  A sample of leaf c stands for size_c / min(spl, size_c)
+// candidates (fixed point, 4 fraction bits); the threshold is the largest
+// 16-bit sample value whose weight at or above it reaches 1.5k, found with two
+// 8-bit histogram passes.  A row whose leaves hold at most `cap` keys in all
+// takes every candidate (no threshold).
+__global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
+  __shared__ u64 hist[kPfNW][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kPfNW + w;
+  const bool live = row < a.R;
+  const int lev = a.s.L - 1;
+  const int64_t Pe = a.s.P[lev];
+  int h = 0, p = -1;
+  if (live) {
+    h = (int)(row % a.s.Hq) / a.s.G;
+    p = a.s.q_pos[row / a.s.Hq];
+  }
+  const int* offL = a.s.off[lev] + (size_t)h * (Pe + 1);
+  const int32_t* lfr = a.lf + (size_t)(live ? row : 0) * a.nl;
+  const uint16_t* sm = a.smp + (size_t)(live ? row : 0) * a.nl * a.spl;
+  int64_t tot = 0;
+  if (live)
+    for (int sl = lane; sl < a.nl; sl += 64) {
+      const int leaf = lfr[sl];
+      if (leaf >= 0) tot += offL[leaf + 1] - offL[leaf];
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+  const bool want = live && p >= 0 && (int64_t)p < a.s.N && tot > a.cap;
+  const u64 target = (u64)((double)kPfTarget * a.s.k * 16.0);
+  int d1 = -1, d2 = -1;
+  u64 ab1 = 0ull, ab2 = 0ull;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int b = lane; b < 256; b += 64) hist[w][b] = 0ull;
+    __syncthreads();
+    if (want && (pass == 0 || d1 >= 0))
+      for (int sl = lane; sl < a.nl; sl += 64) {
+        const int leaf = lfr[sl];
+        if (leaf < 0) continue;
+        const int sz = offL[leaf + 1] - offL[leaf];
+        const int se = sz < a.spl ? sz : a.spl;
+        if (se == 0) continue;
+        const u64 wt = ((u64)sz << 4) / (u64)se;
+        for (int q = 0; q < se; ++q) {
+          const uint32_t v = sm[(size_t)sl * a.spl + q];
+          if (v == 0u) continue;
+          if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
+          else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
+        }
+      }
+    __syncthreads();
+    if (pass == 0) d1 = wave_find_bin(hist[w], target, &ab1);
+    else if (d1 >= 0) d2 = wave_find_bin(hist[w], target - ab1, &ab2);
+    __syncthreads();
+  }
+  float tf = -__builtin_huge_valf();
+  if (want && d1 >= 0 && d2 >= 0) tf = order_u32_to_f32(((uint32_t)d1 << 24) | ((uint32_t)d2 << 16));
+  if (live && lane == 0) a.tauf[row] = tf;
+}
+
+// ---------------------------------------------------------------------------
+// per-row exact top-k and output
+// ---------------------------------------------------------------------------
+
+template <int DL, int M>
+__global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
+  constexpr int BLOCK = kPfMergeBlock, CAP = M * BLOCK, NW = BLOCK / 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ RadixScratch rs;
+  __shared__ int n_sh, wsum[NW];
+  u64* buf = (u64*)smem;
+  int* lpre = (int*)(buf + CAP);
+  int* lrow = lpre + a.nl + 1;
+  const int64_t row = blockIdx.x;
+  const int t = (int)(row / a.s.Hq), h = (int)(row % a.s.Hq) / a.s.G;
+  const int p = a.s.q_pos[t];
+  const int lev = a.s.L - 1;
+  const int* offL = a.s.off[lev] + (size_t)h * (a.s.P[lev] + 1);
+  const int32_t* lfr = a.lf + (size_t)row * a.nl;
+  // the row's leaves in slot order: CSR row starts and candidate prefix counts
+  const int per = (a.nl + BLOCK - 1) / BLOCK;
+  const int i0 = min(a.nl, (int)threadIdx.x * per), i1 = min(a.nl, i0 + per);
+  int c = 0, sz = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int leaf = lfr[i];
+    if (leaf >= 0) {
+      ++c;
+      sz += offL[leaf + 1] - offL[leaf];
+    }
+  }
+  int nlv, total;
+  int pos = block_exclusive_scan<BLOCK>(c, wsum, &nlv);
+  int run = block_exclusive_scan<BLOCK>(sz, wsum, &total);
+  int32_t* ol = a.s.out_leaves ? a.s.out_leaves + (size_t)row * a.s.nl_cap : nullptr;
+  for (int i = i0; i < i1; ++i) {
+    const int leaf = lfr[i];
+    if (leaf < 0) continue;
+    const int r0 = offL[leaf];
+    lrow[pos] = r0;
+    lpre[pos] = run;
+    if (ol) ol[pos] = leaf;
+    run += offL[leaf + 1] - r0;
+    ++pos;
+  }
+  if (threadIdx.x == 0) lpre[nlv] = total;
+  if (ol)
+    for (int i = nlv + threadIdx.x; i < a.s.nl_cap; i += BLOCK) ol[i] = -1;
+  __syncthreads();
+  int32_t* orow = a.s.out_idx + (size_t)row * a.s.width;
+  float* srow = a.s.out_scores ? a.s.out_scores + (size_t)row * a.s.k : nullptr;
+  if (p < 0 || (int64_t)p >= a.s.N) {
+    write_invalid_row<BLOCK>(a.s.width, a.s.k, orow, srow);
+    return;
+  }
+  const int n_in = (int)a.s.part_n[row];
+  const float tau = a.tauf[row];
+  int n;
+  if ((int64_t)n_in > a.cap || (n_in < a.s.k && tau > -__builtin_huge_valf())) {
+    // the threshold let fewer than k keys through, or the list overflowed:
+    // score every candidate of the row
+    n = gather_stream<bf16_t, DL, M, 4, BLOCK>(a.s, row, h, a.s.sink, p - a.s.window, lpre, lrow, nlv, 0, total,
+                                               0ull, buf, &n_sh, &rs);
+  } else {
+    const u64* src = a.s.part_keys + (size_t)row * a.cap;
+    for (int i = threadIdx.x; i < n_in; i += BLOCK) buf[i] = src[i];
+    n = n_in;
+    __syncthreads();
+  }
+  if (n > a.s.k) {
+    topk_compact<BLOCK, M>(buf, n, a.s.k, &rs);
+    n = a.s.k;
+  }
+  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, a.s.k, a.s.window, orow, srow);
+}
+
+__global__ void pf_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct PfWs {
+  float* qlat;
+  uint16_t* qlat16;
+  int2* E[kMaxLevels];
+  uint32_t* ccnt[kMaxLevels];
+  uint32_t* cfill[kMaxLevels];
+  uint32_t* cstart[kMaxLevels];
+  u64* mask;
+  int32_t* lf;
+  uint16_t* smp;
+  float* tauf;
+  u64* part_keys;
+  uint32_t* part_n;
+};
+
+size_t carve_prefill(const lsa_index_desc& d, const PfPlan& pl, int64_t R, void* base, PfWs* out) {
+  const Layout L = compute_layout(d);
+  Carver c(base);
+  PfWs w;
+  memset(&w, 0, sizeof(w));
+  const int DL = d.d_latent;
+  w.qlat = c.take<float>((size_t)(R * DL));
+  w.qlat16 = c.take<uint16_t>((size_t)(R * DL));
+  for (int e = 0; e < d.n_levels; ++e) {
+    w.E[e] = c.take<int2>((size_t)(R * pl.nl[e + 1]));
+    const size_t nodes = (size_t)(d.n_kv_heads * L.nodes[e + 1]);
+    w.ccnt[e] = c.take<uint32_t>(nodes);
+    w.cfill[e] = c.take<uint32_t>(nodes);
+    w.cstart[e] = c.take<uint32_t>(nodes);
+  }
+  w.mask = c.take<u64>((size_t)(R * pl.nl[d.n_levels - 1]));
+  w.lf = c.take<int32_t>((size_t)(R * pl.nl[d.n_levels]));
+  w.smp = c.take<uint16_t>((size_t)(R * pl.nl[d.n_levels] * pl.spl));
+  w.tauf = c.take<float>((size_t)R);
+  w.part_keys = c.take<u64>((size_t)(R * pl.cap));
+  w.part_n = c.take<uint32_t>((size_t)R);
+  if (out) *out = w;
+  return align_up(c.used);
+}
+
+int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
+
+template <int DL, int NT>
+void launch_count_b(const PfArgs& a, int64_t grid, int be, hipStream_t st) {
+  if (be <= 4) hipLaunchKernelGGL((pf_level_count<DL, NT, 4>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+  else if (be <= 8) hipLaunchKernelGGL((pf_level_count<DL, NT, 8>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+  else hipLaunchKernelGGL((pf_level_count<DL, NT, 16>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+}
+
+template <int DL, int M>
+void launch_pf_merge(const PfArgs& a, hipStream_t st) {
+  auto mk = pf_merge_kernel<DL, M>;
+  const size_t lds = (size_t)M * kPfMergeBlock * 8 + ((size_t)a.nl * 2 + 2) * 4;
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)mk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(mk, dim3((unsigned)a.R), dim3(kPfMergeBlock), lds, st, a);
+}
+
+template <typename KT, int DL>
+int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPlan& pl, const void* index,
+                const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, char* err, size_t errlen) {
+  const Layout L = compute_layout(d);
+  const char* blob = (const char*)index;
+  const int64_t R = (int64_t)T * Hq;
+  PfWs w;
+  carve_prefill(d, pl, R, ws, &w);
+  PfArgs a;
+  memset(&a, 0, sizeof(a));
+  SelArgs& s = a.s;
+  s.lat = blob + L.latent;
+  s.perm = (const int*)(blob + L.perm);
+  s.N = d.n_keys;
+  s.Hkv = d.n_kv_heads;
+  s.G = Hq / d.n_kv_heads;
+  s.Hq = Hq;
+  s.T = T;
+  s.d_head = d.d_head;
+  s.queries = queries;
+  s.W = (const float*)(blob + L.W);
+  s.qlat = w.qlat;
+  s.q_pos = q_pos;
+  s.sink = p.sink;
+  s.window = p.window;
+  s.k = p.k;
+  s.width = p.sink + p.k + p.window;
+  s.L = d.n_levels;
+  for (int l = 0; l < d.n_levels; ++l) {
+    s.cscore[l] = blob + L.cscore[l];
+    s.off[l] = (const int*)(blob + L.offsets[l]);
+    s.F[l] = d.fanout[l];
+    s.P[l] = L.nodes[l + 1];
+  }
+  s.b = p.b;
+  s.beam = p.beam;
+  s.nl_cap = pl.nl_out;
+  s.out_leaves = out_leaves;
+  s.part_keys = w.part_keys;
+  s.part_n = w.part_n;
+  s.part_cap = pl.cap;
+  s.out_idx = out_idx;
+  s.out_scores = out_scores;
+  a.qlat16 = w.qlat16;
+  a.R = R;
+  a.TG = T * s.G;
+  a.mask = w.mask;
+  a.lf = w.lf;
+  a.nl = pl.nl[d.n_levels];
+  a.spl = pl.spl;
+  a.smp = w.smp;
+  a.tauf = w.tauf;
+  a.cap = pl.cap;
+
+#define PF_CHECK(what)                                                               \
+  do {                                                                               \
+    hipError_t e_ = hipGetLastError();                                               \
+    if (e_ != hipSuccess) {                                                          \
+      snprintf(err, errlen, "%s launch failed: %s", what, hipGetErrorString(e_));    \
+      return LSA_ERR_HIP;                                                            \
+    }                                                                                \
+  } while (0)
+
+  prof_begin(LSA_STAGE_DESCEND, st);
+  hipLaunchKernelGGL((pf_qproj_kernel<KT, DL>), dim3((unsigned)R), dim3(256), 0, st, a);
+  PF_CHECK("query projection");
+  for (int lev = 0; lev < d.n_levels; ++lev) {
+    const int64_t nodes = (int64_t)d.n_kv_heads * L.nodes[lev + 1];
+    hipLaunchKernelGGL(pf_fill_u32, dim3(clampi((nodes + 255) / 256, 1, 4096)), dim3(256), 0, st, w.ccnt[lev], nodes, 0u);
+    hipLaunchKernelGGL(pf_fill_u32, dim3(clampi((nodes + 255) / 256, 1, 4096)), dim3(256), 0, st, w.cfill[lev], nodes, 0u);
+    a.lev = lev;
+    a.be = pl.be[lev];
+    a.sub = pl.nl[d.n_levels] / pl.nl[lev + 1];
+    a.CH = pl.ch[lev];
+    a.P_par = L.nodes[lev];
+    a.pstart = lev ? w.cstart[lev - 1] : nullptr;
+    a.pcnt = lev ? w.ccnt[lev - 1] : nullptr;
+    a.Eprev = lev ? w.E[lev - 1] : nullptr;
+    a.Enext = w.E[lev];
+    a.ccnt = w.ccnt[lev];
+    a.cfill = w.cfill[lev];
+    a.cstart = w.cstart[lev];
+    const int64_t grid = (int64_t)d.n_kv_heads * L.nodes[lev] * a.CH;
+    if (d.fanout[lev] <= 32) launch_count_b<DL, 1>(a, grid, a.be, st);
+    else launch_count_b<DL, 2>(a, grid, a.be, st);
+    PF_CHECK("level scoring");
+    hipLaunchKernelGGL(pf_level_scatter, dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    PF_CHECK("level lists");
+  }
+  prof_end(LSA_STAGE_DESCEND, st);
+  prof_begin(LSA_STAGE_GATHER, st);
+  {
+    const int lev = d.n_levels - 1;
+    a.lev = lev;
+    a.CH = pl.chg;
+    a.P_par = L.nodes[lev];
+    a.Enext = w.E[lev];
+    a.ccnt = w.ccnt[lev];
+    a.cstart = w.cstart[lev];
+    const int64_t grid = (int64_t)d.n_kv_heads * L.nodes[lev] * a.CH;
+    hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    PF_CHECK("sample pass");
+    hipLaunchKernelGGL(pf_tau_kernel, dim3((unsigned)((R + kPfNW - 1) / kPfNW)), dim3(kPfBlock), 0, st, a);
+    PF_CHECK("thresholds");
+    hipLaunchKernelGGL((pf_gather<DL, false>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    PF_CHECK("gather");
+  }
+  prof_end(LSA_STAGE_GATHER, st);
+  prof_begin(LSA_STAGE_MERGE, st);
+  switch (pl.merge_m) {
+    case 1: launch_pf_merge<DL, 1>(a, st); break;
+    case 2: launch_pf_merge<DL, 2>(a, st); break;
+    case 4: launch_pf_merge<DL, 4>(a, st); break;
+    case 8: launch_pf_merge<DL, 8>(a, st); break;
+    default: launch_pf_merge<DL, 16>(a, st); break;
+  }
+  prof_end(LSA_STAGE_MERGE, st);
+  PF_CHECK("merge");
+#undef PF_CHECK
+  return LSA_OK;
+}
+
+}  // namespace
+
+PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq) {
+  PfPlan pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.ok = false;
+  if (d.latent_dtype != LSA_BF16 || (d.d_latent != 32 && d.d_latent != 64)) return pl;
+  if (p.beam != LSA_BEAM_PER_PARENT || p.k > 2048 || p.k < 1) return pl;
+  const int G = Hq / d.n_kv_heads;
+  if ((int64_t)T * G < kPfMinRows) return pl;
+  const Layout L = compute_layout(d);
+  const int64_t R = (int64_t)T * Hq;
+  pl.nl[0] = 1;
+  for (int e = 0; e < d.n_levels; ++e) {
+    const int F = d.fanout[e];
+    if (F > kPfMaxF) return pl;
+    pl.be[e] = p.b < F ? p.b : F;
+    if (pl.be[e] > kPfMaxB || pl.be[e] < 1) return pl;
+    pl.nl[e + 1] = pl.nl[e] * pl.be[e];
+  }
+  const int nl = pl.nl[d.n_levels];
+  if (R * nl >= ((int64_t)1 << 31)) return pl;
+  pl.nl_out = 1;
+  for (int e = 0; e < d.n_levels; ++e) pl.nl_out *= p.b;
+  pl.cap = 3 * (int64_t)p.k;
+  int capl = 512;
+  while (capl < pl.cap || capl < 2 * p.k) capl <<= 1;
+  pl.merge_m = capl / kPfMergeBlock;
+  if (pl.merge_m > 16) return pl;
+  const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
+  pl.spl = clampi((int64_t)ceil(kPfSampleR * avg_leaf / (kPfTarget * p.k)), 1, 32);
+  for (int e = 0; e < d.n_levels; ++e) {
+    const double parents = (double)d.n_kv_heads * (double)L.nodes[e];
+    const double tiles = (double)R * pl.nl[e] / parents / 32.0;
+    pl.ch[e] = clampi((int64_t)ceil(tiles / (2.0 * kPfNW)), 1, 4096);
+  }
+  {
+    const int lev = d.n_levels - 1;
+    const double rows_per_leaf = (double)R * nl / ((double)d.n_kv_heads * (double)L.nodes[lev + 1]);
+    const double items = (double)d.fanout[lev] * ceil(rows_per_leaf / 32.0);
+    pl.chg = clampi((int64_t)ceil(items / (2.0 * kPfNW)), 1, 4096);
+  }
+  pl.bytes = carve_prefill(d, pl, R, nullptr, nullptr);
+  pl.ok = true;
+  return pl;
+}
+
+int launch_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPlan& pl, const void* index,
+                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                   float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, char* err, size_t errlen) {
+  const bool kb = d.key_dtype == LSA_BF16;
+  if (d.d_latent == 64) {
+    if (kb) return run_prefill<bf16_t, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+    return run_prefill<float, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+  }
+  if (kb) return run_prefill<bf16_t, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+  return run_prefill<float, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+}
+
+}  // namespace lsa

@@ -23,87 +23,9 @@
 //   qproj_kernel     query latents for the flat scan
 //   flat_kernel      full scan of one KV head's rows for its G query heads
 //                    (each row read once for G heads), streaming top-k each
-#include "lsa_device.h"
-#include "lsa_internal.h"
+#include "select_device.h"
 
 namespace lsa {
-
-struct SelArgs {
-  const void* lat;             // [Hkv][N][DL] CSR latent
-  const int* perm;             // [Hkv][N]
-  int64_t N;
-  int Hkv, G, Hq, T, d_head;
-  const void* queries;         // [T][Hq][d_head] key dtype
-  const float* W;              // [Hkv][d_head][DL]
-  float* qlat;                 // [T*Hq][DL]
-  const int* q_pos;            // [T]
-  int sink, window, k, width;
-  const void* cscore[kMaxLevels];
-  const int* off[kMaxLevels];
-  int F[kMaxLevels];
-  int64_t P[kMaxLevels];
-  int L, b, beam, nl_cap;
-  int* leafrow;                // [QH][nl_cap]
-  int* leafpre;                // [QH][nl_cap+1]
-  int* nleaf;                  // [QH]
-  int* out_leaves;             // [QH][nl_cap] or null
-  int S;                       // workgroups per query head (gather) or per (t, KV head) (flat)
-  unsigned long long* part_keys;  // [QH][part_cap] appended local top-k lists
-  unsigned int* part_n;        // [QH] entries appended
-  int64_t part_cap;
-  unsigned long long* tau;     // [QH] sampled lower bound for the best k (0 = none)
-  int32_t* out_idx;            // [QH][width]
-  float* out_scores;           // [QH][k] or null
-  int64_t qh0;                 // first query head of this launch
-};
-
-template <typename LT, int DL>
-__device__ __forceinline__ float row_dot(const LT* row, const float* q) {
-  const uint4* r = (const uint4*)row;
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < DL / Lat<LT>::PER16; ++i) acc += Lat<LT>::dot16(r[i], q + i * Lat<LT>::PER16);
-  return acc;
-}
-
-// q~ = round_latent(q . W_h) into q_out (LDS) and the workspace.  d_head is
-// cut into kQSlices slices; thread (slice, j) sums one slice of output j and
-// the slice sums are added in slice order, so every kernel that projects a
-// query gets the same bits (needs blockDim >= kQSlices * DL).  qin holds
-// d_head + kQSlices * DL floats of LDS.
-constexpr int kQSlices = 4;
-
-template <typename KT, typename LT, int DL>
-__device__ __forceinline__ void query_latent(const SelArgs& a, int64_t qh, int h, float* qin, float* q_out) {
-  const KT* qrow = (const KT*)a.queries + qh * a.d_head;
-  float* part = qin + a.d_head;
-  for (int i = threadIdx.x; i < a.d_head; i += blockDim.x) qin[i] = KeyLoad<KT>::get(qrow, i);
-  __syncthreads();
-  if (threadIdx.x < kQSlices * DL) {
-    const int j = threadIdx.x % DL, sl = threadIdx.x / DL;
-    const int per = a.d_head / kQSlices;
-    const float* Wh = a.W + (size_t)h * a.d_head * DL + j;
-    float acc = 0.f;
-    for (int i = sl * per; i < (sl + 1) * per; i += 8) {   // per is a multiple of 8
-      float wv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) wv[u] = Wh[(size_t)(i + u) * DL];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(qin[i + u], wv[u], acc);
-    }
-    part[sl * DL + j] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x < DL) {
-    float v = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < kQSlices; ++k2) v += part[k2 * DL + threadIdx.x];
-    v = Lat<LT>::PER16 == 8 ? round_to_bf16(v) : v;
-    q_out[threadIdx.x] = v;
-    a.qlat[qh * DL + threadIdx.x] = v;
-  }
-  __syncthreads();
-}
 
 // ---------------------------------------------------------------------------
 // descent
@@ -350,143 +272,6 @@ __global__ __launch_bounds__(256) void qproj_kernel(SelArgs a) {
   if (threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;
 }
 
-// ---------------------------------------------------------------------------
-// streaming top-k helpers
-// ---------------------------------------------------------------------------
-
-// Append the keys with pred set to the LDS buffer (one LDS atomic per wave).
-__device__ __forceinline__ void wave_append(bool pred, u64 key, u64* buf, int* n) {
-  const u64 bal = __ballot(pred);
-  if (bal == 0ull) return;
-  int base = 0;
-  if (lane_id() == 0) base = atomicAdd(n, __popcll(bal));
-  base = __shfl(base, 0, 64);
-  if (pred) buf[base + mbcnt64(bal)] = key;
-}
-
-// Append the keys with pred[u] set (up to U <= 15 per lane) with one LDS
-// atomic per wave: the lane's exclusive offset comes from bit-plane ballots
-// of its count.
-template <int U>
-__device__ __forceinline__ void wave_append_many(const bool* pred, const u64* key, u64* buf, int* n) {
-  static_assert(U <= 15, "four bit planes");
-  constexpr int PL = U < 2 ? 1 : U < 4 ? 2 : U < 8 ? 3 : 4;
-  int c = 0;
-#pragma unroll
-  for (int u = 0; u < U; ++u) c += pred[u] ? 1 : 0;
-  int tot = 0, pre = 0;
-#pragma unroll
-  for (int b = 0; b < PL; ++b) {
-    const u64 bb = __ballot((c >> b) & 1);
-    tot += __popcll(bb) << b;
-    pre += (int)mbcnt64(bb) << b;
-  }
-  if (tot == 0) return;
-  int base = 0;
-  if (lane_id() == 0) base = atomicAdd(n, tot);
-  base = __builtin_amdgcn_readfirstlane(base);
-  int pos = base + pre;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (pred[u]) buf[pos++] = key[u];
-}
-
-// Append this workgroup's n local keys to the query head's array.
-template <int BLOCK>
-__device__ void append_part(const SelArgs& a, int64_t qh, const u64* buf, int n, int* base_sh) {
-  if (threadIdx.x == 0) *base_sh = (int)atomicAdd(&a.part_n[qh], (unsigned)n);
-  __syncthreads();
-  u64* dst = a.part_keys + qh * a.part_cap + *base_sh;
-  for (int i = threadIdx.x; i < n; i += BLOCK) dst[i] = buf[i];
-}
-
-// ---------------------------------------------------------------------------
-// gather-and-score
-// ---------------------------------------------------------------------------
-
-// Score candidates [lo, hi) of a query head's leaf list (CSR rows of KV head
-// h; lpre / lrow in LDS) and append the rank keys above thr to buf, keeping
-// at most the best k when the buffer fills (streaming radix-select
-// compaction).  Returns the number of keys left in buf.  Block-wide.
-template <typename LT, int DL, int M, int U, int BLOCK>
-__device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int chi, const int* lpre,
-                             const int* lrow, int nl, int64_t lo, int64_t hi, u64 thr, u64* buf, int* n_sh,
-                             RadixScratch* rs) {
-  constexpr int NW = BLOCK / 64;
-  constexpr int CAP = M * BLOCK;
-  constexpr int E = Lat<LT>::PER16;              // latent elements per lane load
-  constexpr int LPK = DL / E;                    // lanes per key
-  constexpr int KPW = 64 / LPK;                  // keys per wave per load
-  constexpr int ROUND = NW * KPW * U;            // candidates per round
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lig = lane % LPK, g = lane / LPK;
-  if (threadIdx.x == 0) *n_sh = 0;
-  __syncthreads();
-  const int64_t wlen = (hi - lo + NW - 1) / NW;
-  const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
-  QSlice<LT> qv;
-  qv.load(a.qlat + qh * DL + lig * E);
-  // first leaf of this wave's range (largest i with lpre[i] <= wlo)
-  int cur = 0;
-  {
-    int lo_i = 0, hi_i = nl;
-    while (hi_i - lo_i > 1) {
-      const int mid = (lo_i + hi_i) >> 1;
-      if (lpre[mid] <= wlo) lo_i = mid; else hi_i = mid;
-    }
-    cur = lo_i;
-  }
-  const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
-  const int* permb = a.perm + (size_t)h * a.N;
-  const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
-  const bool fits = hi - lo <= CAP;
-  uint4 v[U], vn[U];
-  int idx[U], idxn[U];
-  auto fetch = [&](int64_t r, uint4* vv, int* ii) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t o = wlo + (r * U + u) * KPW + g;
-      vv[u] = make_uint4(0u, 0u, 0u, 0u);
-      ii[u] = -1;
-      if (o < whi) {
-        while (lpre[cur + 1] <= o) ++cur;
-        const int64_t row = lrow[cur] + (o - lpre[cur]);
-        vv[u] = *(const uint4*)(latb + row * DL + lig * E);
-        ii[u] = permb[row];
-      }
-    }
-  };
-  if (rounds > 0) fetch(0, v, idx);
-  for (int64_t r = 0; r < rounds; ++r) {
-    if (r + 1 < rounds) fetch(r + 1, vn, idxn);
-    bool pr[U];
-    u64 ky[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float sc = group_sum_lead<LPK>(qv.dot(v[u]));
-      const bool cand = lig == 0 && idx[u] >= clo && idx[u] <= chi;
-      ky[u] = cand ? rank_key(sc, idx[u]) : 0ull;
-      pr[u] = cand && ky[u] > thr;
-    }
-    wave_append_many<U>(pr, ky, buf, n_sh);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = vn[u];
-      idx[u] = idxn[u];
-    }
-    if (fits) continue;          // every candidate of the range fits: no compaction
-    __syncthreads();
-    if (*n_sh + ROUND > CAP) {
-      const int n = *n_sh;
-      thr = topk_compact<BLOCK, M>(buf, n, a.k, rs);
-      if (threadIdx.x == 0) *n_sh = a.k;
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-  return *n_sh;
-}
-
 template <typename LT, int DL, int M, int U, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   constexpr int CAP = M * BLOCK;
@@ -539,40 +324,6 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
 // top) find a prefix that every key of the best k reaches; one more pass
 // appends only the keys at or above it, and the streaming compaction picks
 // the exact best k among them.
-template <int BLOCK>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, int* wsum, int* d_out,
-                                           uint32_t* above_out, uint32_t* hd_out) {
-  // thread t owns bins [4t, 4t+4); counts above a bin come from a scan that
-  // runs from the highest thread down
-  constexpr int PER = 4096 / BLOCK;
-  const int t = threadIdx.x;
-  uint32_t hb[PER];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    hb[i] = hist[t * PER + i];
-    s += hb[i];
-  }
-  int total;
-  // exclusive scan in reversed thread order = keys in bins of higher threads
-  const int rev_t = BLOCK - 1 - t;
-  (void)rev_t;
-  const uint32_t above_t = (uint32_t)block_exclusive_scan_rev<BLOCK>((int)s, wsum, &total);
-  if (above_t < need && need <= above_t + s) {
-    uint32_t acc = above_t;
-    for (int i = PER - 1; i >= 0; --i) {
-      if (acc + hb[i] >= need) {
-        *d_out = t * PER + i;
-        *above_out = acc;
-        *hd_out = hb[i];
-        break;
-      }
-      acc += hb[i];
-    }
-  }
-  __syncthreads();
-}
-
 template <typename LT, int DL, int BLOCK, int M>
 __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   constexpr int CAP = M * BLOCK;
@@ -1090,6 +841,11 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   sf = sf < 1 ? 1 : (sf > 1024 ? 1024 : sf);
   pl.flat_splits = (int)sf;
   pl.bytes = carve_select(d, p, pl, T, Hq, flat, nullptr, nullptr);
+  memset(&pl.pf, 0, sizeof(pl.pf));
+  if (!flat) {
+    pl.pf = plan_prefill(d, p, T, Hq);
+    if (pl.pf.ok) pl.bytes = pl.pf.bytes;
+  }
   return pl;
 }
 
@@ -1097,6 +853,8 @@ int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const Sel
                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                   float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, bool flat, char* err,
                   size_t errlen) {
+  if (!flat && pl.pf.ok)
+    return launch_prefill(d, p, pl.pf, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
   const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
 #define LSA_RUN(KT, LT, DLV) \
   return run_select<KT, LT, DLV>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen)

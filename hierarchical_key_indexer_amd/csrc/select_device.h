@@ -1,0 +1,264 @@
+// Device routines shared by the selection kernels of the per-query-head path
+// (select.hip) and the node-major prefill path (prefill.hip): the argument
+// block, the query latent, the LDS append helpers and the streaming
+// gather-and-score over a query head's leaf list.
+#pragma once
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+struct SelArgs {
+  const void* lat;             // [Hkv][N][DL] CSR latent
+  const int* perm;             // [Hkv][N]
+  int64_t N;
+  int Hkv, G, Hq, T, d_head;
+  const void* queries;         // [T][Hq][d_head] key dtype
+  const float* W;              // [Hkv][d_head][DL]
+  float* qlat;                 // [T*Hq][DL]
+  const int* q_pos;            // [T]
+  int sink, window, k, width;
+  const void* cscore[kMaxLevels];
+  const int* off[kMaxLevels];
+  int F[kMaxLevels];
+  int64_t P[kMaxLevels];
+  int L, b, beam, nl_cap;
+  int* leafrow;                // [QH][nl_cap]
+  int* leafpre;                // [QH][nl_cap+1]
+  int* nleaf;                  // [QH]
+  int* out_leaves;             // [QH][nl_cap] or null
+  int S;                       // workgroups per query head (gather) or per (t, KV head) (flat)
+  unsigned long long* part_keys;  // [QH][part_cap] appended local top-k lists
+  unsigned int* part_n;        // [QH] entries appended
+  int64_t part_cap;
+  unsigned long long* tau;     // [QH] sampled lower bound for the best k (0 = none)
+  int32_t* out_idx;            // [QH][width]
+  float* out_scores;           // [QH][k] or null
+  int64_t qh0;                 // first query head of this launch
+};
+
+template <typename LT, int DL>
+__device__ __forceinline__ float row_dot(const LT* row, const float* q) {
+  const uint4* r = (const uint4*)row;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < DL / Lat<LT>::PER16; ++i) acc += Lat<LT>::dot16(r[i], q + i * Lat<LT>::PER16);
+  return acc;
+}
+
+// q~ = round_latent(q . W_h) into q_out (LDS) and the workspace.  d_head is
+// cut into kQSlices slices; thread (slice, j) sums one slice of output j and
+// the slice sums are added in slice order, so every kernel that projects a
+// query gets the same bits (needs blockDim >= kQSlices * DL).  qin holds
+// d_head + kQSlices * DL floats of LDS.
+constexpr int kQSlices = 4;
+
+template <typename KT, typename LT, int DL>
+__device__ __forceinline__ void query_latent(const SelArgs& a, int64_t qh, int h, float* qin, float* q_out) {
+  const KT* qrow = (const KT*)a.queries + qh * a.d_head;
+  float* part = qin + a.d_head;
+  for (int i = threadIdx.x; i < a.d_head; i += blockDim.x) qin[i] = KeyLoad<KT>::get(qrow, i);
+  __syncthreads();
+  if (threadIdx.x < kQSlices * DL) {
+    const int j = threadIdx.x % DL, sl = threadIdx.x / DL;
+    const int per = a.d_head / kQSlices;
+    const float* Wh = a.W + (size_t)h * a.d_head * DL + j;
+    float acc = 0.f;
+    for (int i = sl * per; i < (sl + 1) * per; i += 8) {   // per is a multiple of 8
+      float wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) wv[u] = Wh[(size_t)(i + u) * DL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(qin[i + u], wv[u], acc);
+    }
+    part[sl * DL + j] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < DL) {
+    float v = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < kQSlices; ++k2) v += part[k2 * DL + threadIdx.x];
+    v = Lat<LT>::PER16 == 8 ? round_to_bf16(v) : v;
+    q_out[threadIdx.x] = v;
+    a.qlat[qh * DL + threadIdx.x] = v;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// streaming top-k helpers
+// ---------------------------------------------------------------------------
+
+// Append the keys with pred set to the LDS buffer (one LDS atomic per wave).
+__device__ __forceinline__ void wave_append(bool pred, u64 key, u64* buf, int* n) {
+  const u64 bal = __ballot(pred);
+  if (bal == 0ull) return;
+  int base = 0;
+  if (lane_id() == 0) base = atomicAdd(n, __popcll(bal));
+  base = __shfl(base, 0, 64);
+  if (pred) buf[base + mbcnt64(bal)] = key;
+}
+
+// Append the keys with pred[u] set (up to U <= 15 per lane) with one LDS
+// atomic per wave: the lane's exclusive offset comes from bit-plane ballots
+// of its count.
+template <int U>
+__device__ __forceinline__ void wave_append_many(const bool* pred, const u64* key, u64* buf, int* n) {
+  static_assert(U <= 15, "four bit planes");
+  constexpr int PL = U < 2 ? 1 : U < 4 ? 2 : U < 8 ? 3 : 4;
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) c += pred[u] ? 1 : 0;
+  int tot = 0, pre = 0;
+#pragma unroll
+  for (int b = 0; b < PL; ++b) {
+    const u64 bb = __ballot((c >> b) & 1);
+    tot += __popcll(bb) << b;
+    pre += (int)mbcnt64(bb) << b;
+  }
+  if (tot == 0) return;
+  int base = 0;
+  if (lane_id() == 0) base = atomicAdd(n, tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+  int pos = base + pre;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (pred[u]) buf[pos++] = key[u];
+}
+
+// Append this workgroup's n local keys to the query head's array.
+template <int BLOCK>
+__device__ void append_part(const SelArgs& a, int64_t qh, const u64* buf, int n, int* base_sh) {
+  if (threadIdx.x == 0) *base_sh = (int)atomicAdd(&a.part_n[qh], (unsigned)n);
+  __syncthreads();
+  u64* dst = a.part_keys + qh * a.part_cap + *base_sh;
+  for (int i = threadIdx.x; i < n; i += BLOCK) dst[i] = buf[i];
+}
+
+// ---------------------------------------------------------------------------
+// gather-and-score
+// ---------------------------------------------------------------------------
+
+// Score candidates [lo, hi) of a query head's leaf list (CSR rows of KV head
+// h; lpre / lrow in LDS) and append the rank keys above thr to buf, keeping
+// at most the best k when the buffer fills (streaming radix-select
+// compaction).  Returns the number of keys left in buf.  Block-wide.
+template <typename LT, int DL, int M, int U, int BLOCK>
+__device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int chi, const int* lpre,
+                             const int* lrow, int nl, int64_t lo, int64_t hi, u64 thr, u64* buf, int* n_sh,
+                             RadixScratch* rs) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int CAP = M * BLOCK;
+  constexpr int E = Lat<LT>::PER16;              // latent elements per lane load
+  constexpr int LPK = DL / E;                    // lanes per key
+  constexpr int KPW = 64 / LPK;                  // keys per wave per load
+  constexpr int ROUND = NW * KPW * U;            // candidates per round
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lig = lane % LPK, g = lane / LPK;
+  if (threadIdx.x == 0) *n_sh = 0;
+  __syncthreads();
+  const int64_t wlen = (hi - lo + NW - 1) / NW;
+  const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
+  QSlice<LT> qv;
+  qv.load(a.qlat + qh * DL + lig * E);
+  // first leaf of this wave's range (largest i with lpre[i] <= wlo)
+  int cur = 0;
+  {
+    int lo_i = 0, hi_i = nl;
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (lpre[mid] <= wlo) lo_i = mid; else hi_i = mid;
+    }
+    cur = lo_i;
+  }
+  const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
+  const int* permb = a.perm + (size_t)h * a.N;
+  const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
+  const bool fits = hi - lo <= CAP;
+  uint4 v[U], vn[U];
+  int idx[U], idxn[U];
+  auto fetch = [&](int64_t r, uint4* vv, int* ii) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = wlo + (r * U + u) * KPW + g;
+      vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      ii[u] = -1;
+      if (o < whi) {
+        while (lpre[cur + 1] <= o) ++cur;
+        const int64_t row = lrow[cur] + (o - lpre[cur]);
+        vv[u] = *(const uint4*)(latb + row * DL + lig * E);
+        ii[u] = permb[row];
+      }
+    }
+  };
+  if (rounds > 0) fetch(0, v, idx);
+  for (int64_t r = 0; r < rounds; ++r) {
+    if (r + 1 < rounds) fetch(r + 1, vn, idxn);
+    bool pr[U];
+    u64 ky[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float sc = group_sum_lead<LPK>(qv.dot(v[u]));
+      const bool cand = lig == 0 && idx[u] >= clo && idx[u] <= chi;
+      ky[u] = cand ? rank_key(sc, idx[u]) : 0ull;
+      pr[u] = cand && ky[u] > thr;
+    }
+    wave_append_many<U>(pr, ky, buf, n_sh);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = vn[u];
+      idx[u] = idxn[u];
+    }
+    if (fits) continue;          // every candidate of the range fits: no compaction
+    __syncthreads();
+    if (*n_sh + ROUND > CAP) {
+      const int n = *n_sh;
+      thr = topk_compact<BLOCK, M>(buf, n, a.k, rs);
+      if (threadIdx.x == 0) *n_sh = a.k;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  return *n_sh;
+}
+
+// Find, in a 4096-bin histogram of 12-bit digits, the bin that holds the
+// need-th largest key: *d_out gets the bin, *above_out the keys in higher
+// bins, *hd_out the keys in the bin.  Block-wide (BLOCK divides 4096).
+template <int BLOCK>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, int* wsum, int* d_out,
+                                           uint32_t* above_out, uint32_t* hd_out) {
+  // thread t owns bins [4t, 4t+4); counts above a bin come from a scan that
+  // runs from the highest thread down
+  constexpr int PER = 4096 / BLOCK;
+  const int t = threadIdx.x;
+  uint32_t hb[PER];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    hb[i] = hist[t * PER + i];
+    s += hb[i];
+  }
+  int total;
+  // exclusive scan in reversed thread order = keys in bins of higher threads
+  const int rev_t = BLOCK - 1 - t;
+  (void)rev_t;
+  const uint32_t above_t = (uint32_t)block_exclusive_scan_rev<BLOCK>((int)s, wsum, &total);
+  if (above_t < need && need <= above_t + s) {
+    uint32_t acc = above_t;
+    for (int i = PER - 1; i >= 0; --i) {
+      if (acc + hb[i] >= need) {
+        *d_out = t * PER + i;
+        *above_out = acc;
+        *hd_out = hb[i];
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  __syncthreads();
+}
+
+
+}  // namespace lsa

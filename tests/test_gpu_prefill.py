@@ -1,0 +1,78 @@
+"""GPU parity of the node-major prefill path (large query batches: at least
+256 query heads per KV head, bf16 latent, per-parent beam) against the CPU
+oracle, on oracle-built index blobs.  The cases cover two and three levels,
+fanouts up to 64, an fp32 key store with a 32-dim latent, rows whose leaves
+hold more keys than the append capacity (sampled threshold, with rows near
+the sequence start that fall back to a full re-score) and rows that take
+every candidate; positions include the sequence start, the sink and window
+edges and invalid positions."""
+import numpy as np
+import pytest
+
+from oracle import lsa_oracle as O
+from synth import gen_keys, gen_queries, gen_W, get_workload
+from tests.gpu_helpers import _li, gpu_select
+from tests.parity import compare_select, log
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_key_indexer_amd import _abi
+    _abi.load()
+
+
+def _pf(**kw):
+    base = dict(n_keys=20000, n_kv_heads=2, group=4, d_latent=64, n_centers=200, n_tokens=64, kmeans_iters=4,
+                fanout=(16, 16), b=4, k=64, sink=4, window=32)
+    base.update(kw)
+    return get_workload("prefill_1m").scaled(**base)
+
+
+PF_CASES = {
+    "pf_2lvl_g4": _pf(),
+    "pf_3lvl_g4": _pf(n_keys=30000, n_kv_heads=1, fanout=(8, 8, 8), b=3, k=100, n_tokens=80),
+    "pf_f32keys_dl32": _pf(key_dtype="f32", d_latent=32, fanout=(32, 8), b=5, k=150, group=2, n_tokens=160),
+    "pf_take_all": _pf(n_keys=6000, fanout=(8, 8), b=2, k=400),
+    "pf_fanout64": _pf(n_keys=40000, n_kv_heads=1, fanout=(64, 48), b=6, k=128, n_tokens=70),
+    "pf_b16_k2048": _pf(n_keys=60000, n_kv_heads=1, n_centers=400, fanout=(32, 32), b=16, k=2048, window=512,
+                        n_tokens=64),
+}
+
+
+def _positions(wl):
+    """Tail positions, with the sequence start, the sink / window edges and
+    two invalid positions mixed in."""
+    T, N = wl.n_tokens, wl.n_keys
+    pos = np.arange(N - T, N, dtype=np.int64)
+    edge = [0, wl.sink - 1, wl.sink + wl.window, wl.sink + wl.window + 5, 200, N // 2, -1, N]
+    pos[:len(edge)] = edge
+    return pos.astype(np.int32)
+
+
+@pytest.mark.parametrize("case", list(PF_CASES))
+def test_prefill_path_on_oracle_index(case):
+    wl = PF_CASES[case]
+    log(f"[prefill path] case={case} N={wl.n_keys} fanout={wl.fanout} b={wl.b} k={wl.k} T={wl.n_tokens} "
+        f"G={wl.group}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    queries = gen_queries(wl, keys)
+    pos = _positions(wl)
+    li = _li(desc, O.index_blob(oidx))
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    gi, gs, gl = gpu_select(li, queries, pos, prm)
+    valid = [t for t in range(wl.n_tokens) if 0 <= pos[t] < wl.n_keys]
+    pairs = [(t, hq) for t in valid for hq in range(wl.n_q_heads)]
+    compare_select(oidx, queries, pos, prm, gi, gs, gl, pairs=pairs, log=log)
+    bad = [t for t in range(wl.n_tokens) if t not in valid]
+    assert np.all(gi[bad] == -1) and np.all(np.isneginf(gs[bad])), "invalid positions"
+    # the same call again gives the same bits (the append order may differ)
+    gi2, gs2, gl2 = gpu_select(li, queries, pos, prm)
+    assert np.array_equal(gi, gi2) and np.array_equal(gs.view(np.uint32), gs2.view(np.uint32))
+    assert np.array_equal(np.sort(gl, axis=-1), np.sort(gl2, axis=-1))
