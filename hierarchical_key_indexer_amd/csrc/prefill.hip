@@ -20,17 +20,21 @@
 //   pf_level_scatter    the rows of every kept child are written to the
 //                       child's list (the next level's groups); at the last
 //                       level also the per-row leaf slots
-//   pf_gather           leaf-major scoring: one item is (leaf, 32 rows), the
-//                       rows' latents are the A operand, 32 keys of the leaf
-//                       the B operand.  Sample mode keeps the first s scores of
-//                       every (row, leaf); main mode appends the keys at or
-//                       above the row's threshold to the row's list
+//   pf_gather           leaf-major scoring: one item is (leaf, 32 rows), 32
+//                       keys of the leaf are the A operand of a 32x32x16 bf16
+//                       MFMA, the rows' latents the B operand.  Sample mode
+//                       keeps the first s scores of every (row, leaf); main
+//                       mode counts each row's keys at or above its threshold,
+//                       reserves their places with one atomic per row and
+//                       writes them
 //   pf_tau_kernel       per row, a threshold from the weighted samples such
 //                       that about 1.5k candidates are expected above it
 //   pf_merge_kernel     per row, the exact best k of the appended keys and the
 //                       output row; a row whose threshold let fewer than k keys
 //                       through (or whose list overflowed) is scored again in
 //                       full from its leaf list
+#include <limits.h>
+
 #include "select_device.h"
 
 namespace lsa {
@@ -42,7 +46,7 @@ namespace {
 
 constexpr int kPfBlock = 256;        // level and gather workgroups: 4 waves
 constexpr int kPfNW = kPfBlock / 64;
-constexpr int kPfMergeBlock = 512;
+constexpr int kPfMergeBlock = 256;
 constexpr int kPfMinRows = 256;      // query heads per KV head for this path
 constexpr int kPfMaxB = 16;
 constexpr int kPfMaxF = 64;
@@ -94,6 +98,29 @@ __device__ __forceinline__ void pf_parent(const PfArgs& a, int64_t gp, int h, in
   }
 }
 
+// Workgroup -> (parent, chunk).  Workgroups are dealt to the 8 XCDs in turn;
+// when the KV heads divide evenly, all workgroups of a KV head are mapped to
+// one XCD, so that head's query latents and list heads stay in that XCD's L2.
+__device__ __forceinline__ void pf_block(const PfArgs& a, int64_t* gp, int* ch) {
+  const int64_t b = blockIdx.x;
+  const int64_t per_head = a.P_par * a.CH;
+  int64_t logical = b;
+  if (a.s.Hkv % 8 == 0) {
+    const int64_t x = b % 8, q = b / 8;
+    logical = (x + 8 * (q / per_head)) * per_head + q % per_head;
+  }
+  *gp = logical / a.CH;
+  *ch = (int)(logical % a.CH);
+}
+
+// Append counter of a row, stored head-major (KV head, token, group member)
+// so one KV head's counters share no cache line with another head's.
+__device__ __forceinline__ uint32_t* pf_count_of(const PfArgs& a, int64_t row) {
+  const int64_t t = row / a.s.Hq, hq = row % a.s.Hq;
+  const int64_t h = hq / a.s.G, g = hq % a.s.G;
+  return a.s.part_n + (h * a.s.T + t) * a.s.G + g;
+}
+
 __device__ __forceinline__ v8s as_v8s(const uint4& u) { return __builtin_bit_cast(v8s, u); }
 
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
@@ -114,7 +141,7 @@ __global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
   const int h = (int)(row % a.s.Hq) / a.s.G;
   query_latent<KT, bf16_t, DL>(a.s, row, h, qin, q);
   if (threadIdx.x < DL) a.qlat16[row * DL + threadIdx.x] = (uint16_t)(__float_as_uint(q[threadIdx.x]) >> 16);
-  if (threadIdx.x == 0) a.s.part_n[row] = 0u;
+  if (threadIdx.x == 0) *pf_count_of(a, row) = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -136,8 +163,9 @@ template <int DL, int NT, int BMAX>
 __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
   constexpr int KS = DL / 16;                    // k-steps of 16 latent dims
   __shared__ uint32_t lcnt[kPfMaxF];
-  const int64_t gp = blockIdx.x / a.CH;
-  const int ch = (int)(blockIdx.x % a.CH);
+  int64_t gp;
+  int ch;
+  pf_block(a, &gp, &ch);
   const int h = (int)(gp / a.P_par);
   const int64_t par = gp % a.P_par;
   const int F = a.s.F[a.lev];
@@ -259,8 +287,9 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
 
 __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   __shared__ uint32_t lcnt[kPfMaxF], lbase[kPfMaxF], lfill[kPfMaxF], cst[kPfMaxF];
-  const int64_t gp = blockIdx.x / a.CH;
-  const int ch = (int)(blockIdx.x % a.CH);
+  int64_t gp;
+  int ch;
+  pf_block(a, &gp, &ch);
   const int h = (int)(gp / a.P_par);
   const int64_t par = gp % a.P_par;
   const int F = a.s.F[a.lev];
@@ -338,7 +367,12 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
 // ---------------------------------------------------------------------------
 
 // Items of a workgroup: (leaf c of the parent, tile i of 32 of the leaf's
-// rows); per item every 32-key tile of the leaf (sample mode: the first).
+// rows).  Keys are the A operand and rows the B operand, so a lane holds one
+// row (its threshold and causal limit stay in registers) against 16 keys of
+// every 32-key tile.  Main mode runs over the leaf's key tiles twice: once to
+// count each row's keys at or above its threshold (one atomic per row and
+// item reserves their places), once to write them.  Sample mode scores the
+// first key tile and keeps the first spl scores of every row.
 template <int DL, bool SAMPLE>
 __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
   constexpr int KS = DL / 16;
@@ -346,8 +380,9 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
   __shared__ uint32_t lst[kPfMaxF], lcn[kPfMaxF];
   __shared__ int o0s[kPfMaxF], o1s[kPfMaxF];
   const int lev = a.s.L - 1;
-  const int64_t gp = blockIdx.x / a.CH;
-  const int ch = (int)(blockIdx.x % a.CH);
+  int64_t gp;
+  int ch;
+  pf_block(a, &gp, &ch);
   const int h = (int)(gp / a.P_par);
   const int64_t par = gp % a.P_par;
   const int F = a.s.F[lev];
@@ -390,10 +425,12 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
       c = lo;
     }
     const int i = it - (int)tpre[c];
-    // this lane's row of the tile (lanes l and l + 32 share row l % 32)
+    // this lane's row (lanes l and l + 32 share row l % 32)
     const int r_in = i * 32 + l32;
+    // a lane past the end of the leaf's rows has no row: nothing reaches its
+    // threshold and it writes nothing
     int row = -1, slot = 0, chi = -1;
-    float tau = 0.f;
+    float tau = __builtin_huge_valf();
     if (r_in < (int)lcn[c]) {
       const int2 e = a.Enext[lst[c] + r_in];
       row = e.x;
@@ -402,71 +439,102 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
       chi = (p >= 0 && (int64_t)p < a.s.N) ? p - a.s.window : -1;
       if (!SAMPLE) tau = a.tauf[row];
     }
-    v8s Aq[KS];
+    v8s Bq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 u = make_uint4(0u, 0u, 0u, 0u);
       if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
-      Aq[s] = as_v8s(u);
-    }
-    // the 16 rows this lane's results belong to: m = 8(i/4) + 4 half + i%4
-    int rowm[16], chim[16], slotm[16];
-    float taum[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-      rowm[r] = __shfl(row, m, 64);
-      chim[r] = __shfl(chi, m, 64);
-      if (SAMPLE) slotm[r] = __shfl(slot, m, 64);
-      else taum[r] = __shfl(tau, m, 64);
+      Bq[s] = as_v8s(u);
     }
     const int o0 = o0s[c], o1 = o1s[c];
-    const int nkt = SAMPLE ? (o1 > o0 ? 1 : 0) : (o1 - o0 + 31) / 32;
-    for (int kt = 0; kt < nkt; ++kt) {
+    // key tile kt: A operand (key l32's dims) and the key's index (INT_MAX
+    // for a missing key or one inside the sink)
+    auto load_keys = [&](int kt, v8s* A, int* jl) {
       const int krow = o0 + 32 * kt + l32;
       const bool kv = krow < o1;
-      int j = -1;
-      v16f acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         uint4 u = make_uint4(0u, 0u, 0u, 0u);
         if (kv) u = *(const uint4*)(latb + (size_t)krow * DL + 16 * s + 8 * half);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aq[s], as_v8s(u), acc, 0, 0, 0);
+        A[s] = as_v8s(u);
       }
-      if (kv) j = permb[krow];
-      const bool jc = kv && j >= sink;
-      if (SAMPLE) {
-        if (l32 < a.spl) {
+      const int j = kv ? permb[krow] : INT_MAX;
+      *jl = j >= sink ? j : INT_MAX;
+    };
+    // results: lane holds row l32 against keys m = 8(r/4) + 4 half + r%4
+    if (SAMPLE) {
+      if (o1 <= o0) continue;
+      v8s A[KS];
+      int jl;
+      load_keys(0, A, &jl);
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+        const int jm = __shfl(jl, m, 64);
+        if (m < a.spl && row >= 0) {
+          const uint16_t v = jm <= chi ? (uint16_t)(order_u32(acc[r]) >> 16) : (uint16_t)0;
+          a.smp[((size_t)row * a.nl + slot) * a.spl + m] = v;
+        }
+      }
+      continue;
+    }
+    const int nkt = (o1 - o0 + 31) / 32;
+    // the smallest causal limit of the item's rows: a tile whose keys all
+    // lie in [sink, that limit] needs no per-key range test when counting
+    int chimin = row >= 0 ? chi : INT_MAX;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) chimin = min(chimin, __shfl_xor(chimin, o, 64));
+    uint32_t pos = 0u;
+    for (int pass = 0; pass < 2; ++pass) {
+      int cnt = 0;
+      v8s A[KS], An[KS];
+      int jl = INT_MAX, jn = INT_MAX;
+      if (nkt > 0) load_keys(0, A, &jl);
+      for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + 1 < nkt) load_keys(kt + 1, An, &jn);
+        v16f acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+        int jmax = jl;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) jmax = max(jmax, __shfl_xor(jmax, o, 64));
+        if (pass == 0 && jmax <= chimin) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cnt += acc[r] >= tau ? 1 : 0;
+        } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            if (rowm[r] < 0) continue;
-            const bool cand = jc && j <= chim[r];
-            const uint16_t v = cand ? (uint16_t)(order_u32(acc[r]) >> 16) : (uint16_t)0;
-            a.smp[((size_t)rowm[r] * a.nl + slotm[r]) * a.spl + l32] = v;
+            const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+            const int jm = __shfl(jl, m, 64);
+            const bool ok = jm <= chi && acc[r] >= tau;
+            if (pass == 0) {
+              cnt += ok ? 1 : 0;
+            } else if (ok) {
+              if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)row * a.cap + pos] = rank_key(acc[r], jm);
+              ++pos;
+            }
           }
         }
-      } else {
-        u64 bal[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) bal[r] = __ballot(jc && j <= chim[r] && acc[r] >= taum[r]);
-        uint32_t base[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t cnt = (uint32_t)__popcll(half ? (bal[r] >> 32) : (bal[r] & 0xFFFFFFFFull));
-          base[r] = 0u;
-          if (l32 == 0 && cnt != 0u) base[r] = atomicAdd(&a.s.part_n[rowm[r]], cnt);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (bal[r] == 0ull) continue;
-          const uint32_t b0 = (uint32_t)__shfl((int)base[r], lane & 32, 64);
-          const uint32_t below = (uint32_t)__popcll(bal[r] & ((1ull << lane) - 1ull) & (half ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull));
-          const uint64_t pos = (uint64_t)b0 + below;
-          if (((bal[r] >> lane) & 1ull) && pos < (uint64_t)a.cap)
-            a.s.part_keys[(size_t)rowm[r] * a.cap + pos] = rank_key(acc[r], j);
-        }
+        for (int s = 0; s < KS; ++s) A[s] = An[s];
+        jl = jn;
+      }
+      if (pass == 0) {
+        // one atomic per row reserves the places of both halves' keys
+        const int lo_cnt = __shfl(cnt, l32, 64);            // half 0's count of this row
+        const int tot = lo_cnt + __shfl(cnt, l32 + 32, 64);
+        uint32_t base = 0u;
+        if (half == 0 && row >= 0 && tot > 0) base = atomicAdd(pf_count_of(a, row), (uint32_t)tot);
+        base = (uint32_t)__shfl((int)base, l32, 64);
+        pos = base + (half ? (uint32_t)lo_cnt : 0u);
+        if (__ballot(tot > 0) == 0ull) break;
       }
     }
   }
@@ -627,25 +695,36 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
     write_invalid_row<BLOCK>(a.s.width, a.s.k, orow, srow);
     return;
   }
-  const int n_in = (int)a.s.part_n[row];
+  const int k = a.s.k;
+  const int n_in = (int)*pf_count_of(a, row);
   const float tau = a.tauf[row];
-  int n;
-  if ((int64_t)n_in > a.cap || (n_in < a.s.k && tau > -__builtin_huge_valf())) {
+  int n = 0;
+  if ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf())) {
     // the threshold let fewer than k keys through, or the list overflowed:
     // score every candidate of the row
     n = gather_stream<bf16_t, DL, M, 4, BLOCK>(a.s, row, h, a.s.sink, p - a.s.window, lpre, lrow, nlv, 0, total,
                                                0ull, buf, &n_sh, &rs);
   } else {
+    // stream the appended keys through the buffer (CAP >= 2k), keeping the
+    // best k whenever it fills before the end
     const u64* src = a.s.part_keys + (size_t)row * a.cap;
-    for (int i = threadIdx.x; i < n_in; i += BLOCK) buf[i] = src[i];
-    n = n_in;
-    __syncthreads();
+    for (int done = 0; done < n_in;) {
+      const int take = min(CAP - n, n_in - done);
+      for (int i = threadIdx.x; i < take; i += BLOCK) buf[n + i] = src[done + i];
+      n += take;
+      done += take;
+      __syncthreads();
+      if (done < n_in) {
+        topk_compact<BLOCK, M>(buf, n, k, &rs);
+        n = k;
+      }
+    }
   }
-  if (n > a.s.k) {
-    topk_compact<BLOCK, M>(buf, n, a.s.k, &rs);
-    n = a.s.k;
+  if (n > k) {
+    topk_compact<BLOCK, M>(buf, n, k, &rs);
+    n = k;
   }
-  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, a.s.k, a.s.window, orow, srow);
+  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, k, a.s.window, orow, srow);
 }
 
 __global__ void pf_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
@@ -814,9 +893,10 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     a.ccnt = w.ccnt[lev];
     a.cstart = w.cstart[lev];
     const int64_t grid = (int64_t)d.n_kv_heads * L.nodes[lev] * a.CH;
+    const unsigned rgrid = (unsigned)((R + kPfNW - 1) / kPfNW);
     hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("sample pass");
-    hipLaunchKernelGGL(pf_tau_kernel, dim3((unsigned)((R + kPfNW - 1) / kPfNW)), dim3(kPfBlock), 0, st, a);
+    hipLaunchKernelGGL(pf_tau_kernel, dim3(rgrid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("thresholds");
     hipLaunchKernelGGL((pf_gather<DL, false>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("gather");
@@ -862,7 +942,7 @@ PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t
   for (int e = 0; e < d.n_levels; ++e) pl.nl_out *= p.b;
   pl.cap = 3 * (int64_t)p.k;
   int capl = 512;
-  while (capl < pl.cap || capl < 2 * p.k) capl <<= 1;
+  while (capl < 2 * p.k) capl <<= 1;
   pl.merge_m = capl / kPfMergeBlock;
   if (pl.merge_m > 16) return pl;
   const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
