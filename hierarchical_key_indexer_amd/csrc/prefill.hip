@@ -660,46 +660,57 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   const int lev = a.s.L - 1;
   const int* offL = a.s.off[lev] + (size_t)h * (a.s.P[lev] + 1);
   const int32_t* lfr = a.lf + (size_t)row * a.nl;
-  // the row's leaves in slot order: CSR row starts and candidate prefix counts
-  const int per = (a.nl + BLOCK - 1) / BLOCK;
-  const int i0 = min(a.nl, (int)threadIdx.x * per), i1 = min(a.nl, i0 + per);
-  int c = 0, sz = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int leaf = lfr[i];
-    if (leaf >= 0) {
-      ++c;
-      sz += offL[leaf + 1] - offL[leaf];
+  // the row's leaves in slot order (the out_leaves row, and for a re-score
+  // the CSR row starts and candidate prefix counts); block-wide
+  auto leaf_list = [&](bool lists, int* nlv_out, int* total_out) {
+    const int per = (a.nl + BLOCK - 1) / BLOCK;
+    const int i0 = min(a.nl, (int)threadIdx.x * per), i1 = min(a.nl, i0 + per);
+    int c = 0, sz = 0;
+    for (int i = i0; i < i1; ++i) {
+      const int leaf = lfr[i];
+      if (leaf >= 0) {
+        ++c;
+        if (lists) sz += offL[leaf + 1] - offL[leaf];
+      }
     }
-  }
-  int nlv, total;
-  int pos = block_exclusive_scan<BLOCK>(c, wsum, &nlv);
-  int run = block_exclusive_scan<BLOCK>(sz, wsum, &total);
-  int32_t* ol = a.s.out_leaves ? a.s.out_leaves + (size_t)row * a.s.nl_cap : nullptr;
-  for (int i = i0; i < i1; ++i) {
-    const int leaf = lfr[i];
-    if (leaf < 0) continue;
-    const int r0 = offL[leaf];
-    lrow[pos] = r0;
-    lpre[pos] = run;
-    if (ol) ol[pos] = leaf;
-    run += offL[leaf + 1] - r0;
-    ++pos;
-  }
-  if (threadIdx.x == 0) lpre[nlv] = total;
-  if (ol)
-    for (int i = nlv + threadIdx.x; i < a.s.nl_cap; i += BLOCK) ol[i] = -1;
-  __syncthreads();
+    int nlv, total = 0;
+    int pos = block_exclusive_scan<BLOCK>(c, wsum, &nlv);
+    int run = lists ? block_exclusive_scan<BLOCK>(sz, wsum, &total) : 0;
+    int32_t* ol = a.s.out_leaves ? a.s.out_leaves + (size_t)row * a.s.nl_cap : nullptr;
+    for (int i = i0; i < i1; ++i) {
+      const int leaf = lfr[i];
+      if (leaf < 0) continue;
+      if (lists) {
+        const int r0 = offL[leaf];
+        lrow[pos] = r0;
+        lpre[pos] = run;
+        run += offL[leaf + 1] - r0;
+      }
+      if (ol) ol[pos] = leaf;
+      ++pos;
+    }
+    if (lists && threadIdx.x == 0) lpre[nlv] = total;
+    if (ol)
+      for (int i = nlv + threadIdx.x; i < a.s.nl_cap; i += BLOCK) ol[i] = -1;
+    __syncthreads();
+    *nlv_out = nlv;
+    *total_out = total;
+  };
   int32_t* orow = a.s.out_idx + (size_t)row * a.s.width;
   float* srow = a.s.out_scores ? a.s.out_scores + (size_t)row * a.s.k : nullptr;
-  if (p < 0 || (int64_t)p >= a.s.N) {
+  const bool valid_p = p >= 0 && (int64_t)p < a.s.N;
+  const int k = a.s.k;
+  const int n_in = valid_p ? (int)*pf_count_of(a, row) : 0;
+  const float tau = a.tauf[row];
+  const bool rescore = valid_p && ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf()));
+  int nlv = 0, total = 0;
+  if (rescore || a.s.out_leaves) leaf_list(rescore, &nlv, &total);
+  if (!valid_p) {
     write_invalid_row<BLOCK>(a.s.width, a.s.k, orow, srow);
     return;
   }
-  const int k = a.s.k;
-  const int n_in = (int)*pf_count_of(a, row);
-  const float tau = a.tauf[row];
   int n = 0;
-  if ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf())) {
+  if (rescore) {
     // the threshold let fewer than k keys through, or the list overflowed:
     // score every candidate of the row
     n = gather_stream<bf16_t, DL, M, 4, BLOCK>(a.s, row, h, a.s.sink, p - a.s.window, lpre, lrow, nlv, 0, total,
