@@ -5,15 +5,21 @@
 
 A step is one ``lsa_select`` call over the workload's batch of query heads
 (query projection, centroid descent, gather-and-score, top-k, assembly), with
-the key cache and its index already resident in HBM.  The index build and the
+the key cache and its index already resident in HBM.  ``value`` comes from the
+wall time of K steps with nothing else in the stream; the per-stage kernel
+times come from a second, shorter run with HIP events around every stage.  The index build and the
 full-scan baseline (``lsa_flat_select``) are timed in the same run and
 reported beside it, together with tree-vs-flat recall.
 
-Prints one JSON line.  ``roofline`` describes the dominant kernel of the step
-(the gather-and-score): algorithmic bytes per launch (keys scored x bytes per
-key row) over its average duration, measured with HIP events that the library
-records on its own launch stream.  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line.  ``roofline`` describes the dominant kernel of the step,
+timed with HIP events that the library records on its own launch stream:
+  * per-query-head path (decode): the gather-and-score kernel against HBM,
+    algorithmic bytes per launch = keys scored x bytes per key row;
+  * node-major path (prefill batches): the main pass of the leaf-major gather
+    against the bf16 matrix-core peak, algorithmic flops per launch = keys
+    scored x 2 x latent dim (one dot product per scored key); the centroid
+    descent is reported the same way under ``centroid_scoring``.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -30,9 +36,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "indexer query-heads/s and keys-scored/s at 1M/10M keys; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_key_indexer_amd", "csrc", f)
-                  for f in ("select.hip", "lsa_device.h")]
+                  for f in ("select.hip", "select_device.h", "prefill.hip", "lsa_device.h")]
 
 
 def log(msg):
@@ -59,9 +66,13 @@ class HipEvents:
         return out
 
     def elapsed_ms(self, a, b):
-        assert self.hip.hipEventSynchronize(b) == 0
+        """Milliseconds between two recorded events, None if they were never
+        recorded (a stage the call did not run)."""
+        if self.hip.hipEventSynchronize(b) != 0:
+            return None
         ms = ctypes.c_float()
-        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            return None
         return ms.value
 
     def destroy(self, evs):
@@ -88,21 +99,26 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed_steps(fn, steps, hip, stage, abi):
-    """Run fn() `steps` times; return (wall ms per step, stage ms per step)."""
+def timed_steps(fn, steps, hip, stages, abi):
+    """Run fn() `steps` times; return (wall ms per step, {stage: ms per step,
+    None for a stage the call does not run})."""
     import torch
-    starts, stops = hip.create(steps), hip.create(steps)
+    ev = {st: (hip.create(steps), hip.create(steps)) for st in stages}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        abi.set_profile_events(stage, starts[i], stops[i])
+        for st in stages:
+            abi.set_profile_events(st, ev[st][0][i], ev[st][1][i])
         fn()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    abi.set_profile_events(stage, None, None)
-    stage_ms = sum(hip.elapsed_ms(a, b) for a, b in zip(starts, stops)) / steps
-    hip.destroy(starts + stops)
-    return wall, stage_ms
+    out = {}
+    for st in stages:
+        abi.set_profile_events(st, None, None)
+        ms = [hip.elapsed_ms(a, b) for a, b in zip(*ev[st])]
+        out[st] = None if any(m is None for m in ms) else sum(ms) / steps
+        hip.destroy(ev[st][0] + ev[st][1])
+    return wall, out
 
 
 def cpu_baseline(wl, keys, W, queries, pos):
@@ -201,20 +217,52 @@ def main():
     for _ in range(args.warmup):
         li.select(qd, pd, prm, leaves=False, out=(out[0], out[1], None))
     torch.cuda.synchronize()
-    log(f"timing {args.steps} select steps")
-    ms_step, gather_ms = timed_steps(lambda: li.select(qd, pd, prm, leaves=False, out=(out[0], out[1], None)),
-                                     args.steps, hip, _abi.STAGE_GATHER, _abi)
+    node_major = _abi.select_path(desc, prm, wl.n_tokens, wl.n_q_heads) == _abi.PATH_NODE_MAJOR
+    log(f"timing {args.steps} select steps ({'node-major' if node_major else 'per-query-head'} path)")
+    step = lambda: li.select(qd, pd, prm, leaves=False, out=(out[0], out[1], None))  # noqa: E731
+    # the value: wall time of K steps with no events in the stream
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-stage kernel time (events around each stage) in a second, shorter run
+    stages = [_abi.STAGE_DESCEND, _abi.STAGE_GATHER, _abi.STAGE_MERGE] + ([_abi.STAGE_SAMPLE] if node_major else [])
+    _, stage_ms = timed_steps(step, max(1, min(args.steps, 20)), hip, stages, _abi)
+    gather_ms = stage_ms[_abi.STAGE_GATHER]
     qheads = wl.n_tokens * wl.n_q_heads
     tree_idx = out[0].cpu().numpy()
 
-    gather_bytes = keys_scored * row_bytes
-    roof = {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(wl.name, "gather")
-    roof["kernel"] = "gather_kernel"
-    roof["algorithmic_bytes_per_launch"] = gather_bytes
-    roof["kernel_ms"] = gather_ms
+    if node_major:
+        flops = keys_scored * 2 * wl.d_latent
+        roof = {"bound": "mfma", "achieved": flops / (gather_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = load_traffic(wl.name, "pf_gather")
+        roof["kernel"] = "pf_gather (main pass)"
+        roof["algorithmic_flops_per_launch"] = flops
+        roof["kernel_ms"] = gather_ms
+        # centroid dots per query head: F_1 + b F_2 + b^2 F_3 + ...
+        dots, kept = 0, 1
+        for f in wl.fanout:
+            dots += kept * f
+            kept *= min(wl.b, f)
+        cflops = qheads * dots * 2 * wl.d_latent
+        dms = stage_ms[_abi.STAGE_DESCEND]
+        centroid = {"flops_per_call": cflops, "ms": dms, "achieved_TFLOPs": cflops / (dms * 1e-3) / 1e12,
+                    "frac_of_mfma_peak": cflops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "includes": "query projection, per-level MFMA scoring with exact top-b, child lists"}
+    else:
+        gather_bytes = keys_scored * row_bytes
+        roof = {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = load_traffic(wl.name, "gather")
+        roof["kernel"] = "gather_kernel"
+        roof["algorithmic_bytes_per_launch"] = gather_bytes
+        roof["kernel_ms"] = gather_ms
+        centroid = None
 
     result = {
         "metric": METRIC, "value": qheads / (ms_step * 1e-3), "unit": "query-heads/s", "n_gpus": 1,
@@ -227,16 +275,33 @@ def main():
         "keys_scored_per_s": keys_scored / (ms_step * 1e-3),
         "keys_scored_per_step": keys_scored,
         "roofline": roof,
+        "select_path": "node-major" if node_major else "per-query-head",
+        "stages_ms": {name: stage_ms.get(st) for name, st in (("descend", _abi.STAGE_DESCEND),
+                      ("sample", _abi.STAGE_SAMPLE), ("gather", _abi.STAGE_GATHER), ("merge", _abi.STAGE_MERGE))},
         "build_ms": build_ms,
     }
+    if centroid is not None:
+        result["centroid_scoring"] = centroid
 
-    if not args.no_flat:
+    if not args.no_flat and node_major:
+        # the full scan has no node-major form yet: one call of the
+        # per-query-head scan over a prefill batch reads the whole cache once
+        # per token and KV head
+        result["flat"] = {"skipped": "full scan of a prefill batch not timed (no matrix-core form yet)"}
+    elif not args.no_flat:
         fsteps = args.flat_steps or max(5, min(args.steps, 50))
         fout = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, flat=True)
         for _ in range(3):
             li.flat_select(qd, pd, prm, out=fout)
-        flat_ms, flat_kernel_ms = timed_steps(lambda: li.flat_select(qd, pd, prm, out=fout), fsteps, hip,
-                                              _abi.STAGE_FLAT, _abi)
+        fstep = lambda: li.flat_select(qd, pd, prm, out=fout)  # noqa: E731
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(fsteps):
+            fstep()
+        torch.cuda.synchronize()
+        flat_ms = (time.perf_counter() - t0) * 1e3 / fsteps
+        _, fst = timed_steps(fstep, max(1, min(fsteps, 10)), hip, [_abi.STAGE_FLAT], _abi)
+        flat_kernel_ms = fst[_abi.STAGE_FLAT]
         flat_idx = fout[0].cpu().numpy()
         s0, k = wl.sink, wl.k
         rec = []

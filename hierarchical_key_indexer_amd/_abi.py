@@ -19,9 +19,10 @@ DTYPES = {"f32": LSA_F32, "bf16": LSA_BF16}
 BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
 
 EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
-           "lsa_select_workspace_bytes", "lsa_select", "lsa_flat_workspace_bytes", "lsa_flat_select",
-           "lsa_last_error", "lsa_abi_version", "lsa_set_profile_events")
-STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT = 1, 2, 3, 4, 5
+           "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
+           "lsa_flat_select", "lsa_last_error", "lsa_abi_version", "lsa_set_profile_events")
+STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
+PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR = 0, 1
 
 
 class IndexDesc(ctypes.Structure):
@@ -78,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_select_out_width.argtypes, lib.lsa_select_out_width.restype = [S], I32
     lib.lsa_select_workspace_bytes.argtypes, lib.lsa_select_workspace_bytes.restype = [D, S, I32, I32], SZ
     lib.lsa_flat_workspace_bytes.argtypes, lib.lsa_flat_workspace_bytes.restype = [D, S, I32, I32], SZ
+    lib.lsa_select_path.argtypes, lib.lsa_select_path.restype = [D, S, I32, I32], I32
     lib.lsa_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
     lib.lsa_select.restype = ctypes.c_int
     lib.lsa_flat_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, SZ, VP]
@@ -135,6 +137,15 @@ def select_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:
     if n == 0:
         raise LsaError(LSA_ERR_INVALID_ARG, last_error())
     return n
+
+
+def select_path(desc, params, n_tokens, n_q_heads) -> int:
+    """PATH_PER_QUERY_HEAD or PATH_NODE_MAJOR: how lsa_select computes a
+    batch of this shape."""
+    r = load().lsa_select_path(ctypes.byref(desc), ctypes.byref(params), n_tokens, n_q_heads)
+    if r < 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return r
 
 
 def flat_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:

@@ -113,7 +113,7 @@ int32_t lsa_abi_version(void) { return 1; }
 
 int lsa_set_profile_events(int32_t stage, void* start, void* stop) {
   clear_err();
-  if (stage < LSA_STAGE_PROJECT || stage > LSA_STAGE_FLAT) return fail(LSA_ERR_INVALID_ARG, "unknown stage %d", stage);
+  if (stage < LSA_STAGE_PROJECT || stage > LSA_STAGE_SAMPLE) return fail(LSA_ERR_INVALID_ARG, "unknown stage %d", stage);
   if ((start == nullptr) != (stop == nullptr)) return fail(LSA_ERR_INVALID_ARG, "start and stop must both be set or both NULL");
   lsa::g_stage[stage].start = start;
   lsa::g_stage[stage].stop = stop;
@@ -161,6 +161,14 @@ size_t lsa_select_workspace_bytes(const lsa_index_desc* desc, const lsa_select_p
   clear_err();
   if (check_desc(desc) || check_params(desc, params, false) || check_shape(desc, n_tokens, n_q_heads, false)) return 0;
   return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false).bytes;
+}
+
+int32_t lsa_select_path(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                        int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) || check_params(desc, params, false) || check_shape(desc, n_tokens, n_q_heads, false)) return -1;
+  return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false).pf.ok ? LSA_PATH_NODE_MAJOR
+                                                                           : LSA_PATH_PER_QUERY_HEAD;
 }
 
 size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,

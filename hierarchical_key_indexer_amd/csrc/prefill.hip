@@ -894,7 +894,6 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     PF_CHECK("level lists");
   }
   prof_end(LSA_STAGE_DESCEND, st);
-  prof_begin(LSA_STAGE_GATHER, st);
   {
     const int lev = d.n_levels - 1;
     a.lev = lev;
@@ -905,14 +904,17 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     a.cstart = w.cstart[lev];
     const int64_t grid = (int64_t)d.n_kv_heads * L.nodes[lev] * a.CH;
     const unsigned rgrid = (unsigned)((R + kPfNW - 1) / kPfNW);
+    prof_begin(LSA_STAGE_SAMPLE, st);
     hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("sample pass");
     hipLaunchKernelGGL(pf_tau_kernel, dim3(rgrid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("thresholds");
+    prof_end(LSA_STAGE_SAMPLE, st);
+    prof_begin(LSA_STAGE_GATHER, st);
     hipLaunchKernelGGL((pf_gather<DL, false>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("gather");
+    prof_end(LSA_STAGE_GATHER, st);
   }
-  prof_end(LSA_STAGE_GATHER, st);
   prof_begin(LSA_STAGE_MERGE, st);
   switch (pl.merge_m) {
     case 1: launch_pf_merge<DL, 1>(a, st); break;

@@ -173,6 +173,20 @@ int lsa_select(const lsa_index_desc* desc, const void* index, const void* querie
                float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* How lsa_select computes a batch of this shape (same result either way):
+ *   LSA_PATH_PER_QUERY_HEAD  every query head descends and gathers on its own
+ *                            (decode and small batches)
+ *   LSA_PATH_NODE_MAJOR      every tree node is visited once with all the
+ *                            query heads that kept its parent, centroids and
+ *                            keys scored on bf16 matrix tiles (large batches:
+ *                            at least 256 query heads per KV head, bf16
+ *                            latent, per-parent beam, fanouts <= 64,
+ *                            b <= 16, k <= 2048)
+ * Returns -1 (and sets lsa_last_error) for invalid arguments. */
+typedef enum { LSA_PATH_PER_QUERY_HEAD = 0, LSA_PATH_NODE_MAJOR = 1 } lsa_select_path_kind;
+int32_t lsa_select_path(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                        int32_t n_q_heads);
+
 /* Bytes of device workspace lsa_flat_select needs; 0 if invalid. */
 size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
                                 int32_t n_tokens, int32_t n_q_heads);
@@ -193,7 +207,9 @@ typedef enum {
   LSA_STAGE_DESCEND = 2, /* centroid scoring and descent                    */
   LSA_STAGE_GATHER = 3,  /* gather-and-score with top-k (lsa_select)       */
   LSA_STAGE_MERGE = 4,   /* merge of split top-k lists                      */
-  LSA_STAGE_FLAT = 5     /* full scan with top-k (lsa_flat_select)         */
+  LSA_STAGE_FLAT = 5,    /* full scan with top-k (lsa_flat_select)         */
+  LSA_STAGE_SAMPLE = 6   /* node-major path: sampled scores and per-query
+                            thresholds (between DESCEND and GATHER)        */
 } lsa_stage;
 
 /* Instrumentation: until reset, every lsa_select / lsa_flat_select call on

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(A):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = A.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -125,3 +125,24 @@ def test_validation_rejects_bad_calls_before_any_device_work(A):
     # global beam limit
     g = A.SelectParams.make(65, 2048, 4, 512, "global")
     assert A.load().lsa_select_workspace_bytes(ctypes.byref(d), ctypes.byref(g), 1, 32) == 0
+
+
+def test_select_path_follows_the_batch_shape(A):
+    """Decode batches take the per-query-head path, large bf16 batches the
+    node-major path; fp32 latents, the global beam, wide fanouts and large k
+    stay on the per-query-head path."""
+    dec, pre = get_workload("decode_1m"), get_workload("prefill_1m")
+    d = A.IndexDesc.of(dec)
+    p = A.SelectParams.make(dec.b, dec.k, dec.sink, dec.window)
+    assert A.select_path(d, p, 1, 32) == A.PATH_PER_QUERY_HEAD
+    assert A.select_path(d, p, 4096, 32) == A.PATH_NODE_MAJOR
+    assert A.select_path(d, p, 63, 32) == A.PATH_PER_QUERY_HEAD      # 252 query heads per KV head
+    assert A.select_path(d, p, 64, 32) == A.PATH_NODE_MAJOR          # 256
+    assert A.select_path(d, A.SelectParams.make(16, 2048, 4, 512, "global"), 4096, 32) == A.PATH_PER_QUERY_HEAD
+    assert A.select_path(d, A.SelectParams.make(16, 4096, 4, 512), 4096, 32) == A.PATH_PER_QUERY_HEAD
+    tiny = get_workload("tiny_flat_65k")
+    dt = A.IndexDesc.of(tiny)
+    assert A.select_path(dt, A.SelectParams.make(8, 256, 4, 128), 4096, 1) == A.PATH_PER_QUERY_HEAD
+    assert A.select_path(A.IndexDesc.of(pre), A.SelectParams.make(16, 2048, 4, 512), 4096, 32) == A.PATH_NODE_MAJOR
+    with pytest.raises(A.LsaError):
+        A.select_path(d, p, 1, 7)

@@ -11,7 +11,7 @@ import pytest
 
 from oracle import lsa_oracle as O
 from synth import gen_keys, gen_queries, gen_W, get_workload
-from tests.gpu_helpers import _li, gpu_select
+from tests.gpu_helpers import _abi, _li, _params, gpu_select
 from tests.parity import compare_select, log
 
 pytestmark = pytest.mark.gpu
@@ -66,6 +66,8 @@ def test_prefill_path_on_oracle_index(case):
     pos = _positions(wl)
     li = _li(desc, O.index_blob(oidx))
     prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    A = _abi()
+    assert A.select_path(li.desc, _params(prm), wl.n_tokens, wl.n_q_heads) == A.PATH_NODE_MAJOR
     gi, gs, gl = gpu_select(li, queries, pos, prm)
     valid = [t for t in range(wl.n_tokens) if 0 <= pos[t] < wl.n_keys]
     pairs = [(t, hq) for t in valid for hq in range(wl.n_q_heads)]
