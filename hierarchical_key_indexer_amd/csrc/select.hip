@@ -214,7 +214,7 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   }
   if (!a.tau) return;
   // Sampled threshold: score NS candidates spread evenly over the leaf list
-  // and keep the r-th best sample key, r chosen so that about 3k candidates
+  // and keep the r-th best sample key, r chosen so that about 2k candidates
   // are expected above it.  The gather appends only keys above this value;
   // a query head that ends with fewer than k such keys is redone without it.
   __syncthreads();
@@ -223,9 +223,9 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   u64 tau = 0ull;
   if (p >= 0 && (int64_t)p < a.N && (int64_t)total > 4 * (int64_t)a.k) {
     // every wave scores 64 of BLOCK evenly spaced candidates and keeps its
-    // r-th best (r = expected share of 3k); tau is the median wave value
+    // r-th best (r = expected share of 2k); tau is the median wave value
     const int64_t NS = BLOCK;
-    const int r = (int)((3LL * a.k * 64 + total - 1) / total);
+    const int r = (int)((2LL * a.k * 64 + total - 1) / total);
     const int64_t o = (int64_t)threadIdx.x * total / NS;
     int lo_i = 0, hi_i = nf;   // fb[lo_i] <= o < fb[hi_i]
     while (hi_i - lo_i > 1) {
@@ -364,6 +364,19 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
     return;
   }
   const u64* src = a.part_keys + qh * a.part_cap;
+  if (n_in <= CAP) {
+    // everything fits the buffer: one coalesced load and one selection
+    for (int i = threadIdx.x; i < n_in; i += BLOCK) buf[i] = src[i];
+    __syncthreads();
+    int n = n_in;
+    if (n > a.k) {
+      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+      n = a.k;
+    }
+    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
+                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    return;
+  }
   u64 lowest = 0ull;                         // keys below this are never needed
   if (n_in > 8 * a.k) {
     uint32_t need = (uint32_t)a.k;
