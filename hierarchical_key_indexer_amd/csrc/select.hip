@@ -93,6 +93,60 @@ __device__ __forceinline__ void wave_select_top(const u64* key, int need, u64* i
   for (int j = 0; j < J; ++j) in[j] |= cand[j];
 }
 
+// Mark the `need` largest of the nonzero 32-bit keys the wave holds (J per
+// lane; equal keys rank by slot j, then by lane): bit-serial select with
+// ballots from the top bit down until the undecided keys are exactly the
+// ones still needed; keys equal in all 32 bits take the lowest (j, lane).
+template <int J>
+__device__ __forceinline__ void wave_select_top32(const uint32_t* key, int need, u64* in) {
+  u64 cand[J];
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    cand[j] = __ballot(key[j] != 0u);
+    in[j] = 0ull;
+    ncand += __popcll(cand[j]);
+  }
+  if (ncand <= need) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) in[j] = cand[j];
+    return;
+  }
+  int remaining = need;
+  for (int bit = 31; bit >= 0 && ncand > remaining; --bit) {
+    u64 ones[J];
+    int c1 = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      ones[j] = __ballot((key[j] >> bit) & 1u) & cand[j];
+      c1 += __popcll(ones[j]);
+    }
+    ncand = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (c1 >= remaining) {
+        cand[j] = ones[j];                   // the best `remaining` all have this bit
+      } else {
+        in[j] |= ones[j];                    // all of these are in
+        cand[j] &= ~ones[j];
+      }
+      ncand += __popcll(cand[j]);
+    }
+    if (c1 < remaining) remaining -= c1;
+  }
+  // cand: keys still tied over every bit; the first `remaining` in (j, lane) order
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    u64 c = cand[j];
+    while (c != 0ull && remaining > 0) {
+      const u64 low = c & (~c + 1ull);
+      in[j] |= low;
+      c ^= low;
+      --remaining;
+    }
+  }
+}
+
 template <typename KT, typename LT, int DL, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   constexpr int NW = BLOCK / 64;
@@ -126,6 +180,50 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
     if (a.beam == LSA_BEAM_PER_PARENT) {
       const int NJ = (F + 63) / 64;
       const int bs = min(a.b, F);
+      if (F <= 64) {
+        // A parent's children are one contiguous block of centroid rows: LPK
+        // lanes read a row (16 bytes each, so a load instruction covers KPW
+        // whole rows) and reduce their partial dots with DPP; each lane then
+        // takes its own child's score and the wave ranks them.
+        constexpr int E = Lat<LT>::PER16;
+        constexpr int LPK = DL / E;           // lanes per centroid row
+        constexpr int KPW = 64 / LPK;         // rows per load instruction
+        constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
+        const int lig = lane % LPK, g = lane / LPK;
+        QSlice<LT> qv;
+        qv.load(q + lig * E);
+        for (int i = w; i < nf; i += NW) {
+          const int64_t node0 = (int64_t)fa[i] * F;
+          uint4 v[NR];
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int c = r * KPW + g;
+            v[r] = make_uint4(0u, 0u, 0u, 0u);
+            if (c < F) v[r] = *(const uint4*)(cs + (node0 + c) * DL + lig * E);
+          }
+          int o0 = 0, o1 = 0;
+          if (lane < F) {
+            o0 = off[node0 + lane];
+            o1 = off[node0 + lane + 1];
+          }
+          float part[NR];
+#pragma unroll
+          for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
+          // child `lane` is row g' = lane % KPW of round lane / KPW, summed at lane g' * LPK
+          float sc = 0.f;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const float x = __shfl(part[r], (lane % KPW) * LPK, 64);
+            if (lane / KPW == r) sc = x;
+          }
+          const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
+          u64 in[1];
+          wave_select_top32<1>(&key, bs, in);
+          // kept in child order (ties went to the lower child id)
+          if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
+          for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
+        }
+      } else
       for (int i = w; i < nf; i += NW) {
         const int par = fa[i];
         u64 key[4];
@@ -235,13 +333,18 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
     const int64_t row = fa[lo_i] + (o - fb[lo_i]);
     const int j = a.perm[(size_t)h * a.N + row];
     const float sc = row_dot<LT, DL>((const LT*)a.lat + ((size_t)h * a.N + row) * DL, q);
-    u64 key[1] = {(j >= a.sink && j <= p - a.window) ? rank_key(sc, j) : 0ull};
-    const int nvalid = __popcll(__ballot(key[0] != 0ull));
+    const uint32_t key = (j >= a.sink && j <= p - a.window) ? order_u32(sc) : 0u;
+    const int nvalid = __popcll(__ballot(key != 0u));
     u64 wt = 0ull;
     if (r < nvalid) {
       u64 in[1];
-      wave_select_top<1>(key, r, in);
-      wt = wave_min_u64(((in[0] >> lane) & 1ull) ? key[0] : ~0ull);
+      wave_select_top32<1>(&key, r, in);
+      // the r-th best score of the wave's samples, as the smallest rank key
+      // of that score
+      uint32_t m = ((in[0] >> lane) & 1ull) ? key : 0xFFFFFFFFu;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      wt = (u64)m << 32;
     }
     if (lane == 0) sk[w] = wt;
     __syncthreads();
