@@ -330,9 +330,29 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
       const int mid = (lo_i + hi_i) >> 1;
       if (fb[mid] <= o) lo_i = mid; else hi_i = mid;
     }
-    const int64_t row = fa[lo_i] + (o - fb[lo_i]);
+    const int row = fa[lo_i] + (int)(o - fb[lo_i]);
     const int j = a.perm[(size_t)h * a.N + row];
-    const float sc = row_dot<LT, DL>((const LT*)a.lat + ((size_t)h * a.N + row) * DL, q);
+    // the wave's 64 sample rows are read LPK lanes per row (16-byte slices,
+    // whole rows per load instruction) and the partial dots reduced with
+    // DPP; lane L then takes the score of sample L
+    constexpr int E = Lat<LT>::PER16, LPK = DL / E, KPW = 64 / LPK, NR = 64 / KPW;
+    const int lig = lane % LPK, g = lane / LPK;
+    QSlice<LT> qv;
+    qv.load(q + lig * E);
+    const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
+    uint4 v[NR];
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const int rw = __shfl(row, rr * KPW + g, 64);
+      v[rr] = *(const uint4*)(latb + (size_t)rw * DL + lig * E);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const float part = group_sum_lead<LPK>(qv.dot(v[rr]));
+      const float x = __shfl(part, (lane % KPW) * LPK, 64);
+      if (lane / KPW == rr) sc = x;
+    }
     const uint32_t key = (j >= a.sink && j <= p - a.window) ? order_u32(sc) : 0u;
     const int nvalid = __popcll(__ballot(key != 0u));
     u64 wt = 0ull;
@@ -936,16 +956,15 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   const Layout L = compute_layout(d);
   const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
   const double expect = avg_leaf * pl.nl_cap;
-  // a few query heads: split each over S workgroups so the chip fills; a
-  // split should hold >= 2k candidates (its local top-k then shrinks the
-  // merge input) and, on average, fit the split buffer with room to spare
-  // few query heads: split each over S workgroups so the chip fills (a few
-  // workgroups per CU); the sampled threshold keeps every split's append
+  // few query heads: split each over S workgroups so that the grid is one
+  // round of resident workgroups (the 256-thread gather holds 3 per CU: 768
+  // on 256 CUs; a fourth would run alone in a second round), each with at
+  // least 512 candidates; the sampled threshold keeps every split's append
   // list short
   int S = 1;
-  if (pl.qh < 1024) {
-    S = (int)((1024 + pl.qh - 1) / pl.qh);
-    const int by_work = (int)(expect / 1024.0);
+  if (pl.qh < 768) {
+    S = (int)((768 + pl.qh - 1) / pl.qh);
+    const int by_work = (int)(expect / 512.0);
     S = S < by_work ? S : by_work;
     S = S < 1 ? 1 : (S > 64 ? 64 : S);
   }
