@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_1m")
     ap.add_argument("--flat-steps", type=int, default=None)
+    ap.add_argument("--flat-tokens", type=int, default=64,
+                    help="tokens of a prefill chunk the full scan is timed on (scaled to the chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -284,10 +286,43 @@ def main():
         result["centroid_scoring"] = centroid
 
     if not args.no_flat and node_major:
-        # the full scan has no node-major form yet: one call of the
-        # per-query-head scan over a prefill batch reads the whole cache once
-        # per token and KV head
-        result["flat"] = {"skipped": "full scan of a prefill batch not timed (no matrix-core form yet)"}
+        # The full scan costs the same for every token (each scans the whole
+        # cache), so it is timed on a slice of the chunk's tokens and scaled
+        # to the chunk; recall is measured on the slice's rows.
+        ts = min(wl.n_tokens, args.flat_tokens)
+        t0s = wl.n_tokens - ts
+        qs, ps = qd[t0s:].contiguous(), pd[t0s:].contiguous()
+        fout = li.alloc_select_outputs(ts, wl.n_q_heads, prm, scores=True, flat=True)
+        li.flat_select(qs, ps, prm, out=fout)
+        fstep = lambda: li.flat_select(qs, ps, prm, out=fout)  # noqa: E731
+        fsteps = args.flat_steps or 3
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(fsteps):
+            fstep()
+        torch.cuda.synchronize()
+        slice_ms = (time.perf_counter() - t0) * 1e3 / fsteps
+        flat_idx = fout[0].cpu().numpy()
+        s0, k = wl.sink, wl.k
+        rec = []
+        for t_ in range(ts):
+            for hq in range(wl.n_q_heads):
+                a = tree_idx[t0s + t_, hq, s0:s0 + k]
+                b = flat_idx[t_, hq, s0:s0 + k]
+                a, b = set(a[a >= 0].tolist()), set(b[b >= 0].tolist())
+                rec.append(len(a & b) / max(1, len(b)))
+        chunk_ms = slice_ms * wl.n_tokens / ts
+        result["flat"] = {
+            "ms_per_call_slice": slice_ms, "slice_tokens": ts,
+            "ms_per_call_scaled_to_chunk": chunk_ms,
+            "query_heads_per_s": ts * wl.n_q_heads / (slice_ms * 1e-3),
+            "kernel": "flat_kernel",
+            "note": f"per-query-head full scan timed on the last {ts} tokens of the chunk; the chunk time is that "
+                    f"slice's time x {wl.n_tokens}/{ts} (every token scans the whole cache)",
+        }
+        result["recall_at_k_vs_flat"] = {"mean": float(np.mean(rec)), "p5": float(np.percentile(rec, 5)),
+                                         "rows": len(rec)}
+        result["speedup_vs_flat"] = chunk_ms / ms_step
     elif not args.no_flat:
         fsteps = args.flat_steps or max(5, min(args.steps, 50))
         fout = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, flat=True)
