@@ -20,9 +20,13 @@
 //                    compaction); with S > 1 the local lists are appended to
 //                    one per-query-head array
 //   merge_kernel     streaming top-k over that array, then the output row
+//   flat_tau_kernel  query latents for the flat scan and a sampled threshold per
+//                    query head (qproj_kernel: latents only, unsplit scans)
 //   qproj_kernel     query latents for the flat scan
 //   flat_kernel      full scan of one KV head's rows for its G query heads
 //                    (each row read once for G heads), streaming top-k each
+#include <algorithm>
+
 #include "select_device.h"
 
 namespace lsa {
@@ -439,6 +443,126 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   }
 }
 
+// r-th largest of the nonzero keys[0..n) in LDS (0 if fewer than r): three
+// histogram passes over 11, 11 and 10-bit digits from the top.  Block-wide.
+template <int BLOCK>
+__device__ uint32_t block_kth_u32(const uint32_t* keys, int n, int r, uint32_t* hist, int* dsel, uint32_t* asel) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0u, pmask = 0u, need = (uint32_t)r;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0), nb = pass < 2 ? 2048 : 1024;
+    for (int i = threadIdx.x; i < 2048; i += BLOCK) hist[i] = 0u;
+    if (threadIdx.x == 0) *dsel = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += BLOCK) {
+      const uint32_t v = keys[i];
+      if (v != 0u && (v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l owns bins [32 l, 32 l + 32); counts above come from higher lanes
+      uint32_t hb[32], sum = 0u;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        hb[i] = hist[32 * lane + i];
+        sum += hb[i];
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = (uint32_t)__shfl_down((int)incl, o, 64);
+        if (lane + o < 64) incl += x;
+      }
+      const uint32_t above = incl - sum;
+      if (above < need && need <= incl) {
+        uint32_t acc = above;
+        for (int i = 31; i >= 0; --i) {
+          if (acc + hb[i] >= need) {
+            *dsel = 32 * lane + i;
+            *asel = acc;
+            break;
+          }
+          acc += hb[i];
+        }
+      }
+    }
+    __syncthreads();
+    const int d = *dsel;
+    const uint32_t ab = *asel;
+    __syncthreads();
+    if (d < 0) return 0u;                       // fewer than r keys
+    prefix |= (uint32_t)d << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+    need -= ab;
+  }
+  return prefix;
+}
+
+// Query latents for the full scan, and a sampled threshold per query head:
+// NS rows of the KV head at a fixed stride (CSR order spreads them over every
+// leaf) are scored, whole rows per load instruction; the exact r-th best
+// candidate sample, r chosen so that about `target` candidates are expected
+// at or above it, gives the threshold the scan appends above.  A query head
+// with at most 2 target candidates takes none.
+template <typename KT, typename LT, int DL>
+__global__ __launch_bounds__(1024) void flat_tau_kernel(SelArgs a, int NS, int target) {
+  constexpr int BLOCK = 1024, NW = BLOCK / 64;
+  constexpr int E = Lat<LT>::PER16, LPK = DL / E, KPW = 64 / LPK;
+  constexpr int UB = 8;                          // sample rows in flight per lane group
+  extern __shared__ __align__(16) uint32_t skey[];   // [NS]
+  __shared__ uint32_t hist[2048];
+  __shared__ float qin[256 + kQSlices * DL];
+  __shared__ float q[DL];
+  __shared__ int dsel, nv_sh;
+  __shared__ uint32_t asel;
+  const int64_t qh = a.qh0 + blockIdx.x;
+  const int h = (int)(qh % a.Hq) / a.G;
+  query_latent<KT, LT, DL>(a, qh, h, qin, q);
+  if (threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;
+  const int p = a.q_pos[qh / a.Hq];
+  const int64_t n_cand = (p >= 0 && (int64_t)p < a.N) ? max(0, p - a.window - a.sink + 1) : 0;
+  if (n_cand <= 2 * (int64_t)target) {
+    if (threadIdx.x == 0) a.tau[qh] = 0ull;
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lig = lane % LPK, g = lane / LPK;
+  QSlice<LT> qv;
+  qv.load(q + lig * E);
+  const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
+  const int* permb = a.perm + (size_t)h * a.N;
+  const int clo = a.sink, chi = p - a.window;
+  if (threadIdx.x == 0) nv_sh = 0;
+  __syncthreads();
+  int nv = 0;
+  for (int base = w * KPW * UB; base < NS; base += NW * KPW * UB) {
+    uint4 v[UB];
+    int si[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      si[u] = base + u * KPW + g;
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (si[u] < NS) v[u] = *(const uint4*)(latb + ((int64_t)si[u] * a.N / NS) * DL + lig * E);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const float sc = group_sum_lead<LPK>(qv.dot(v[u]));
+      if (lig == 0 && si[u] < NS) {
+        const int j = permb[(int64_t)si[u] * a.N / NS];
+        const bool c = j >= clo && j <= chi;
+        skey[si[u]] = c ? order_u32(sc) : 0u;
+        nv += c ? 1 : 0;
+      }
+    }
+  }
+  atomicAdd(&nv_sh, nv);
+  __syncthreads();
+  const int64_t r = ((int64_t)target * nv_sh + n_cand - 1) / n_cand;
+  uint32_t kth = 0u;
+  if (r >= 1 && r <= nv_sh) kth = block_kth_u32<BLOCK>(skey, NS, (int)r, hist, &dsel, &asel);
+  if (threadIdx.x == 0) a.tau[qh] = (u64)kth << 32;
+}
+
 // ---------------------------------------------------------------------------
 // merge: streaming top-k over a query head's appended local lists
 // ---------------------------------------------------------------------------
@@ -466,6 +590,28 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   }
   const int n_in = (int)a.part_n[qh];
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
+  if (n_in < a.k && thr0 != 0ull && !a.nleaf) {
+    // full scan: the sampled threshold let fewer than k keys through; scan
+    // every row of the KV head here, without it
+    int* lpre = (int*)(buf + CAP);
+    int* lrow = lpre + 2;
+    if (threadIdx.x == 0) {
+      lpre[0] = 0;
+      lpre[1] = (int)a.N;
+      lrow[0] = 0;
+    }
+    __syncthreads();
+    const int h = (int)(qh % a.Hq) / a.G;
+    int n = gather_stream<LT, DL, M, 4, BLOCK>(a, qh, h, a.sink, p - a.window, lpre, lrow, 1, 0, a.N, 0ull, buf,
+                                               &n_sh, &rs);
+    if (n > a.k) {
+      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+      n = a.k;
+    }
+    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
+                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    return;
+  }
   if (n_in < a.k && thr0 != 0ull && a.nleaf) {
     // the sampled threshold let fewer than k keys through: score every
     // candidate of this query head here, without it
@@ -608,7 +754,7 @@ __global__ __launch_bounds__(1024) void flat_kernel(SelArgs a) {
   const int* permb = a.perm + (size_t)h * a.N;
   u64 thr[NQ];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) thr[j] = 0ull;
+  for (int j = 0; j < NQ; ++j) thr[j] = a.tau ? a.tau[qh_base + j] : 0ull;
   const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
   uint4 v[U], vn[U];
   int idx[U], idxn[U];
@@ -647,14 +793,19 @@ __global__ __launch_bounds__(1024) void flat_kernel(SelArgs a) {
       v[u] = vn[u];
       idx[u] = idxn[u];
     }
-    __syncthreads();
+    // the barrier of every round also keeps the waves' streams in step,
+    // which reads faster than letting them drift apart
+    {
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      if (n_sh[j] + ROUND > CAP) {
-        const int n = n_sh[j];
-        thr[j] = topk_compact<BLOCK, M>(bufs + j * CAP, n, a.k, &rs);
-        if (threadIdx.x == 0) n_sh[j] = a.k;
-        __syncthreads();
+      for (int j = 0; j < NQ; ++j) {
+        if (n_sh[j] + ROUND > CAP) {
+          const int n = n_sh[j];
+          const u64 t2 = topk_compact<BLOCK, M>(bufs + j * CAP, n, a.k, &rs);
+          thr[j] = t2 > thr[j] ? t2 : thr[j];
+          if (threadIdx.x == 0) n_sh[j] = a.k;
+          __syncthreads();
+        }
       }
     }
   }
@@ -699,6 +850,7 @@ int pick_m(int need, int block) {
 constexpr int kMergeBlock = 1024;
 constexpr int kSplitM = 8;                 // 1024-thread split buffer: 8192 keys
 constexpr int kFlatU = 4;
+constexpr int kFlatR = 40;                 // samples expected above a full-scan threshold
 
 struct SelWs {
   float* qlat;
@@ -721,10 +873,8 @@ size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const S
     w.leafrow = c.take<int>((size_t)(qh * pl.nl_cap));
     w.leafpre = c.take<int>((size_t)(qh * (pl.nl_cap + 1)));
     w.nleaf = c.take<int>((size_t)qh);
-    w.tau = c.take<unsigned long long>((size_t)qh);
-  } else {
-    w.tau = nullptr;
   }
+  w.tau = c.take<unsigned long long>((size_t)qh);
   const int S = flat ? pl.flat_splits : pl.splits;
   w.part_keys = nullptr;
   w.part_n = nullptr;
@@ -884,10 +1034,29 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   a.part_cap = (int64_t)a.S * p.k;
   const int G = a.G;
   prof_begin(LSA_STAGE_PROJECT, st);
-  for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
-    a.qh0 = q0;
-    const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
-    hipLaunchKernelGGL((qproj_kernel<KT, LT, DL>), dim3((unsigned)nq), dim3(256), 0, st, a);
+  if (a.S > 1) {
+    // sampled thresholds: enough samples that about kFlatR of them are
+    // expected above the threshold, which aims at >= 8k candidates
+    int64_t ns = 2048;
+    while (ns < 16384 && ns * 8 * (int64_t)p.k < (int64_t)kFlatR * d.n_keys) ns <<= 1;
+    const int64_t tg = std::max<int64_t>(8 * (int64_t)p.k, ((int64_t)kFlatR * d.n_keys + ns - 1) / ns);
+    const int target = (int)std::min<int64_t>(tg, (int64_t)1 << 30);
+    auto tk = flat_tau_kernel<KT, LT, DL>;
+    const size_t tlds = (size_t)ns * 4;
+    allow_lds(tk, tlds);
+    for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
+      a.qh0 = q0;
+      const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
+      hipLaunchKernelGGL(tk, dim3((unsigned)nq), dim3(1024), tlds, st, a, (int)ns, target);
+    }
+  } else {
+    // one workgroup per (token, KV head) writes its rows itself: no threshold
+    a.tau = nullptr;
+    for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
+      a.qh0 = q0;
+      const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
+      hipLaunchKernelGGL((qproj_kernel<KT, LT, DL>), dim3((unsigned)nq), dim3(256), 0, st, a);
+    }
   }
   prof_end(LSA_STAGE_PROJECT, st);
   a.qh0 = 0;

@@ -185,6 +185,30 @@ def test_tiny_flat_65k_build_and_select():
     assert np.array_equal(blob, _blob_of(gpu_build(desc, keys, W)))
 
 
+
+def test_flat_scan_threshold_across_positions():
+    """The split full scan appends only keys above a sampled threshold and
+    re-scans a query head whose threshold let fewer than k keys through.
+    Positions from the sequence start to the end make the threshold's sample
+    of valid candidates range from a handful to all of them (near the start
+    the threshold is noisy and a re-scan likely); every row must still equal
+    the oracle's full scan, and repeat calls give the same bits."""
+    wl = get_workload("tiny_flat_65k").scaled(n_tokens=4, k=64)
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    li = _li(desc, O.index_blob(oidx))
+    rng = np.random.default_rng(5)
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    for p0 in (600, 1500, 4000, 20000, wl.n_keys - 4):
+        pos = np.array([p0, p0 + 1, p0 + 2, p0 + 3], dtype=np.int32)
+        pos = np.minimum(pos, wl.n_keys - 1)
+        queries = gen_queries(wl.scaled(query_id=wl.query_id + int(rng.integers(1, 1000))), keys)
+        fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+        compare_select(oidx, queries, pos, prm, fi, fs, flat=True, log=log)
+        fi2, fs2, _ = gpu_select(li, queries, pos, prm, flat=True)
+        assert np.array_equal(fi, fi2) and np.array_equal(fs.view(np.uint32), fs2.view(np.uint32))
+
 @pytest.fixture(scope="module")
 def c1():
     wl = get_workload("decode_1m")
