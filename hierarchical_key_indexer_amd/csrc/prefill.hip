@@ -963,13 +963,15 @@ PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t
   for (int e = 0; e < d.n_levels; ++e) {
     const double parents = (double)d.n_kv_heads * (double)L.nodes[e];
     const double tiles = (double)R * pl.nl[e] / parents / 32.0;
-    pl.ch[e] = clampi((int64_t)ceil(tiles / (2.0 * kPfNW)), 1, 4096);
+    pl.ch[e] = clampi((int64_t)ceil(tiles / (4.0 * kPfNW)), 1, 4096);
   }
   {
     const int lev = d.n_levels - 1;
     const double rows_per_leaf = (double)R * nl / ((double)d.n_kv_heads * (double)L.nodes[lev + 1]);
     const double items = (double)d.fanout[lev] * ceil(rows_per_leaf / 32.0);
-    pl.chg = clampi((int64_t)ceil(items / (2.0 * kPfNW)), 1, 4096);
+    // several items per wave: a short workgroup costs more to dispatch than
+    // its items take
+    pl.chg = clampi((int64_t)ceil(items / (4.0 * kPfNW)), 1, 4096);
   }
   pl.bytes = carve_prefill(d, pl, R, nullptr, nullptr);
   pl.ok = true;
