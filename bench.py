@@ -153,6 +153,20 @@ def cpu_baseline(wl, keys, W, queries, pos):
     }
 
 
+def recall_rows(tree_out, flat_out, sink, k):
+    """Per query head |tree top-k & flat top-k| / |flat top-k|, computed on
+    the device from the two output tensors [T, Hq, width]."""
+    import numpy as np
+    import torch
+    a = tree_out[:, :, sink:sink + k].reshape(-1, k).long()
+    b = flat_out[:, :, sink:sink + k].reshape(-1, k).long()
+    bs, _ = torch.sort(b, dim=1)
+    pos = torch.searchsorted(bs, a).clamp(max=k - 1)
+    hit = (torch.gather(bs, 1, pos) == a) & (a >= 0)
+    nb = (b >= 0).sum(1).clamp(min=1)
+    return np.asarray((hit.sum(1).double() / nb.double()).cpu())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,8 +174,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_1m")
     ap.add_argument("--flat-steps", type=int, default=None)
-    ap.add_argument("--flat-tokens", type=int, default=64,
-                    help="tokens of a prefill chunk the full scan is timed on (scaled to the chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -286,43 +298,38 @@ def main():
         result["centroid_scoring"] = centroid
 
     if not args.no_flat and node_major:
-        # The full scan costs the same for every token (each scans the whole
-        # cache), so it is timed on a slice of the chunk's tokens and scaled
-        # to the chunk; recall is measured on the slice's rows.
-        ts = min(wl.n_tokens, args.flat_tokens)
-        t0s = wl.n_tokens - ts
-        qs, ps = qd[t0s:].contiguous(), pd[t0s:].contiguous()
-        fout = li.alloc_select_outputs(ts, wl.n_q_heads, prm, scores=True, flat=True)
-        li.flat_select(qs, ps, prm, out=fout)
-        fstep = lambda: li.flat_select(qs, ps, prm, out=fout)  # noqa: E731
+        # The full scan of the whole chunk on the matrix cores (row-tiled):
+        # every key scored against every query head, with the same output
+        # rows as the tree.
+        fout = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, flat=True)
+        li.flat_select(qd, pd, prm, out=fout)
+        fstep = lambda: li.flat_select(qd, pd, prm, out=fout)  # noqa: E731
         fsteps = args.flat_steps or 3
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(fsteps):
             fstep()
         torch.cuda.synchronize()
-        slice_ms = (time.perf_counter() - t0) * 1e3 / fsteps
-        flat_idx = fout[0].cpu().numpy()
-        s0, k = wl.sink, wl.k
-        rec = []
-        for t_ in range(ts):
-            for hq in range(wl.n_q_heads):
-                a = tree_idx[t0s + t_, hq, s0:s0 + k]
-                b = flat_idx[t_, hq, s0:s0 + k]
-                a, b = set(a[a >= 0].tolist()), set(b[b >= 0].tolist())
-                rec.append(len(a & b) / max(1, len(b)))
-        chunk_ms = slice_ms * wl.n_tokens / ts
+        flat_ms = (time.perf_counter() - t0) * 1e3 / fsteps
+        fstages = [_abi.STAGE_PROJECT, _abi.STAGE_SAMPLE, _abi.STAGE_FLAT, _abi.STAGE_MERGE]
+        _, fst = timed_steps(fstep, fsteps, hip, fstages, _abi)
+        scan_ms = fst[_abi.STAGE_FLAT]
+        fflops = qheads * wl.n_keys * 2 * wl.d_latent
+        rec = recall_rows(out[0], fout[0], wl.sink, wl.k)
         result["flat"] = {
-            "ms_per_call_slice": slice_ms, "slice_tokens": ts,
-            "ms_per_call_scaled_to_chunk": chunk_ms,
-            "query_heads_per_s": ts * wl.n_q_heads / (slice_ms * 1e-3),
-            "kernel": "flat_kernel",
-            "note": f"per-query-head full scan timed on the last {ts} tokens of the chunk; the chunk time is that "
-                    f"slice's time x {wl.n_tokens}/{ts} (every token scans the whole cache)",
+            "ms_per_call": flat_ms, "query_heads_per_s": qheads / (flat_ms * 1e-3),
+            "keys_scored_per_s": qheads * wl.n_keys / (flat_ms * 1e-3),
+            "path": "row-tiled (matrix cores)", "kernel": "fs_scan_kernel", "kernel_ms": scan_ms,
+            "algorithmic_flops_per_launch": fflops,
+            "achieved_TFLOPs": fflops / (scan_ms * 1e-3) / 1e12,
+            "frac_of_mfma_peak": fflops / (scan_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "stages_ms": {name: fst.get(st) for name, st in (("project", _abi.STAGE_PROJECT),
+                          ("sample", _abi.STAGE_SAMPLE), ("scan", _abi.STAGE_FLAT), ("merge", _abi.STAGE_MERGE))},
+            "traffic": load_traffic(wl.name, "fs_scan"),
         }
-        result["recall_at_k_vs_flat"] = {"mean": float(np.mean(rec)), "p5": float(np.percentile(rec, 5)),
-                                         "rows": len(rec)}
-        result["speedup_vs_flat"] = chunk_ms / ms_step
+        result["recall_at_k_vs_flat"] = {"mean": float(rec.mean()), "p5": float(np.percentile(rec, 5)),
+                                         "rows": int(rec.size)}
+        result["speedup_vs_flat"] = flat_ms / ms_step
     elif not args.no_flat:
         fsteps = args.flat_steps or max(5, min(args.steps, 50))
         fout = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, flat=True)

@@ -20,9 +20,10 @@ BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
 
 EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
-           "lsa_flat_select", "lsa_last_error", "lsa_abi_version", "lsa_set_profile_events")
+           "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
+           "lsa_set_profile_events")
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
-PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR = 0, 1
+PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
 
 
 class IndexDesc(ctypes.Structure):
@@ -80,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_select_workspace_bytes.argtypes, lib.lsa_select_workspace_bytes.restype = [D, S, I32, I32], SZ
     lib.lsa_flat_workspace_bytes.argtypes, lib.lsa_flat_workspace_bytes.restype = [D, S, I32, I32], SZ
     lib.lsa_select_path.argtypes, lib.lsa_select_path.restype = [D, S, I32, I32], I32
+    lib.lsa_flat_select_path.argtypes, lib.lsa_flat_select_path.restype = [D, S, I32, I32], I32
     lib.lsa_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
     lib.lsa_select.restype = ctypes.c_int
     lib.lsa_flat_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, SZ, VP]
@@ -137,6 +139,15 @@ def select_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:
     if n == 0:
         raise LsaError(LSA_ERR_INVALID_ARG, last_error())
     return n
+
+
+def flat_select_path(desc, params, n_tokens, n_q_heads) -> int:
+    """PATH_PER_QUERY_HEAD or PATH_ROW_TILED: how lsa_flat_select computes a
+    batch of this shape."""
+    r = load().lsa_flat_select_path(ctypes.byref(desc), ctypes.byref(params), n_tokens, n_q_heads)
+    if r < 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return r
 
 
 def select_path(desc, params, n_tokens, n_q_heads) -> int:

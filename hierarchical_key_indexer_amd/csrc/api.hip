@@ -171,6 +171,14 @@ int32_t lsa_select_path(const lsa_index_desc* desc, const lsa_select_params* par
                                                                            : LSA_PATH_PER_QUERY_HEAD;
 }
 
+int32_t lsa_flat_select_path(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                             int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) || check_params(desc, params, true) || check_shape(desc, n_tokens, n_q_heads, true)) return -1;
+  return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, true).fs.ok ? LSA_PATH_ROW_TILED
+                                                                          : LSA_PATH_PER_QUERY_HEAD;
+}
+
 size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
                                 int32_t n_q_heads) {
   clear_err();

@@ -99,6 +99,23 @@ int launch_prefill(const lsa_index_desc& d, const lsa_select_params& p, const Pf
                    const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                    float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, char* err, size_t errlen);
 
+// Row-tiled full scan (prefill.hip): lsa_flat_select for large query batches
+// on a bf16 latent.
+struct FsPlan {
+  bool ok;                     // the path applies
+  int64_t ns;                  // sampled keys per KV head
+  int64_t cap;                 // appended keys per query head
+  int merge_m;                 // merge buffer entries per thread
+  int rb;                      // row blocks (256 query heads) per KV head
+  int split;                   // key splits per (KV head, row block)
+  int64_t keys;                // keys per split
+  size_t bytes;                // workspace bytes
+};
+FsPlan plan_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq);
+int launch_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, const FsPlan& pl, const void* index,
+                      const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                      float* out_scores, void* ws, hipStream_t st, char* err, size_t errlen);
+
 struct SelectPlan {
   int64_t qh;          // T * Hq
   int nl_cap;          // leaf-list capacity per query head
@@ -106,6 +123,7 @@ struct SelectPlan {
   int flat_splits;     // workgroups per (token, KV head) in the flat scan
   size_t bytes;        // workspace bytes
   PfPlan pf;           // node-major prefill path (pf.ok)
+  FsPlan fs;           // row-tiled full scan (fs.ok)
 };
 SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat);
 int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& plan,

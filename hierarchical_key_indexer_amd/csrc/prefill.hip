@@ -79,6 +79,12 @@ struct PfArgs {
   uint16_t* smp;               // [R][nl][spl] top 16 bits of order(score), 0 = not a candidate
   float* tauf;                 // [R] score threshold, -inf = none
   int64_t cap;                 // append capacity per row
+  // row-tiled full scan
+  bool flat;                   // every key in [sink, p - window] is a candidate of every row
+  int64_t ns;                  // sampled keys per KV head
+  int64_t fs_keys;             // keys per split
+  int fs_split;                // key splits per (KV head, row block)
+  int fs_rb;                   // row blocks per KV head
 };
 
 __device__ __forceinline__ int2 pf_entry(const PfArgs& a, int64_t pos, int h) {
@@ -704,7 +710,21 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   const float tau = a.tauf[row];
   const bool rescore = valid_p && ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf()));
   int nlv = 0, total = 0;
-  if (rescore || a.s.out_leaves) leaf_list(rescore, &nlv, &total);
+  if (a.flat) {
+    // a full scan's candidates are one range of the CSR latent
+    if (rescore) {
+      if (threadIdx.x == 0) {
+        lrow[0] = 0;
+        lpre[0] = 0;
+        lpre[1] = (int)a.s.N;
+      }
+      __syncthreads();
+      nlv = 1;
+      total = (int)a.s.N;
+    }
+  } else if (rescore || a.s.out_leaves) {
+    leaf_list(rescore, &nlv, &total);
+  }
   if (!valid_p) {
     write_invalid_row<BLOCK>(a.s.width, a.s.k, orow, srow);
     return;
@@ -736,6 +756,335 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
     n = k;
   }
   write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, k, a.s.window, orow, srow);
+}
+
+// ---------------------------------------------------------------------------
+// row-tiled full scan (lsa_flat_select for large query batches)
+// ---------------------------------------------------------------------------
+
+constexpr int kFsBlock = 256;                              // 4 waves
+constexpr int kFsWaveRows = 64;                            // two 32-row B tiles per wave
+constexpr int kFsRows = (kFsBlock / 64) * kFsWaveRows;     // rows per workgroup
+constexpr int kFsKT = 64;                                  // keys per LDS stage
+constexpr int kFsStage = 1024;                             // staged appends per wave (16 x 64)
+constexpr int kFsSampleR = 32;                             // order statistic kept per lane
+
+// In-order LDS traffic of one wave, kept in program order by the compiler.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Rows of a KV head in scan order: i = token * G + group member.
+__device__ __forceinline__ int fs_row(const PfArgs& a, int h, int64_t i) {
+  return (int)((i / a.s.G) * a.s.Hq + (int64_t)h * a.s.G + i % a.s.G);
+}
+
+// Per-row threshold of the full scan.  ns keys evenly spaced over the CSR
+// latent (a stratified sample: every bucket contributes in proportion to its
+// size) are scored on the matrix cores against 32 rows per wave.  Each lane
+// keeps the 32 best candidate scores of its half of the samples in a sorted
+// register list (one v_med3 per entry and insertion), and the threshold is
+// the smaller of the two halves' 32nd best, so at least 64 samples reach it
+// and about 64 N / ns keys are expected at or above it.  Rows with an invalid
+// position get +inf (nothing is appended); a row whose samples hold fewer
+// than 32 candidates per half gets -inf (every candidate is appended).
+template <int DL>
+__global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
+  constexpr int KS = DL / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t tiles = (a.TG + 31) / 32;          // row tiles per KV head
+  const int64_t gw = (int64_t)blockIdx.x * (kFsBlock / 64) + w;
+  if (gw >= tiles * a.s.Hkv) return;
+  const int h = (int)(gw / tiles);
+  const int64_t i = (gw % tiles) * 32 + l32;
+  int row = -1, chi = -1;
+  bool pv = false;
+  if (i < a.TG) {
+    row = fs_row(a, h, i);
+    const int p = a.s.q_pos[row / a.s.Hq];
+    pv = p >= 0 && (int64_t)p < a.s.N;
+    chi = pv ? p - a.s.window : -1;
+  }
+  v8s Bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+    Bq[s] = as_v8s(u);
+  }
+  const bf16_t* latb = (const bf16_t*)a.s.lat + (size_t)h * a.s.N * DL;
+  const int* permb = a.s.perm + (size_t)h * a.s.N;
+  const int64_t N = a.s.N, ns = a.ns;
+  // sample tile: key l32 of the tile is sample tile * 32 + l32
+  auto load = [&](int64_t tile, v8s* A, int* jl) {
+    const int64_t j = tile * 32 + l32;
+    const bool ok = j < ns;
+    const int64_t key = ok ? j * N / ns : 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) u = *(const uint4*)(latb + (size_t)key * DL + 16 * s + 8 * half);
+      A[s] = as_v8s(u);
+    }
+    const int pos = ok ? permb[key] : INT_MAX;
+    *jl = pos >= a.s.sink ? pos : INT_MAX;
+  };
+  float t[kFsSampleR];
+#pragma unroll
+  for (int q = 0; q < kFsSampleR; ++q) t[q] = -__builtin_huge_valf();
+  const int64_t ntile = (ns + 31) / 32;
+  v8s A[KS], An[KS];
+  int jl = INT_MAX, jn = INT_MAX;
+  load(0, A, &jl);
+  for (int64_t tile = 0; tile < ntile; ++tile) {
+    if (tile + 1 < ntile) load(tile + 1, An, &jn);
+    v16f acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+      const int jm = __shfl(jl, m, 64);
+      const float v = jm <= chi ? acc[r] : -__builtin_huge_valf();
+      if (__ballot(v > t[kFsSampleR - 1]) != 0ull) {
+#pragma unroll
+        for (int q = kFsSampleR - 1; q > 0; --q) t[q] = __builtin_amdgcn_fmed3f(t[q - 1], t[q], v);
+        t[0] = fmaxf(t[0], v);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) A[s] = An[s];
+    jl = jn;
+  }
+  const float mine = t[kFsSampleR - 1];
+  const float other = __shfl_xor(mine, 32, 64);
+  if (half == 0 && row >= 0) a.tauf[row] = pv ? fminf(mine, other) : __builtin_huge_valf();
+}
+
+// The scan.  A workgroup takes 256 rows of one KV head (64 per wave, as two
+// 32-row B operands held in registers) and one range of keys, staged through
+// LDS 64 keys at a time and shared by the four waves.  Every 32-key tile is
+// scored against both row tiles; a tile whose key positions all lie in every
+// row's candidate range skips the per-key range test.  Scores at or above the
+// row's threshold are staged in LDS per wave and flushed to the rows' append
+// lists with one global atomic per row and flush.
+template <int DL>
+__global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
+  constexpr int KS = DL / 16;
+  constexpr int RP = DL * 2 / 16;                  // 16-byte pieces per key row
+  constexpr int PITCH = DL * 2 + 16;               // LDS bytes per key row (the pad spreads rows over banks)
+  constexpr int PIECES = kFsKT * RP;
+  constexpr int PPT = (PIECES + kFsBlock - 1) / kFsBlock;
+  constexpr int NW = kFsBlock / 64;
+  constexpr int SE = kFsStage / 64;
+  __shared__ __align__(16) unsigned char klds[2][kFsKT * PITCH];
+  __shared__ __align__(16) int kpos[2][kFsKT];
+  __shared__ int kmx[2][kFsKT / 32];
+  __shared__ u64 skey[NW][kFsStage];
+  __shared__ uint8_t srl[NW][kFsStage];
+  __shared__ uint32_t scnt[NW][64];
+  __shared__ int srid[NW][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  // workgroup -> (KV head, key split, row block); with the KV heads a
+  // multiple of 8, all workgroups of a head run on one XCD, so its key
+  // stages are shared through that XCD's L2
+  const int64_t per_head = (int64_t)a.fs_rb * a.fs_split;
+  int64_t logical = blockIdx.x;
+  if (a.s.Hkv % 8 == 0) {
+    const int64_t x = logical % 8, q = logical / 8;
+    logical = (x + 8 * (q / per_head)) * per_head + q % per_head;
+  }
+  const int h = (int)(logical / per_head);
+  const int sp = (int)((logical % per_head) / a.fs_rb);
+  const int rb = (int)(logical % a.fs_rb);
+  // this lane's rows: row tile u holds rows i0 + 32 u + l32
+  const int64_t i0 = (int64_t)rb * kFsRows + w * kFsWaveRows;
+  int rowu[2], chi[2];
+  float tau[2];
+  v8s B[2][KS];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t i = i0 + 32 * u + l32;
+    rowu[u] = -1;
+    chi[u] = -1;
+    tau[u] = __builtin_huge_valf();
+    if (i < a.TG) {
+      const int row = fs_row(a, h, i);
+      const int p = a.s.q_pos[row / a.s.Hq];
+      if (p >= 0 && (int64_t)p < a.s.N) {
+        tau[u] = a.tauf[row];
+        chi[u] = p - a.s.window;
+      }
+      rowu[u] = row;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (rowu[u] >= 0) v = *(const uint4*)(a.qlat16 + (size_t)rowu[u] * DL + 16 * s + 8 * half);
+      B[u][s] = as_v8s(v);
+    }
+  }
+  srid[w][lane] = rowu[half];                      // staged row index 32 u + l32 -> row
+  // the smallest causal limit of the rows that can take keys
+  int chimin = INT_MAX;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (tau[u] < __builtin_huge_valf()) chimin = min(chimin, chi[u]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) chimin = min(chimin, __shfl_xor(chimin, o, 64));
+
+  const bf16_t* latb = (const bf16_t*)a.s.lat + (size_t)h * a.s.N * DL;
+  const int* permb = a.s.perm + (size_t)h * a.s.N;
+  const int64_t k0 = (int64_t)sp * a.fs_keys;
+  const int64_t k1 = min(a.s.N, k0 + a.fs_keys);
+  const int nst = k1 > k0 ? (int)((k1 - k0 + kFsKT - 1) / kFsKT) : 0;
+  uint4 pv[PPT];
+  int jv = INT_MAX;
+  auto gload = [&](int st) {
+    const int64_t kb = k0 + (int64_t)st * kFsKT;
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int c = threadIdx.x + q * kFsBlock;
+      pv[q] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < PIECES) {
+        const int64_t key = kb + c / RP;
+        if (key < k1) pv[q] = *(const uint4*)(latb + (size_t)key * DL + (c % RP) * 8);
+      }
+    }
+    if (threadIdx.x < kFsKT) {
+      const int64_t key = kb + threadIdx.x;
+      const int j = key < k1 ? permb[key] : INT_MAX;
+      jv = j >= a.s.sink ? j : INT_MAX;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int c = threadIdx.x + q * kFsBlock;
+      if (c < PIECES) *(uint4*)(klds[buf] + (c / RP) * PITCH + (c % RP) * 16) = pv[q];
+    }
+    if (threadIdx.x < kFsKT) {                     // wave 0: one position per lane
+      kpos[buf][threadIdx.x] = jv;
+      int mx = jv;
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+      if ((threadIdx.x & 31) == 0) kmx[buf][threadIdx.x >> 5] = mx;
+    }
+  };
+  // staged entries -> the rows' append lists
+  auto flush = [&](int n) {
+    scnt[w][lane] = 0u;
+    wave_lds_sync();
+    uint32_t lp[SE];
+#pragma unroll
+    for (int q = 0; q < SE; ++q) {
+      const int e = lane + 64 * q;
+      lp[q] = e < n ? atomicAdd(&scnt[w][srl[w][e]], 1u) : 0u;
+    }
+    wave_lds_sync();
+    const uint32_t c = scnt[w][lane];
+    uint32_t base = 0u;
+    if (c != 0u) base = atomicAdd(pf_count_of(a, srid[w][lane]), c);
+    wave_lds_sync();
+    scnt[w][lane] = base;
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < SE; ++q) {
+      const int e = lane + 64 * q;
+      if (e < n) {
+        const int rl = srl[w][e];
+        const uint32_t pos = scnt[w][rl] + lp[q];
+        if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)srid[w][rl] * a.cap + pos] = skey[w][e];
+      }
+    }
+    wave_lds_sync();
+  };
+
+  int cnt = 0;                                     // staged entries of this wave (wave-uniform)
+  if (nst > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) gload(st + 1);
+#pragma unroll
+    for (int t = 0; t < kFsKT / 32; ++t) {
+      v8s A[KS];
+      const unsigned char* kr = klds[cur] + (32 * t + l32) * PITCH + 16 * half;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) A[s] = as_v8s(*(const uint4*)(kr + 32 * s));
+      v16f acc0, acc1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[r] = 0.f;
+        acc1[r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[0][s], acc0, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[1][s], acc1, 0, 0, 0);
+      // results: lane holds its rows against keys m = 8 (r / 4) + 4 half + r % 4
+      const int* kp = kpos[cur] + 32 * t + 4 * half;
+      if (kmx[cur][t] > chimin) {
+        // some key lies outside some row's range: those scores become NaN,
+        // which no comparison passes and fmaxf ignores
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int4 jq = *(const int4*)(kp + 8 * q);
+          const int js[4] = {jq.x, jq.y, jq.z, jq.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (js[c] > chi[0]) acc0[4 * q + c] = __builtin_nanf("");
+            if (js[c] > chi[1]) acc1[4 * q + c] = __builtin_nanf("");
+          }
+        }
+      }
+      float m0 = acc0[0], m1 = acc1[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        m0 = fmaxf(m0, acc0[r]);
+        m1 = fmaxf(m1, acc1[r]);
+      }
+      if (__ballot(m0 >= tau[0] || m1 >= tau[1]) == 0ull) continue;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // one row tile adds at most 16 x 64 = kFsStage entries
+        u64 bal[16];
+        int tot = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bal[r] = __ballot((u ? acc1[r] : acc0[r]) >= tau[u]);
+          tot += __popcll(bal[r]);
+        }
+        if (tot == 0) continue;
+        if (cnt + tot > kFsStage) {
+          flush(cnt);
+          cnt = 0;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (bal[r] == 0ull) continue;
+          const float v = u ? acc1[r] : acc0[r];
+          if (v >= tau[u]) {
+            const int e = cnt + (int)mbcnt64(bal[r]);
+            skey[w][e] = rank_key(v, kp[8 * (r >> 2) + (r & 3)]);
+            srl[w][e] = (uint8_t)(32 * u + l32);
+          }
+          cnt += __popcll(bal[r]);
+        }
+      }
+    }
+    if (st + 1 < nst) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  if (cnt > 0) flush(cnt);
 }
 
 __global__ void pf_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
@@ -929,6 +1278,114 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
   return LSA_OK;
 }
 
+struct FsWs {
+  float* qlat;
+  uint16_t* qlat16;
+  float* tauf;
+  u64* part_keys;
+  uint32_t* part_n;
+};
+
+size_t carve_flat_tiled(const lsa_index_desc& d, const FsPlan& pl, int64_t R, void* base, FsWs* out) {
+  Carver c(base);
+  FsWs w;
+  w.qlat = c.take<float>((size_t)(R * d.d_latent));
+  w.qlat16 = c.take<uint16_t>((size_t)(R * d.d_latent));
+  w.tauf = c.take<float>((size_t)R);
+  w.part_keys = c.take<u64>((size_t)(R * pl.cap));
+  w.part_n = c.take<uint32_t>((size_t)R);
+  if (out) *out = w;
+  return align_up(c.used);
+}
+
+template <typename KT, int DL>
+int run_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, const FsPlan& pl, const void* index,
+                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                   float* out_scores, void* ws, hipStream_t st, char* err, size_t errlen) {
+  const Layout L = compute_layout(d);
+  const char* blob = (const char*)index;
+  const int64_t R = (int64_t)T * Hq;
+  FsWs w;
+  carve_flat_tiled(d, pl, R, ws, &w);
+  PfArgs a;
+  memset(&a, 0, sizeof(a));
+  SelArgs& s = a.s;
+  s.lat = blob + L.latent;
+  s.perm = (const int*)(blob + L.perm);
+  s.N = d.n_keys;
+  s.Hkv = d.n_kv_heads;
+  s.G = Hq / d.n_kv_heads;
+  s.Hq = Hq;
+  s.T = T;
+  s.d_head = d.d_head;
+  s.queries = queries;
+  s.W = (const float*)(blob + L.W);
+  s.qlat = w.qlat;
+  s.q_pos = q_pos;
+  s.sink = p.sink;
+  s.window = p.window;
+  s.k = p.k;
+  s.width = p.sink + p.k + p.window;
+  s.L = d.n_levels;
+  s.part_keys = w.part_keys;
+  s.part_n = w.part_n;
+  s.part_cap = pl.cap;
+  s.out_idx = out_idx;
+  s.out_scores = out_scores;
+  a.qlat16 = w.qlat16;
+  a.R = R;
+  a.TG = T * s.G;
+  a.nl = 1;
+  a.tauf = w.tauf;
+  a.cap = pl.cap;
+  a.flat = true;
+  a.ns = pl.ns;
+  a.fs_keys = pl.keys;
+  a.fs_split = pl.split;
+  a.fs_rb = pl.rb;
+
+#define FS_CHECK(what)                                                               \
+  do {                                                                               \
+    hipError_t e_ = hipGetLastError();                                               \
+    if (e_ != hipSuccess) {                                                          \
+      snprintf(err, errlen, "%s launch failed: %s", what, hipGetErrorString(e_));    \
+      return LSA_ERR_HIP;                                                            \
+    }                                                                                \
+  } while (0)
+
+  prof_begin(LSA_STAGE_PROJECT, st);
+  hipLaunchKernelGGL((pf_qproj_kernel<KT, DL>), dim3((unsigned)R), dim3(256), 0, st, a);
+  prof_end(LSA_STAGE_PROJECT, st);
+  FS_CHECK("query projection");
+  prof_begin(LSA_STAGE_SAMPLE, st);
+  {
+    const int64_t waves = (int64_t)d.n_kv_heads * ((a.TG + 31) / 32);
+    const int64_t blocks = (waves + kFsBlock / 64 - 1) / (kFsBlock / 64);
+    hipLaunchKernelGGL((fs_tau_kernel<DL>), dim3((unsigned)blocks), dim3(kFsBlock), 0, st, a);
+  }
+  prof_end(LSA_STAGE_SAMPLE, st);
+  FS_CHECK("thresholds");
+  prof_begin(LSA_STAGE_FLAT, st);
+  {
+    const int64_t blocks = (int64_t)d.n_kv_heads * pl.rb * pl.split;
+    hipLaunchKernelGGL((fs_scan_kernel<DL>), dim3((unsigned)blocks), dim3(kFsBlock), 0, st, a);
+  }
+  prof_end(LSA_STAGE_FLAT, st);
+  FS_CHECK("full scan");
+  prof_begin(LSA_STAGE_MERGE, st);
+  switch (pl.merge_m) {
+    case 1: launch_pf_merge<DL, 1>(a, st); break;
+    case 2: launch_pf_merge<DL, 2>(a, st); break;
+    case 4: launch_pf_merge<DL, 4>(a, st); break;
+    case 8: launch_pf_merge<DL, 8>(a, st); break;
+    default: launch_pf_merge<DL, 16>(a, st); break;
+  }
+  prof_end(LSA_STAGE_MERGE, st);
+  FS_CHECK("merge");
+#undef FS_CHECK
+  return LSA_OK;
+}
+
 }  // namespace
 
 PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq) {
@@ -988,6 +1445,52 @@ int launch_prefill(const lsa_index_desc& d, const lsa_select_params& p, const Pf
   }
   if (kb) return run_prefill<bf16_t, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
   return run_prefill<float, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+}
+
+
+FsPlan plan_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq) {
+  FsPlan pl;
+  memset(&pl, 0, sizeof(pl));
+  pl.ok = false;
+  if (d.latent_dtype != LSA_BF16 || (d.d_latent != 32 && d.d_latent != 64)) return pl;
+  if (p.k > 2048 || p.k < 1) return pl;
+  const int G = Hq / d.n_kv_heads;
+  const int64_t TG = (int64_t)T * G, R = (int64_t)T * Hq, N = d.n_keys;
+  if (TG < kPfMinRows || R >= ((int64_t)1 << 31)) return pl;
+  // about 64 N / ns keys are expected at or above the sampled threshold:
+  // aim at 2k, and keep 5k places per row (each half's 32nd best sample
+  // sits within a factor 2.5 of its mean far beyond one row in a billion)
+  int64_t ns = (32 * N + p.k - 1) / p.k;
+  ns = (ns + 31) / 32 * 32;
+  if (ns >= N) ns = N;
+  pl.ns = ns;
+  pl.cap = 5 * (int64_t)p.k < N ? 5 * (int64_t)p.k : N;
+  int capl = 512;
+  while (capl < 2 * p.k) capl <<= 1;
+  pl.merge_m = capl / kPfMergeBlock;
+  pl.rb = (int)((TG + kFsRows - 1) / kFsRows);
+  // enough workgroups for two per CU, each with at least 64 key stages
+  const int64_t want = (512 + (int64_t)d.n_kv_heads * pl.rb - 1) / ((int64_t)d.n_kv_heads * pl.rb);
+  const int64_t most = N / (64 * kFsKT) > 1 ? N / (64 * kFsKT) : 1;
+  int64_t S = want < most ? want : most;
+  S = S < 1 ? 1 : S;
+  pl.keys = ((N + S - 1) / S + kFsKT - 1) / kFsKT * kFsKT;
+  pl.split = (int)((N + pl.keys - 1) / pl.keys);
+  pl.bytes = carve_flat_tiled(d, pl, R, nullptr, nullptr);
+  pl.ok = true;
+  return pl;
+}
+
+int launch_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, const FsPlan& pl, const void* index,
+                      const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
+                      float* out_scores, void* ws, hipStream_t st, char* err, size_t errlen) {
+  const bool kb = d.key_dtype == LSA_BF16;
+  if (d.d_latent == 64) {
+    if (kb) return run_flat_tiled<bf16_t, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
+    return run_flat_tiled<float, 64>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
+  }
+  if (kb) return run_flat_tiled<bf16_t, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
+  return run_flat_tiled<float, 32>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
 }
 
 }  // namespace lsa

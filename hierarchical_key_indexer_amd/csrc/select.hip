@@ -1146,9 +1146,13 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   pl.flat_splits = (int)sf;
   pl.bytes = carve_select(d, p, pl, T, Hq, flat, nullptr, nullptr);
   memset(&pl.pf, 0, sizeof(pl.pf));
+  memset(&pl.fs, 0, sizeof(pl.fs));
   if (!flat) {
     pl.pf = plan_prefill(d, p, T, Hq);
     if (pl.pf.ok) pl.bytes = pl.pf.bytes;
+  } else {
+    pl.fs = plan_flat_tiled(d, p, T, Hq);
+    if (pl.fs.ok) pl.bytes = pl.fs.bytes;
   }
   return pl;
 }
@@ -1159,6 +1163,8 @@ int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const Sel
                   size_t errlen) {
   if (!flat && pl.pf.ok)
     return launch_prefill(d, p, pl.pf, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
+  if (flat && pl.fs.ok)
+    return launch_flat_tiled(d, p, pl.fs, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
   const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
 #define LSA_RUN(KT, LT, DLV) \
   return run_select<KT, LT, DLV>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen)

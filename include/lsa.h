@@ -183,9 +183,24 @@ int lsa_select(const lsa_index_desc* desc, const void* index, const void* querie
  *                            latent, per-parent beam, fanouts <= 64,
  *                            b <= 16, k <= 2048)
  * Returns -1 (and sets lsa_last_error) for invalid arguments. */
-typedef enum { LSA_PATH_PER_QUERY_HEAD = 0, LSA_PATH_NODE_MAJOR = 1 } lsa_select_path_kind;
+typedef enum {
+  LSA_PATH_PER_QUERY_HEAD = 0,
+  LSA_PATH_NODE_MAJOR = 1,
+  LSA_PATH_ROW_TILED = 2
+} lsa_select_path_kind;
 int32_t lsa_select_path(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
                         int32_t n_q_heads);
+
+/* Which kernels lsa_flat_select runs for this shape (same results either way):
+ *   LSA_PATH_PER_QUERY_HEAD  a streaming scan per (token, KV head) that reads
+ *                            every key once for the head's G query heads
+ *   LSA_PATH_ROW_TILED       a scan on the matrix cores: 256 query heads of a
+ *                            KV head per workgroup against every key, with a
+ *                            sampled per-query-head threshold (at least 256
+ *                            query heads per KV head, bf16 latent, k <= 2048)
+ * Returns -1 (and sets lsa_last_error) for invalid arguments. */
+int32_t lsa_flat_select_path(const lsa_index_desc* desc, const lsa_select_params* params, int32_t n_tokens,
+                             int32_t n_q_heads);
 
 /* Bytes of device workspace lsa_flat_select needs; 0 if invalid. */
 size_t lsa_flat_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(A):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = A.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -146,3 +146,22 @@ def test_select_path_follows_the_batch_shape(A):
     assert A.select_path(A.IndexDesc.of(pre), A.SelectParams.make(16, 2048, 4, 512), 4096, 32) == A.PATH_NODE_MAJOR
     with pytest.raises(A.LsaError):
         A.select_path(d, p, 1, 7)
+
+
+def test_flat_select_path_follows_the_batch_shape(A):
+    """Full scans of large bf16 batches run on the matrix cores (row-tiled);
+    decode batches, fp32 latents and k > 2048 keep the per-(token, KV head)
+    streaming scan."""
+    dec = get_workload("decode_1m")
+    d = A.IndexDesc.of(dec)
+    p = A.SelectParams.make(dec.b, dec.k, dec.sink, dec.window)
+    assert A.flat_select_path(d, p, 1, 32) == A.PATH_PER_QUERY_HEAD
+    assert A.flat_select_path(d, p, 63, 32) == A.PATH_PER_QUERY_HEAD     # 252 query heads per KV head
+    assert A.flat_select_path(d, p, 64, 32) == A.PATH_ROW_TILED          # 256
+    assert A.flat_select_path(d, p, 4096, 32) == A.PATH_ROW_TILED
+    assert A.flat_select_path(d, A.SelectParams.make(16, 4096, 4, 512), 4096, 32) == A.PATH_PER_QUERY_HEAD
+    tiny = get_workload("tiny_flat_65k")
+    assert A.flat_select_path(A.IndexDesc.of(tiny), A.SelectParams.make(8, 256, 4, 128), 4096, 1) == \
+        A.PATH_PER_QUERY_HEAD
+    with pytest.raises(A.LsaError):
+        A.flat_select_path(d, p, 1, 7)

@@ -55,6 +55,9 @@ def test_prefill_10m_one_head_sampled(head10m):
     pairs = [(int(t), int(h)) for t, h in zip(rng.integers(0, wl2.n_tokens, 48), rng.integers(0, 4, 48))]
     pairs += [(0, 0), (wl2.n_tokens - 1, 3)]
     compare_select(oidx, queries, pos, prm, gi, gs, gl, pairs=pairs, log=log)
+    log("[prefill_10m one head] GPU full scan (row-tiled), 8192 tokens x 4 heads")
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, pairs=pairs[:24], flat=True, log=log)
 
 
 @pytest.mark.timeout(900)

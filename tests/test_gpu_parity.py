@@ -9,7 +9,7 @@ import pytest
 
 from oracle import lsa_oracle as O
 from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
-from tests.gpu_helpers import _abi, _blob_of, _dev, _li, gpu_build, gpu_select
+from tests.gpu_helpers import _abi, _blob_of, _dev, _li, _params, gpu_build, gpu_select
 from tests.parity import check_build, compare_select, log
 
 pytestmark = pytest.mark.gpu
@@ -248,6 +248,11 @@ def test_prefill_1m_select_sampled(c1):
     pairs = [(int(t), int(h)) for t, h in zip(rng.integers(0, wl2.n_tokens, 96), rng.integers(0, 32, 96))]
     pairs += [(0, 0), (wl2.n_tokens - 1, 31)]
     compare_select(oidx, queries, pos, prm, gi, gs, gl, pairs=pairs, log=log)
+    A = _abi()
+    assert A.flat_select_path(li.desc, _params(prm), wl2.n_tokens, wl2.n_q_heads) == A.PATH_ROW_TILED
+    log("[prefill_1m] GPU full scan (row-tiled), 4096 tokens x 32 heads")
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, pairs=pairs, flat=True, log=log)
 
 
 def test_decode_1m_gpu_build(c1):

@@ -1,6 +1,6 @@
-"""GPU parity of the node-major prefill path (large query batches: at least
-256 query heads per KV head, bf16 latent, per-parent beam) against the CPU
-oracle, on oracle-built index blobs.  The cases cover two and three levels,
+"""GPU parity of the large-batch paths (at least 256 query heads per KV head,
+bf16 latent) against the CPU oracle, on oracle-built index blobs: the
+node-major tree selection (per-parent beam) and the row-tiled full scan.  The cases cover two and three levels,
 fanouts up to 64, an fp32 key store with a 32-dim latent, rows whose leaves
 hold more keys than the append capacity (sampled threshold, with rows near
 the sequence start that fall back to a full re-score) and rows that take
@@ -78,3 +78,33 @@ def test_prefill_path_on_oracle_index(case):
     gi2, gs2, gl2 = gpu_select(li, queries, pos, prm)
     assert np.array_equal(gi, gi2) and np.array_equal(gs.view(np.uint32), gs2.view(np.uint32))
     assert np.array_equal(np.sort(gl, axis=-1), np.sort(gl2, axis=-1))
+
+
+FLAT_CASES = dict(PF_CASES)
+# keys that are exact copies of 16 centers: every score is tied with about a
+# thousand others, so the sampled threshold lets a whole center through, the
+# append lists overflow and every row is re-scored in full
+FLAT_CASES["flat_duplicate_keys"] = _pf(n_centers=16, sigma=0.0, fanout=(4, 4), b=2, k=64)
+
+
+@pytest.mark.parametrize("case", list(FLAT_CASES))
+def test_row_tiled_full_scan_on_oracle_index(case):
+    wl = FLAT_CASES[case]
+    log(f"[row-tiled full scan] case={case} N={wl.n_keys} k={wl.k} T={wl.n_tokens} G={wl.group}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    queries = gen_queries(wl, keys)
+    pos = _positions(wl)
+    li = _li(desc, O.index_blob(oidx))
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    A = _abi()
+    assert A.flat_select_path(li.desc, _params(prm), wl.n_tokens, wl.n_q_heads) == A.PATH_ROW_TILED
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    valid = [t for t in range(wl.n_tokens) if 0 <= pos[t] < wl.n_keys]
+    pairs = [(t, hq) for t in valid for hq in range(wl.n_q_heads)]
+    compare_select(oidx, queries, pos, prm, fi, fs, pairs=pairs, flat=True, log=log)
+    bad = [t for t in range(wl.n_tokens) if t not in valid]
+    assert np.all(fi[bad] == -1) and np.all(np.isneginf(fs[bad])), "invalid positions"
+    fi2, fs2, _ = gpu_select(li, queries, pos, prm, flat=True)
+    assert np.array_equal(fi, fi2) and np.array_equal(fs.view(np.uint32), fs2.view(np.uint32))
