@@ -1031,19 +1031,28 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[1][s], acc1, 0, 0, 0);
       // results: lane holds its rows against keys m = 8 (r / 4) + 4 half + r % 4
+      // positions of this lane's 16 keys, read together (one LDS round trip)
       const int* kp = kpos[cur] + 32 * t + 4 * half;
-      if (kmx[cur][t] > chimin) {
-        // some key lies outside some row's range: those scores become NaN,
-        // which no comparison passes and fmaxf ignores
+      int js[16];
+      auto load_pos = [&]() {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int4 jq = *(const int4*)(kp + 8 * q);
-          const int js[4] = {jq.x, jq.y, jq.z, jq.w};
+          js[4 * q] = jq.x;
+          js[4 * q + 1] = jq.y;
+          js[4 * q + 2] = jq.z;
+          js[4 * q + 3] = jq.w;
+        }
+      };
+      const bool dirty = kmx[cur][t] > chimin;
+      if (dirty) {
+        // some key lies outside some row's range: those scores become NaN,
+        // which no comparison passes and fmaxf ignores
+        load_pos();
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (js[c] > chi[0]) acc0[4 * q + c] = __builtin_nanf("");
-            if (js[c] > chi[1]) acc1[4 * q + c] = __builtin_nanf("");
-          }
+        for (int r = 0; r < 16; ++r) {
+          if (js[r] > chi[0]) acc0[r] = __builtin_nanf("");
+          if (js[r] > chi[1]) acc1[r] = __builtin_nanf("");
         }
       }
       float m0 = acc0[0], m1 = acc1[0];
@@ -1053,6 +1062,7 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
         m1 = fmaxf(m1, acc1[r]);
       }
       if (__ballot(m0 >= tau[0] || m1 >= tau[1]) == 0ull) continue;
+      if (!dirty) load_pos();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         // one row tile adds at most 16 x 64 = kFsStage entries
@@ -1074,7 +1084,7 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
           const float v = u ? acc1[r] : acc0[r];
           if (v >= tau[u]) {
             const int e = cnt + (int)mbcnt64(bal[r]);
-            skey[w][e] = rank_key(v, kp[8 * (r >> 2) + (r & 3)]);
+            skey[w][e] = rank_key(v, js[r]);
             srl[w][e] = (uint8_t)(32 * u + l32);
           }
           cnt += __popcll(bal[r]);
