@@ -765,9 +765,10 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
 constexpr int kFsBlock = 256;                              // 4 waves
 constexpr int kFsWaveRows = 64;                            // two 32-row B tiles per wave
 constexpr int kFsRows = (kFsBlock / 64) * kFsWaveRows;     // rows per workgroup
-constexpr int kFsKT = 64;                                  // keys per LDS stage
 constexpr int kFsStage = 1024;                             // staged appends per wave (16 x 64)
 constexpr int kFsSampleR = 32;                             // order statistic kept per lane
+constexpr int64_t kFsSplitKeys = 16384;                     // keys per split of the scan
+constexpr int kFsDepth = 4;                                // key tiles in flight per wave
 
 // In-order LDS traffic of one wave, kept in program order by the compiler.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -866,24 +867,20 @@ __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
 }
 
 // The scan.  A workgroup takes 256 rows of one KV head (64 per wave, as two
-// 32-row B operands held in registers) and one range of keys, staged through
-// LDS 64 keys at a time and shared by the four waves.  Every 32-key tile is
-// scored against both row tiles; a tile whose key positions all lie in every
-// row's candidate range skips the per-key range test.  Scores at or above the
-// row's threshold are staged in LDS per wave and flushed to the rows' append
-// lists with one global atomic per row and flush.
+// 32-row B operands held in registers) and one range of keys.  Every wave
+// streams the range's 32-key tiles straight into its A operand (the four
+// waves read the same keys, so all but the first read hit the caches) with no
+// workgroup barrier: the next tile's loads and the current tile's MFMAs are
+// issued before the previous tile's scores are filtered, so loads, matrix
+// cores and the filter overlap.  A tile whose keys all lie in every row's
+// candidate range (one ballot) skips the per-key range test.  Scores at or
+// above the row's threshold are staged in LDS per wave and flushed to the
+// rows' append lists with one global atomic per row and flush.
 template <int DL>
-__global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
+__global__ __launch_bounds__(kFsBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void fs_scan_kernel(PfArgs a) {
   constexpr int KS = DL / 16;
-  constexpr int RP = DL * 2 / 16;                  // 16-byte pieces per key row
-  constexpr int PITCH = DL * 2 + 16;               // LDS bytes per key row (the pad spreads rows over banks)
-  constexpr int PIECES = kFsKT * RP;
-  constexpr int PPT = (PIECES + kFsBlock - 1) / kFsBlock;
   constexpr int NW = kFsBlock / 64;
   constexpr int SE = kFsStage / 64;
-  __shared__ __align__(16) unsigned char klds[2][kFsKT * PITCH];
-  __shared__ __align__(16) int kpos[2][kFsKT];
-  __shared__ int kmx[2][kFsKT / 32];
   __shared__ u64 skey[NW][kFsStage];
   __shared__ uint8_t srl[NW][kFsStage];
   __shared__ uint32_t scnt[NW][64];
@@ -891,8 +888,8 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   // workgroup -> (KV head, key split, row block); with the KV heads a
-  // multiple of 8, all workgroups of a head run on one XCD, so its key
-  // stages are shared through that XCD's L2
+  // multiple of 8, all workgroups of a head run on one XCD, so its keys are
+  // shared through that XCD's L2
   const int64_t per_head = (int64_t)a.fs_rb * a.fs_split;
   int64_t logical = blockIdx.x;
   if (a.s.Hkv % 8 == 0) {
@@ -942,39 +939,27 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
   const int* permb = a.s.perm + (size_t)h * a.s.N;
   const int64_t k0 = (int64_t)sp * a.fs_keys;
   const int64_t k1 = min(a.s.N, k0 + a.fs_keys);
-  const int nst = k1 > k0 ? (int)((k1 - k0 + kFsKT - 1) / kFsKT) : 0;
-  uint4 pv[PPT];
-  int jv = INT_MAX;
-  auto gload = [&](int st) {
-    const int64_t kb = k0 + (int64_t)st * kFsKT;
+  const int64_t ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
+  // tile i: A operand (key l32's dims) and the key's position.  A lane past
+  // the range loads the range's last key instead (its scores are masked by
+  // position), so the loads are unconditional and nothing here uses the
+  // loaded values: they stay in flight until the tile is scored.
+  auto tile_key = [&](int64_t i) { return min(k0 + i * 32 + l32, k1 - 1); };
+  auto load_tile = [&](int64_t i, v8s* A) {
+    const int64_t key = tile_key(i);
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      const int c = threadIdx.x + q * kFsBlock;
-      pv[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (c < PIECES) {
-        const int64_t key = kb + c / RP;
-        if (key < k1) pv[q] = *(const uint4*)(latb + (size_t)key * DL + (c % RP) * 8);
-      }
-    }
-    if (threadIdx.x < kFsKT) {
-      const int64_t key = kb + threadIdx.x;
-      const int j = key < k1 ? permb[key] : INT_MAX;
-      jv = j >= a.s.sink ? j : INT_MAX;
-    }
+    for (int s = 0; s < KS; ++s) A[s] = as_v8s(*(const uint4*)(latb + (size_t)key * DL + 16 * s + 8 * half));
   };
-  auto sstore = [&](int buf) {
+  auto mfma_tile = [&](const v8s* A, v16f& c0, v16f& c1) {
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      const int c = threadIdx.x + q * kFsBlock;
-      if (c < PIECES) *(uint4*)(klds[buf] + (c / RP) * PITCH + (c % RP) * 16) = pv[q];
+    for (int r = 0; r < 16; ++r) {
+      c0[r] = 0.f;
+      c1[r] = 0.f;
     }
-    if (threadIdx.x < kFsKT) {                     // wave 0: one position per lane
-      kpos[buf][threadIdx.x] = jv;
-      int mx = jv;
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
-      if ((threadIdx.x & 31) == 0) kmx[buf][threadIdx.x >> 5] = mx;
-    }
+    for (int s = 0; s < KS; ++s) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[0][s], c0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[1][s], c1, 0, 0, 0);
   };
   // staged entries -> the rows' append lists
   auto flush = [&](int n) {
@@ -1002,97 +987,96 @@ __global__ __launch_bounds__(kFsBlock) void fs_scan_kernel(PfArgs a) {
         if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)srid[w][rl] * a.cap + pos] = skey[w][e];
       }
     }
+    // loads and stores share one counter here: with the flush's stores
+    // drained, the key loads in flight stay countable across the flush
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
     wave_lds_sync();
   };
-
   int cnt = 0;                                     // staged entries of this wave (wave-uniform)
-  if (nst > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) gload(st + 1);
+  // results: lane holds its rows against keys m = 8 (r / 4) + 4 half + r % 4
+  auto epilogue = [&](v16f& acc0, v16f& acc1, int jraw, int64_t i) {
+    // a sink key, or a lane past the range, is no candidate
+    const int jl = (jraw >= a.s.sink && k0 + i * 32 + l32 < k1) ? jraw : INT_MAX;
+    int js[16];
+    auto positions = [&]() {
 #pragma unroll
-    for (int t = 0; t < kFsKT / 32; ++t) {
-      v8s A[KS];
-      const unsigned char* kr = klds[cur] + (32 * t + l32) * PITCH + 16 * half;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) A[s] = as_v8s(*(const uint4*)(kr + 32 * s));
-      v16f acc0, acc1;
+      for (int r = 0; r < 16; ++r) js[r] = __shfl(jl, 8 * (r >> 2) + 4 * half + (r & 3), 64);
+    };
+    const bool dirty = __ballot(jl > chimin) != 0ull;
+    if (dirty) {
+      // some key lies outside some row's range: those scores become NaN,
+      // which no comparison passes and fmaxf ignores
+      positions();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        acc0[r] = 0.f;
-        acc1[r] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[0][s], acc0, 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B[1][s], acc1, 0, 0, 0);
-      // results: lane holds its rows against keys m = 8 (r / 4) + 4 half + r % 4
-      // positions of this lane's 16 keys, read together (one LDS round trip)
-      const int* kp = kpos[cur] + 32 * t + 4 * half;
-      int js[16];
-      auto load_pos = [&]() {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 jq = *(const int4*)(kp + 8 * q);
-          js[4 * q] = jq.x;
-          js[4 * q + 1] = jq.y;
-          js[4 * q + 2] = jq.z;
-          js[4 * q + 3] = jq.w;
-        }
-      };
-      const bool dirty = kmx[cur][t] > chimin;
-      if (dirty) {
-        // some key lies outside some row's range: those scores become NaN,
-        // which no comparison passes and fmaxf ignores
-        load_pos();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (js[r] > chi[0]) acc0[r] = __builtin_nanf("");
-          if (js[r] > chi[1]) acc1[r] = __builtin_nanf("");
-        }
-      }
-      float m0 = acc0[0], m1 = acc1[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        m0 = fmaxf(m0, acc0[r]);
-        m1 = fmaxf(m1, acc1[r]);
-      }
-      if (__ballot(m0 >= tau[0] || m1 >= tau[1]) == 0ull) continue;
-      if (!dirty) load_pos();
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // one row tile adds at most 16 x 64 = kFsStage entries
-        u64 bal[16];
-        int tot = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          bal[r] = __ballot((u ? acc1[r] : acc0[r]) >= tau[u]);
-          tot += __popcll(bal[r]);
-        }
-        if (tot == 0) continue;
-        if (cnt + tot > kFsStage) {
-          flush(cnt);
-          cnt = 0;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (bal[r] == 0ull) continue;
-          const float v = u ? acc1[r] : acc0[r];
-          if (v >= tau[u]) {
-            const int e = cnt + (int)mbcnt64(bal[r]);
-            skey[w][e] = rank_key(v, js[r]);
-            srl[w][e] = (uint8_t)(32 * u + l32);
-          }
-          cnt += __popcll(bal[r]);
-        }
+        if (js[r] > chi[0]) acc0[r] = __builtin_nanf("");
+        if (js[r] > chi[1]) acc1[r] = __builtin_nanf("");
       }
     }
-    if (st + 1 < nst) sstore(cur ^ 1);
-    __syncthreads();
+    float m0 = acc0[0], m1 = acc1[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      m0 = fmaxf(m0, acc0[r]);
+      m1 = fmaxf(m1, acc1[r]);
+    }
+    if (__ballot(m0 >= tau[0] || m1 >= tau[1]) == 0ull) return;
+    if (!dirty) positions();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // one row tile adds at most 16 x 64 = kFsStage entries
+      u64 bal[16];
+      int tot = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bal[r] = __ballot((u ? acc1[r] : acc0[r]) >= tau[u]);
+        tot += __popcll(bal[r]);
+      }
+      if (tot == 0) continue;
+      if (cnt + tot > kFsStage) {
+        flush(cnt);
+        cnt = 0;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (bal[r] == 0ull) continue;
+        const float v = u ? acc1[r] : acc0[r];
+        if (v >= tau[u]) {
+          const int e = cnt + (int)mbcnt64(bal[r]);
+          skey[w][e] = rank_key(v, js[r]);
+          srl[w][e] = (uint8_t)(32 * u + l32);
+        }
+        cnt += __popcll(bal[r]);
+      }
+    }
+  };
+
+  // kFsDepth tiles in flight: tile i is scored while the loads of tiles
+  // i + 1 .. i + kFsDepth - 1 are outstanding; right after tile i's MFMAs
+  // are issued its registers take tile i + kFsDepth's loads
+  // Every load is unconditional (tiles past the range read its last key and
+  // are masked), so the number of loads issued after any of them is fixed and
+  // each wait covers only its own tile; a tile's position register is
+  // reloaded only after its scores are filtered.
+  if (ntile > 0) {
+    v8s A[kFsDepth][KS];
+    int jt[kFsDepth];
+#pragma unroll
+    for (int d = 0; d < kFsDepth; ++d) {
+      load_tile(d, A[d]);
+      jt[d] = permb[tile_key(d)];
+    }
+    const int64_t ngrp = (ntile + kFsDepth - 1) / kFsDepth;
+    for (int64_t g = 0; g < ngrp; ++g) {
+#pragma unroll
+      for (int d = 0; d < kFsDepth; ++d) {
+        const int64_t i = g * kFsDepth + d;
+        v16f c0, c1;
+        mfma_tile(A[d], c0, c1);
+        load_tile(i + kFsDepth, A[d]);
+        epilogue(c0, c1, jt[d], i);
+        jt[d] = permb[tile_key(i + kFsDepth)];
+      }
+    }
   }
   if (cnt > 0) flush(cnt);
 }
@@ -1479,12 +1463,9 @@ FsPlan plan_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, int3
   while (capl < 2 * p.k) capl <<= 1;
   pl.merge_m = capl / kPfMergeBlock;
   pl.rb = (int)((TG + kFsRows - 1) / kFsRows);
-  // enough workgroups for two per CU, each with at least 64 key stages
-  const int64_t want = (512 + (int64_t)d.n_kv_heads * pl.rb - 1) / ((int64_t)d.n_kv_heads * pl.rb);
-  const int64_t most = N / (64 * kFsKT) > 1 ? N / (64 * kFsKT) : 1;
-  int64_t S = want < most ? want : most;
-  S = S < 1 ? 1 : S;
-  pl.keys = ((N + S - 1) / S + kFsKT - 1) / kFsKT * kFsKT;
+  // key splits of 16384 keys (2 MiB of bf16 latent): the workgroups of one
+  // split are dispatched together and share its keys through L2
+  pl.keys = kFsSplitKeys;
   pl.split = (int)((N + pl.keys - 1) / pl.keys);
   pl.bytes = carve_flat_tiled(d, pl, R, nullptr, nullptr);
   pl.ok = true;
