@@ -35,12 +35,15 @@
 //                       full from its leaf list
 #include <limits.h>
 
+#include <type_traits>
+
 #include "select_device.h"
 
 namespace lsa {
 
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -768,7 +771,7 @@ constexpr int kFsRows = (kFsBlock / 64) * kFsWaveRows;     // rows per workgroup
 constexpr int kFsStage = 1024;                             // staged appends per wave (16 x 64)
 constexpr int kFsSampleR = 32;                             // order statistic kept per lane
 constexpr int64_t kFsSplitKeys = 16384;                     // keys per split of the scan
-constexpr int kFsDepth = 4;                                // key tiles in flight per wave
+constexpr int kFsDepth = 2;                                // key tiles in flight per wave
 
 // In-order LDS traffic of one wave, kept in program order by the compiler.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -867,24 +870,28 @@ __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
 }
 
 // The scan.  A workgroup takes 256 rows of one KV head (64 per wave, as two
-// 32-row B operands held in registers) and one range of keys.  Every wave
-// streams the range's 32-key tiles straight into its A operand (the four
-// waves read the same keys, so all but the first read hit the caches) with no
-// workgroup barrier: the next tile's loads and the current tile's MFMAs are
-// issued before the previous tile's scores are filtered, so loads, matrix
-// cores and the filter overlap.  A tile whose keys all lie in every row's
-// candidate range (one ballot) skips the per-key range test.  Scores at or
-// above the row's threshold are staged in LDS per wave and flushed to the
-// rows' append lists with one global atomic per row and flush.
+// 32-row B operands held in registers) and one split of keys.  Every wave
+// streams the split's 32-key tiles on its own, with no workgroup barrier (the
+// four waves read the same keys, so all but the first read hit the caches):
+// a tile is loaded coalesced two tiles ahead, passed through the wave's LDS
+// tile to become the MFMA operand, and scored while the next tile's loads
+// are in flight.  A tile whose keys all lie in every row's candidate range
+// (one ballot) skips the per-key range test.  Scores at or above the row's
+// threshold are staged in LDS per wave and flushed to the rows' append lists
+// with one global atomic per row and flush.
 template <int DL>
 __global__ __launch_bounds__(kFsBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void fs_scan_kernel(PfArgs a) {
   constexpr int KS = DL / 16;
   constexpr int NW = kFsBlock / 64;
   constexpr int SE = kFsStage / 64;
+  constexpr int TB = 32 * DL * 2;                  // bytes of a 32-key tile
+  constexpr int RP = DL * 2 / 16;                  // 16-byte parts per key row
+  constexpr int PL = TB / 16 / 64;                 // 16-byte parts per lane and tile
   __shared__ u64 skey[NW][kFsStage];
   __shared__ uint8_t srl[NW][kFsStage];
   __shared__ uint32_t scnt[NW][64];
   __shared__ int srid[NW][64];
+  __shared__ __align__(16) unsigned char ktile[NW][2][TB];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   // workgroup -> (KV head, key split, row block); with the KV heads a
@@ -945,10 +952,32 @@ __global__ __launch_bounds__(kFsBlock) __attribute__((amdgpu_waves_per_eu(2, 2))
   // position), so the loads are unconditional and nothing here uses the
   // loaded values: they stay in flight until the tile is scored.
   auto tile_key = [&](int64_t i) { return min(k0 + i * 32 + l32, k1 - 1); };
-  auto load_tile = [&](int64_t i, v8s* A) {
-    const int64_t key = tile_key(i);
+  // A tile is loaded coalesced (eight lanes per 128-byte key row), written to
+  // the wave's LDS tile with the 16-byte parts of row r XOR-swizzled by r % 8,
+  // and read back as the MFMA operand (lane l32 takes key l32's parts) with
+  // no bank conflicts: an operand load straight from global memory would
+  // touch 32 cache lines per instruction.
+  auto load_tile = [&](int64_t i, u32x4* P) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = as_v8s(*(const uint4*)(latb + (size_t)key * DL + 16 * s + 8 * half));
+    for (int q = 0; q < PL; ++q) {
+      const int c = lane + 64 * q;                 // part c: row c / RP, part c % RP
+      const int64_t key = min(k0 + i * 32 + c / RP, k1 - 1);
+      P[q] = *(const u32x4*)(latb + (size_t)key * DL + (c % RP) * 8);
+    }
+  };
+  auto put_tile = [&](const u32x4* P, int buf) {
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int c = lane + 64 * q, r = c / RP, pt = c % RP;
+      *(u32x4*)(&ktile[w][buf][r * RP * 16 + ((pt ^ (r & 7)) % RP) * 16]) = P[q];
+    }
+  };
+  auto get_tile = [&](int buf, v8s* A) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int pt = 2 * s + half;
+      A[s] = as_v8s(*(const uint4*)(&ktile[w][buf][l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16]));
+    }
   };
   auto mfma_tile = [&](const v8s* A, v16f& c0, v16f& c1) {
 #pragma unroll
@@ -1055,27 +1084,42 @@ __global__ __launch_bounds__(kFsBlock) __attribute__((amdgpu_waves_per_eu(2, 2))
   // are issued its registers take tile i + kFsDepth's loads
   // Every load is unconditional (tiles past the range read its last key and
   // are masked), so the number of loads issued after any of them is fixed and
-  // each wait covers only its own tile; a tile's position register is
-  // reloaded only after its scores are filtered.
+  // each wait covers only its own tile; a tile's registers are reloaded only
+  // after they have been written to LDS, its position after its scores are
+  // filtered.  Tile i + 1 goes to LDS before tile i is filtered.
   if (ntile > 0) {
-    v8s A[kFsDepth][KS];
+    u32x4 P[kFsDepth][PL];
     int jt[kFsDepth];
 #pragma unroll
     for (int d = 0; d < kFsDepth; ++d) {
-      load_tile(d, A[d]);
+      load_tile(d, P[d]);
       jt[d] = permb[tile_key(d)];
     }
+    put_tile(P[0], 0);
+    load_tile(kFsDepth, P[0]);
+    // one tile step, with its ring slot d a compile-time constant
+    auto step = [&](int64_t g, auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      constexpr int dn = (d + 1) % kFsDepth;
+      const int64_t i = g * kFsDepth + d;
+      // a wave's LDS accesses execute in order; these only keep the
+      // compiler from moving them across each other
+      __builtin_amdgcn_wave_barrier();
+      v8s A[KS];
+      get_tile((int)(i & 1), A);
+      v16f c0, c1;
+      mfma_tile(A, c0, c1);
+      __builtin_amdgcn_wave_barrier();
+      put_tile(P[dn], (int)((i + 1) & 1));
+      load_tile(i + 1 + kFsDepth, P[dn]);
+      epilogue(c0, c1, jt[d], i);
+      jt[d] = permb[tile_key(i + kFsDepth)];
+    };
+    static_assert(kFsDepth == 2, "the step calls below");
     const int64_t ngrp = (ntile + kFsDepth - 1) / kFsDepth;
     for (int64_t g = 0; g < ngrp; ++g) {
-#pragma unroll
-      for (int d = 0; d < kFsDepth; ++d) {
-        const int64_t i = g * kFsDepth + d;
-        v16f c0, c1;
-        mfma_tile(A[d], c0, c1);
-        load_tile(i + kFsDepth, A[d]);
-        epilogue(c0, c1, jt[d], i);
-        jt[d] = permb[tile_key(i + kFsDepth)];
-      }
+      step(g, std::integral_constant<int, 0>{});
+      step(g, std::integral_constant<int, 1>{});
     }
   }
   if (cnt > 0) flush(cnt);
