@@ -385,6 +385,9 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
 template <int DL, bool SAMPLE>
 __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
   constexpr int KS = DL / 16;
+  constexpr int RP = DL * 2 / 16;                  // 16-byte parts per key row
+  constexpr int PL = 32 * RP / 64;                 // 16-byte parts per lane and 32-key tile
+  __shared__ __align__(16) unsigned char ktile[kPfNW][32 * DL * 2];
   __shared__ uint32_t tpre[kPfMaxF + 1];
   __shared__ uint32_t lst[kPfMaxF], lcn[kPfMaxF];
   __shared__ int o0s[kPfMaxF], o1s[kPfMaxF];
@@ -458,29 +461,56 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
     const int o0 = o0s[c], o1 = o1s[c];
     // key tile kt: A operand (key l32's dims) and the key's index (INT_MAX
     // for a missing key or one inside the sink)
-    auto load_keys = [&](int kt, v8s* A, int* jl) {
-      const int krow = o0 + 32 * kt + l32;
-      const bool kv = krow < o1;
+    // A key tile is loaded coalesced (eight lanes per 128-byte key row; a
+    // lane past the leaf reads its last key, masked by position below),
+    // written to the wave's LDS tile with the 16-byte parts of row r
+    // XOR-swizzled by r % 8, and read back as the MFMA operand (lane l32
+    // takes key l32's parts) with no bank conflicts.  The wave's LDS
+    // accesses execute in order, so one tile buffer serves every tile.
+    unsigned char* kl = ktile[w];
+    auto load_parts = [&](int kt, u32x4* P) {
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const int c = lane + 64 * q;
+        const int krow = min(o0 + 32 * kt + c / RP, o1 - 1);
+        P[q] = *(const u32x4*)(latb + (size_t)krow * DL + (c % RP) * 8);
+      }
+    };
+    auto put_parts = [&](const u32x4* P) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const int c = lane + 64 * q, r = c / RP, pt = c % RP;
+        *(u32x4*)(kl + r * RP * 16 + ((pt ^ (r & 7)) % RP) * 16) = P[q];
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    auto get_a = [&](v8s* A) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
-        if (kv) u = *(const uint4*)(latb + (size_t)krow * DL + 16 * s + 8 * half);
-        A[s] = as_v8s(u);
+        const int pt = 2 * s + half;
+        A[s] = as_v8s(*(const uint4*)(kl + l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16));
       }
-      const int j = kv ? permb[krow] : INT_MAX;
-      *jl = j >= sink ? j : INT_MAX;
     };
+    // key l32's position, raw (read early) and as a candidate test value:
+    // INT_MAX for a missing key or one inside the sink
+    auto pos_raw = [&](int kt) { return permb[min(o0 + 32 * kt + l32, o1 - 1)]; };
+    auto pos_of = [&](int kt, int jraw) { return (o0 + 32 * kt + l32 < o1 && jraw >= sink) ? jraw : INT_MAX; };
     // results: lane holds row l32 against keys m = 8(r/4) + 4 half + r%4
     if (SAMPLE) {
       if (o1 <= o0) continue;
+      u32x4 P[PL];
+      load_parts(0, P);
+      const int jr = pos_raw(0);
+      put_parts(P);
       v8s A[KS];
-      int jl;
-      load_keys(0, A, &jl);
+      get_a(A);
       v16f acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+      const int jl = pos_of(0, jr);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * half + (r & 3);
@@ -501,20 +531,27 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
     uint32_t pos = 0u;
     for (int pass = 0; pass < 2; ++pass) {
       int cnt = 0;
-      v8s A[KS], An[KS];
-      int jl = INT_MAX, jn = INT_MAX;
-      if (nkt > 0) load_keys(0, A, &jl);
+      u32x4 P[PL];
+      int jr = 0, jrn = 0;
+      if (nkt > 0) {
+        load_parts(0, P);
+        jr = pos_raw(0);
+      }
       for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) load_keys(kt + 1, An, &jn);
+        put_parts(P);
+        if (kt + 1 < nkt) {
+          load_parts(kt + 1, P);
+          jrn = pos_raw(kt + 1);
+        }
+        v8s A[KS];
+        get_a(A);
         v16f acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
-        int jmax = jl;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) jmax = max(jmax, __shfl_xor(jmax, o, 64));
-        if (pass == 0 && jmax <= chimin) {
+        const int jl = pos_of(kt, jr);
+        if (pass == 0 && __ballot(jl > chimin) == 0ull) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) cnt += acc[r] >= tau ? 1 : 0;
         } else {
@@ -531,9 +568,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
             }
           }
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) A[s] = An[s];
-        jl = jn;
+        jr = jrn;
       }
       if (pass == 0) {
         // one atomic per row reserves the places of both halves' keys
