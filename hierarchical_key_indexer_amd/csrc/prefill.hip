@@ -857,18 +857,14 @@ __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
   const int* permb = a.s.perm + (size_t)h * a.s.N;
   const int64_t N = a.s.N, ns = a.ns;
   // sample tile: key l32 of the tile is sample tile * 32 + l32
+  // (a lane past the last sample reads the last one and is masked where its
+  // position is tested; nothing here uses the loaded values, so the next
+  // tile's loads stay in flight while this one is scored)
   auto load = [&](int64_t tile, v8s* A, int* jl) {
-    const int64_t j = tile * 32 + l32;
-    const bool ok = j < ns;
-    const int64_t key = ok ? j * N / ns : 0;
+    const int64_t key = min(tile * 32 + l32, ns - 1) * N / ns;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) u = *(const uint4*)(latb + (size_t)key * DL + 16 * s + 8 * half);
-      A[s] = as_v8s(u);
-    }
-    const int pos = ok ? permb[key] : INT_MAX;
-    *jl = pos >= a.s.sink ? pos : INT_MAX;
+    for (int s = 0; s < KS; ++s) A[s] = as_v8s(*(const uint4*)(latb + (size_t)key * DL + 16 * s + 8 * half));
+    *jl = permb[key];
   };
   float t[kFsSampleR];
 #pragma unroll
@@ -884,10 +880,11 @@ __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+    const int jc = (tile * 32 + l32 < ns && jl >= a.s.sink) ? jl : INT_MAX;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-      const int jm = __shfl(jl, m, 64);
+      const int jm = __shfl(jc, m, 64);
       const float v = jm <= chi ? acc[r] : -__builtin_huge_valf();
       if (__ballot(v > t[kFsSampleR - 1]) != 0ull) {
 #pragma unroll
