@@ -388,8 +388,16 @@ __device__ u64* sort_by_index(u64* buf, u64* out, int n, int cap, SortScratch* s
     lo = sc->wmin[i] < lo ? sc->wmin[i] : lo;
     hi = sc->wmax[i] > hi ? sc->wmax[i] : hi;
   }
-  const uint64_t ilo = lo >> 32, span = (hi >> 32) - ilo + 1;
-  auto bucket = [&](u64 key) { return (int)((((key >> 32) - ilo) * (uint64_t)NB) / span); };
+  // bucket = floor((index - lo) * NB / span) without a 64-bit division: a
+  // 32-bit multiply-high by floor(NB * 2^32 / span), which is monotone and
+  // stays below NB; a span of at most NB buckets takes one index per bucket
+  const uint32_t ilo = (uint32_t)(lo >> 32);
+  const uint64_t span = (uint64_t)((uint32_t)(hi >> 32) - ilo) + 1;
+  const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
+  auto bucket = [&](u64 key) {
+    const uint32_t d = (uint32_t)(key >> 32) - ilo;
+    return scale == 0u ? (int)d : (int)__umulhi(d, scale);
+  };
   for (int i = threadIdx.x; i < n; i += BLOCK) atomicAdd(&sc->cnt[bucket(buf[i])], 1u);
   __syncthreads();
   constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
