@@ -55,6 +55,7 @@ constexpr int kPfMaxB = 16;
 constexpr int kPfMaxF = 64;
 constexpr float kPfTarget = 1.5f;    // expected appended keys per row, in units of k
 constexpr int kPfSampleR = 200;      // samples expected above the threshold
+constexpr int kPfStage = 512;        // staged appends per wave in the gather
 
 struct PfArgs {
   SelArgs s;                   // index, queries, outputs; s.qlat fp32 latents; s.part_keys / part_n appends
@@ -131,6 +132,12 @@ __device__ __forceinline__ uint32_t* pf_count_of(const PfArgs& a, int64_t row) {
 }
 
 __device__ __forceinline__ v8s as_v8s(const uint4& u) { return __builtin_bit_cast(v8s, u); }
+
+// In-order LDS traffic of one wave, kept in program order by the compiler.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 __device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
@@ -383,11 +390,19 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
 // item reserves their places), once to write them.  Sample mode scores the
 // first key tile and keeps the first spl scores of every row.
 template <int DL, bool SAMPLE>
-__global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
+__global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) void pf_gather(PfArgs a) {
   constexpr int KS = DL / 16;
   constexpr int RP = DL * 2 / 16;                  // 16-byte parts per key row
   constexpr int PL = 32 * RP / 64;                 // 16-byte parts per lane and 32-key tile
+  // main mode: keys at or above a row's threshold are staged per wave (rank
+  // key and the row's lane, 0..31) and flushed at the end of every item
+  constexpr int SST = SAMPLE ? 64 : kPfStage;
+  constexpr int SE = SST / 64;
   __shared__ __align__(16) unsigned char ktile[kPfNW][32 * DL * 2];
+  __shared__ u64 skey[kPfNW][SST];
+  __shared__ uint8_t srl[kPfNW][SST];
+  __shared__ uint32_t scnt[kPfNW][32];
+  __shared__ int srow[kPfNW][32];
   __shared__ uint32_t tpre[kPfMaxF + 1];
   __shared__ uint32_t lst[kPfMaxF], lcn[kPfMaxF];
   __shared__ int o0s[kPfMaxF], o1s[kPfMaxF];
@@ -524,63 +539,107 @@ __global__ __launch_bounds__(kPfBlock) void pf_gather(PfArgs a) {
     }
     const int nkt = (o1 - o0 + 31) / 32;
     // the smallest causal limit of the item's rows: a tile whose keys all
-    // lie in [sink, that limit] needs no per-key range test when counting
+    // lie in [sink, that limit] needs no per-key range test
     int chimin = row >= 0 ? chi : INT_MAX;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) chimin = min(chimin, __shfl_xor(chimin, o, 64));
-    uint32_t pos = 0u;
-    for (int pass = 0; pass < 2; ++pass) {
-      int cnt = 0;
-      u32x4 P[PL];
-      int jr = 0, jrn = 0;
-      if (nkt > 0) {
-        load_parts(0, P);
-        jr = pos_raw(0);
+    if (half == 0) srow[w][l32] = row;
+    int cnt = 0;                                   // staged entries (wave-uniform)
+    // staged entries -> the rows' append lists: per-row counts in LDS, one
+    // global atomic per row reserves their places
+    auto flush = [&]() {
+      if (half == 0) scnt[w][l32] = 0u;
+      wave_lds_sync();
+      uint32_t lp[SE];
+#pragma unroll
+      for (int q = 0; q < SE; ++q) {
+        const int e = lane + 64 * q;
+        lp[q] = e < cnt ? atomicAdd(&scnt[w][srl[w][e]], 1u) : 0u;
       }
-      for (int kt = 0; kt < nkt; ++kt) {
-        put_parts(P);
-        if (kt + 1 < nkt) {
-          load_parts(kt + 1, P);
-          jrn = pos_raw(kt + 1);
+      wave_lds_sync();
+      if (half == 0) {
+        const uint32_t c = scnt[w][l32];
+        scnt[w][l32] = c != 0u ? atomicAdd(pf_count_of(a, row), c) : 0u;
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int q = 0; q < SE; ++q) {
+        const int e = lane + 64 * q;
+        if (e < cnt) {
+          const int rl = srl[w][e];
+          const uint32_t pos = scnt[w][rl] + lp[q];
+          if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)srow[w][rl] * a.cap + pos] = skey[w][e];
         }
-        v8s A[KS];
-        get_a(A);
-        v16f acc;
+      }
+      wave_lds_sync();
+      cnt = 0;
+    };
+    u32x4 P[PL];
+    int jr = 0, jrn = 0;
+    if (nkt > 0) {
+      load_parts(0, P);
+      jr = pos_raw(0);
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+      put_parts(P);
+      if (kt + 1 < nkt) {
+        load_parts(kt + 1, P);
+        jrn = pos_raw(kt + 1);
+      }
+      v8s A[KS];
+      get_a(A);
+      v16f acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
-        const int jl = pos_of(kt, jr);
-        if (pass == 0 && __ballot(jl > chimin) == 0ull) {
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+      const int jl = pos_of(kt, jr);
+      jr = jrn;
+      int js[16];
+      auto positions = [&]() {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) cnt += acc[r] >= tau ? 1 : 0;
-        } else {
+        for (int r = 0; r < 16; ++r) js[r] = __shfl(jl, 8 * (r >> 2) + 4 * half + (r & 3), 64);
+      };
+      const bool dirty = __ballot(jl > chimin) != 0ull;
+      if (dirty) {
+        // a key outside some row's range: its scores become NaN, which no
+        // comparison passes and fmaxf ignores
+        positions();
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-            const int jm = __shfl(jl, m, 64);
-            const bool ok = jm <= chi && acc[r] >= tau;
-            if (pass == 0) {
-              cnt += ok ? 1 : 0;
-            } else if (ok) {
-              if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)row * a.cap + pos] = rank_key(acc[r], jm);
-              ++pos;
-            }
+        for (int r = 0; r < 16; ++r)
+          if (js[r] > chi) acc[r] = __builtin_nanf("");
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+      if (__ballot(mx >= tau) == 0ull) continue;
+      if (!dirty) positions();
+      // eight registers add at most 8 x 64 = kPfStage entries
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        u64 bal[8];
+        int tot = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          bal[r] = __ballot(acc[8 * hb + r] >= tau);
+          tot += __popcll(bal[r]);
+        }
+        if (tot == 0) continue;
+        if (cnt + tot > SST) flush();
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if (bal[r] == 0ull) continue;
+          const float v = acc[8 * hb + r];
+          if (v >= tau) {
+            const int e = cnt + (int)mbcnt64(bal[r]);
+            skey[w][e] = rank_key(v, js[8 * hb + r]);
+            srl[w][e] = (uint8_t)l32;
           }
+          cnt += __popcll(bal[r]);
         }
-        jr = jrn;
-      }
-      if (pass == 0) {
-        // one atomic per row reserves the places of both halves' keys
-        const int lo_cnt = __shfl(cnt, l32, 64);            // half 0's count of this row
-        const int tot = lo_cnt + __shfl(cnt, l32 + 32, 64);
-        uint32_t base = 0u;
-        if (half == 0 && row >= 0 && tot > 0) base = atomicAdd(pf_count_of(a, row), (uint32_t)tot);
-        base = (uint32_t)__shfl((int)base, l32, 64);
-        pos = base + (half ? (uint32_t)lo_cnt : 0u);
-        if (__ballot(tot > 0) == 0ull) break;
       }
     }
+    if (cnt > 0) flush();
   }
 }
 
@@ -807,12 +866,6 @@ constexpr int kFsStage = 1024;                             // staged appends per
 constexpr int kFsSampleR = 32;                             // order statistic kept per lane
 constexpr int64_t kFsSplitKeys = 16384;                     // keys per split of the scan
 constexpr int kFsDepth = 2;                                // key tiles in flight per wave
-
-// In-order LDS traffic of one wave, kept in program order by the compiler.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
 
 // Rows of a KV head in scan order: i = token * G + group member.
 __device__ __forceinline__ int fs_row(const PfArgs& a, int h, int64_t i) {
