@@ -80,7 +80,8 @@ struct PfArgs {
   int nl;                      // leaf slots per row, prod of the be
   // gather
   int spl;                     // samples per (row, leaf)
-  uint16_t* smp;               // [R][nl][spl] top 16 bits of order(score), 0 = not a candidate
+  int spl4;                    // spl rounded up to a multiple of 4 (the stride of smp)
+  uint16_t* smp;               // [R][nl][spl4] top 16 bits of order(score), 0 = not a candidate
   float* tauf;                 // [R] score threshold, -inf = none
   int64_t cap;                 // append capacity per row
   // row-tiled full scan
@@ -526,14 +527,19 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
       const int jl = pos_of(0, jr);
+      // registers 4g..4g+3 hold samples m0..m0+3 (m0 = 8g + 4 half): one
+      // 8-byte store per group, zero past spl or for a non-candidate
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-        const int jm = __shfl(jl, m, 64);
-        if (m < a.spl && row >= 0) {
-          const uint16_t v = jm <= chi ? (uint16_t)(order_u32(acc[r]) >> 16) : (uint16_t)0;
-          a.smp[((size_t)row * a.nl + slot) * a.spl + m] = v;
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 8 * g + 4 * half;
+        u64 pk = 0ull;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int jm = __shfl(jl, m0 + c, 64);
+          const u64 v = (m0 + c < a.spl && jm <= chi) ? (u64)(order_u32(acc[4 * g + c]) >> 16) : 0ull;
+          pk |= v << (16 * c);
         }
+        if (m0 < a.spl && row >= 0) *(u64*)(a.smp + ((size_t)row * a.nl + slot) * a.spl4 + m0) = pk;
       }
       continue;
     }
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   }
   const int* offL = a.s.off[lev] + (size_t)h * (Pe + 1);
   const int32_t* lfr = a.lf + (size_t)(live ? row : 0) * a.nl;
-  const uint16_t* sm = a.smp + (size_t)(live ? row : 0) * a.nl * a.spl;
+  const uint16_t* sm = a.smp + (size_t)(live ? row : 0) * a.nl * a.spl4;
   int64_t tot = 0;
   if (live)
     for (int sl = lane; sl < a.nl; sl += 64) {
@@ -728,7 +734,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
         if (se == 0) continue;
         const u64 wt = ((u64)sz << 4) / (u64)se;
         for (int q = 0; q < se; ++q) {
-          const uint32_t v = sm[(size_t)sl * a.spl + q];
+          const uint32_t v = sm[(size_t)sl * a.spl4 + q];
           if (v == 0u) continue;
           if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
           else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
@@ -1250,7 +1256,7 @@ size_t carve_prefill(const lsa_index_desc& d, const PfPlan& pl, int64_t R, void*
   }
   w.mask = c.take<u64>((size_t)(R * pl.nl[d.n_levels - 1]));
   w.lf = c.take<int32_t>((size_t)(R * pl.nl[d.n_levels]));
-  w.smp = c.take<uint16_t>((size_t)(R * pl.nl[d.n_levels] * pl.spl));
+  w.smp = c.take<uint16_t>((size_t)(R * pl.nl[d.n_levels] * ((pl.spl + 3) / 4 * 4)));
   w.tauf = c.take<float>((size_t)R);
   w.part_keys = c.take<u64>((size_t)(R * pl.cap));
   w.part_n = c.take<uint32_t>((size_t)R);
@@ -1326,6 +1332,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
   a.lf = w.lf;
   a.nl = pl.nl[d.n_levels];
   a.spl = pl.spl;
+  a.spl4 = (pl.spl + 3) / 4 * 4;
   a.smp = w.smp;
   a.tauf = w.tauf;
   a.cap = pl.cap;
