@@ -467,13 +467,6 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       chi = (p >= 0 && (int64_t)p < a.s.N) ? p - a.s.window : -1;
       if (!SAMPLE) tau = a.tauf[row];
     }
-    v8s Bq[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
-      Bq[s] = as_v8s(u);
-    }
     const int o0 = o0s[c], o1 = o1s[c];
     // key tile kt: A operand (key l32's dims) and the key's index (INT_MAX
     // for a missing key or one inside the sink)
@@ -508,6 +501,29 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
         A[s] = as_v8s(*(const uint4*)(kl + l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16));
       }
     };
+    // the rows' latents (the B operand, a missing row as zeros).  The sample
+    // pass scores one key tile per item, so its row load matters as much as
+    // the key load: it comes coalesced through the LDS tile as well.  The
+    // main pass loads it straight, once per item.
+    v8s Bq[KS];
+    if constexpr (SAMPLE) {
+      u32x4 P[PL];
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const int cq = lane + 64 * q;
+        const int rr = __shfl(row, cq / RP, 64);
+        P[q] = rr >= 0 ? *(const u32x4*)(a.qlat16 + (size_t)rr * DL + (cq % RP) * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+      put_parts(P);
+      get_a(Bq);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+        Bq[s] = as_v8s(u);
+      }
+    }
     // key l32's position, raw (read early) and as a candidate test value:
     // INT_MAX for a missing key or one inside the sink
     auto pos_raw = [&](int kt) { return permb[min(o0 + 32 * kt + l32, o1 - 1)]; };
