@@ -349,115 +349,91 @@ __device__ void bitonic_sort_asc(u64* buf, int n, int cap) {
   }
 }
 
+// Write one output row from the n (<= k) rank keys in buf: sink positions,
+// the keys in ascending index order with their scores, the window positions.
+// buf[0..cap) is sort space; n <= cap / 2.  Every key's index lies in [0, p],
+// so the keys are bucketed by index over that span (1024 buckets; a bucket
+// index is a 32-bit multiply-high, monotone in the index), scattered to
+// buf[cap/2..) in bucket order and insertion-sorted inside every bucket.  A
+// bucket of more than 64 keys (a very uneven index spread) sends the whole
+// set to the bitonic sort instead.
 // LDS scratch of the bucket sort by key index.
 constexpr int kSortBuckets = 1024;
 struct SortScratch {
   uint32_t cnt[kSortBuckets];
   int wsum[16];
-  u64 wmin[16], wmax[16];
   int big;
 };
 
-// Sort the n unique keys buf[0..n) (index in the high 32 bits) ascending
-// into out[0..n): bucket by index over [min, max] (histogram, scan,
-// scatter), then an insertion sort inside every bucket.  A bucket of more
-// than 64 keys (a very uneven index spread) sends the whole set to the
-// bitonic sort instead.  Returns the array holding the sorted keys.
-template <int BLOCK>
-__device__ u64* sort_by_index(u64* buf, u64* out, int n, int cap, SortScratch* sc) {
-  constexpr int NW = BLOCK / 64;
-  constexpr int NB = kSortBuckets;
-  u64 lo = ~0ull, hi = 0ull;
-  for (int i = threadIdx.x; i < n; i += BLOCK) {
-    lo = buf[i] < lo ? buf[i] : lo;
-    hi = buf[i] > hi ? buf[i] : hi;
-  }
-  lo = wave_min_u64(lo);
-  hi = wave_max_u64(hi);
-  if ((threadIdx.x & 63) == 0) {
-    sc->wmin[threadIdx.x >> 6] = lo;
-    sc->wmax[threadIdx.x >> 6] = hi;
-  }
-  for (int b = threadIdx.x; b < NB; b += BLOCK) sc->cnt[b] = 0u;
-  if (threadIdx.x == 0) sc->big = 0;
-  __syncthreads();
-  lo = sc->wmin[0];
-  hi = sc->wmax[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) {
-    lo = sc->wmin[i] < lo ? sc->wmin[i] : lo;
-    hi = sc->wmax[i] > hi ? sc->wmax[i] : hi;
-  }
-  // bucket = floor((index - lo) * NB / span) without a 64-bit division: a
-  // 32-bit multiply-high by floor(NB * 2^32 / span), which is monotone and
-  // stays below NB; a span of at most NB buckets takes one index per bucket
-  const uint32_t ilo = (uint32_t)(lo >> 32);
-  const uint64_t span = (uint64_t)((uint32_t)(hi >> 32) - ilo) + 1;
-  const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
-  auto bucket = [&](u64 key) {
-    const uint32_t d = (uint32_t)(key >> 32) - ilo;
-    return scale == 0u ? (int)d : (int)__umulhi(d, scale);
-  };
-  for (int i = threadIdx.x; i < n; i += BLOCK) atomicAdd(&sc->cnt[bucket(buf[i])], 1u);
-  __syncthreads();
-  constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
-  int mine = 0, mx = 0;
-  if ((int)threadIdx.x * PER < NB)
-    for (int j = 0; j < PER; ++j) {
-      const int c = (int)sc->cnt[threadIdx.x * PER + j];
-      mine += c;
-      mx = c > mx ? c : mx;
-    }
-  if (mx > 64) sc->big = 1;
-  int total;
-  int run = block_exclusive_scan<BLOCK>(mine, sc->wsum, &total);
-  if ((int)threadIdx.x * PER < NB)
-    for (int j = 0; j < PER; ++j) {
-      const int c = (int)sc->cnt[threadIdx.x * PER + j];
-      sc->cnt[threadIdx.x * PER + j] = (uint32_t)run;
-      run += c;
-    }
-  __syncthreads();
-  if (sc->big) {
-    bitonic_sort_asc<BLOCK>(buf, n, cap);
-    return buf;
-  }
-  for (int i = threadIdx.x; i < n; i += BLOCK) {
-    const u64 key = buf[i];
-    out[atomicAdd(&sc->cnt[bucket(key)], 1u)] = key;
-  }
-  __syncthreads();
-  // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
-  for (int b = threadIdx.x; b < NB; b += BLOCK) {
-    const int e = (int)sc->cnt[b], st = b == 0 ? 0 : (int)sc->cnt[b - 1];
-    for (int i = st + 1; i < e; ++i) {
-      const u64 x = out[i];
-      int j = i - 1;
-      while (j >= st && out[j] > x) {
-        out[j + 1] = out[j];
-        --j;
-      }
-      out[j + 1] = x;
-    }
-  }
-  __syncthreads();
-  return out;
-}
-
-// Write one output row from the n (<= k) rank keys in buf: sink positions,
-// the keys in ascending index order with their scores, the window positions.
-// buf[0..cap) is sort space; n <= cap / 2.
 template <int BLOCK>
 __device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
                                     int32_t* row, float* scores_row) {
+  constexpr int NB = kSortBuckets;
   __shared__ SortScratch ss;
-  // re-key as (index << 32 | order(score)) so an ascending sort orders by index
+  const uint64_t span = (uint64_t)(p > 0 ? p : 0) + 1;
+  const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
+  auto bucket = [&](u64 key) {      // clamped, so an index past p still stays in range
+    const uint32_t d = (uint32_t)(key >> 32);
+    return (int)min(scale == 0u ? d : __umulhi(d, scale), (uint32_t)(NB - 1));
+  };
+  for (int b = threadIdx.x; b < NB; b += BLOCK) ss.cnt[b] = 0u;
+  if (threadIdx.x == 0) ss.big = 0;
+  __syncthreads();
+  // re-key as (index << 32 | order(score)) so an ascending sort orders by
+  // index, and count the buckets
   for (int i = threadIdx.x; i < n; i += BLOCK) {
     const u64 key = buf[i];
-    buf[i] = ((u64)(uint32_t)rank_key_index(key) << 32) | (key >> 32);
+    const u64 rk = ((u64)(uint32_t)rank_key_index(key) << 32) | (key >> 32);
+    buf[i] = rk;
+    atomicAdd(&ss.cnt[bucket(rk)], 1u);
   }
   __syncthreads();
-  u64* sorted = n > 1 ? sort_by_index<BLOCK>(buf, buf + cap / 2, n, cap, &ss) : buf;
+  u64* sorted = buf;
+  if (n > 1) {
+    constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
+    int mine = 0, mx = 0;
+    if ((int)threadIdx.x * PER < NB)
+      for (int j = 0; j < PER; ++j) {
+        const int c = (int)ss.cnt[threadIdx.x * PER + j];
+        mine += c;
+        mx = c > mx ? c : mx;
+      }
+    if (mx > 64) ss.big = 1;
+    int total;
+    int run = block_exclusive_scan<BLOCK>(mine, ss.wsum, &total);
+    if ((int)threadIdx.x * PER < NB)
+      for (int j = 0; j < PER; ++j) {
+        const int c = (int)ss.cnt[threadIdx.x * PER + j];
+        ss.cnt[threadIdx.x * PER + j] = (uint32_t)run;
+        run += c;
+      }
+    __syncthreads();
+    if (ss.big) {
+      bitonic_sort_asc<BLOCK>(buf, n, cap);
+    } else {
+      u64* out = buf + cap / 2;
+      for (int i = threadIdx.x; i < n; i += BLOCK) {
+        const u64 key = buf[i];
+        out[atomicAdd(&ss.cnt[bucket(key)], 1u)] = key;
+      }
+      __syncthreads();
+      // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
+      for (int b = threadIdx.x; b < NB; b += BLOCK) {
+        const int e = (int)ss.cnt[b], st = b == 0 ? 0 : (int)ss.cnt[b - 1];
+        for (int i = st + 1; i < e; ++i) {
+          const u64 x = out[i];
+          int j = i - 1;
+          while (j >= st && out[j] > x) {
+            out[j + 1] = out[j];
+            --j;
+          }
+          out[j + 1] = x;
+        }
+      }
+      __syncthreads();
+      sorted = out;
+    }
+  }
   for (int i = threadIdx.x; i < k; i += BLOCK) {
     if (i < n) {
       const u64 key = sorted[i];
