@@ -121,6 +121,32 @@ def timed_steps(fn, steps, hip, stages, abi):
     return wall, out
 
 
+def graph_replay(step, steps, qheads):
+    """The same step captured once in a graph and replayed `steps` times (the
+    library only enqueues kernels, so a call is capturable)."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        return {"ms_per_step": ms, "query_heads_per_s": qheads / (ms * 1e-3)}
+    except Exception as e:  # reported, never fatal to the bench line
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def cpu_baseline(wl, keys, W, queries, pos):
     """The CPU oracle, untuned, on KV head 0 of the workload: its index build
     (reported, not in the value) and the selection of that head's G query
@@ -244,6 +270,7 @@ def main():
     # per-stage kernel time (events around each stage) in a second, shorter run
     stages = [_abi.STAGE_DESCEND, _abi.STAGE_GATHER, _abi.STAGE_MERGE] + ([_abi.STAGE_SAMPLE] if node_major else [])
     _, stage_ms = timed_steps(step, max(1, min(args.steps, 20)), hip, stages, _abi)
+    graph = graph_replay(step, args.steps, wl.n_tokens * wl.n_q_heads)
     gather_ms = stage_ms[_abi.STAGE_GATHER]
     qheads = wl.n_tokens * wl.n_q_heads
     tree_idx = out[0].cpu().numpy()
@@ -293,6 +320,7 @@ def main():
         "stages_ms": {name: stage_ms.get(st) for name, st in (("descend", _abi.STAGE_DESCEND),
                       ("sample", _abi.STAGE_SAMPLE), ("gather", _abi.STAGE_GATHER), ("merge", _abi.STAGE_MERGE))},
         "build_ms": build_ms,
+        "graph_replay": graph,
     }
     if centroid is not None:
         result["centroid_scoring"] = centroid
