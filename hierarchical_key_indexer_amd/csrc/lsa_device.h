@@ -367,9 +367,8 @@ struct SortScratch {
 
 template <int BLOCK>
 __device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
-                                    int32_t* row, float* scores_row) {
+                                    int32_t* row, float* scores_row, SortScratch& ss) {
   constexpr int NB = kSortBuckets;
-  __shared__ SortScratch ss;
   const uint64_t span = (uint64_t)(p > 0 ? p : 0) + 1;
   const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
   auto bucket = [&](u64 key) {      // clamped, so an index past p still stays in range
@@ -449,6 +448,14 @@ __device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, i
   const int w0 = max(sink, p - window + 1);
   const int nw = p - w0 + 1;
   for (int i = threadIdx.x; i < window; i += BLOCK) row[sink + k + i] = i < nw ? w0 + i : -1;
+}
+
+// The same, with the sort scratch in a static LDS block of its own.
+template <int BLOCK>
+__device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
+                                    int32_t* row, float* scores_row) {
+  __shared__ SortScratch ss;
+  write_selection_row<BLOCK>(buf, n, cap, p, sink, k, window, row, scores_row, ss);
 }
 
 // A row for a query whose position is outside [0, N): all -1.

@@ -777,8 +777,11 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   __shared__ RadixScratch rs;
   __shared__ int n_sh, wsum[NW];
   u64* buf = (u64*)smem;
+  // one LDS block serves the leaf lists of a re-score (used while streaming
+  // candidates) and then the index sort's scratch (used only afterwards)
   int* lpre = (int*)(buf + CAP);
   int* lrow = lpre + a.nl + 1;
+  SortScratch& sort_ss = *(SortScratch*)(buf + CAP);
   const int64_t row = blockIdx.x;
   const int t = (int)(row / a.s.Hq), h = (int)(row % a.s.Hq) / a.s.G;
   const int p = a.s.q_pos[t];
@@ -874,7 +877,8 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
     topk_compact<BLOCK, M>(buf, n, k, &rs);
     n = k;
   }
-  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, k, a.s.window, orow, srow);
+  __syncthreads();                                 // the lists are dead; the block becomes sort scratch
+  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, k, a.s.window, orow, srow, sort_ss);
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,7 +1296,8 @@ void launch_count_b(const PfArgs& a, int64_t grid, int be, hipStream_t st) {
 template <int DL, int M>
 void launch_pf_merge(const PfArgs& a, hipStream_t st) {
   auto mk = pf_merge_kernel<DL, M>;
-  const size_t lds = (size_t)M * kPfMergeBlock * 8 + ((size_t)a.nl * 2 + 2) * 4;
+  const size_t lists = ((size_t)a.nl * 2 + 2) * 4;
+  const size_t lds = (size_t)M * kPfMergeBlock * 8 + (lists > sizeof(SortScratch) ? lists : sizeof(SortScratch));
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)mk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(mk, dim3((unsigned)a.R), dim3(kPfMergeBlock), lds, st, a);
 }
