@@ -54,7 +54,7 @@ constexpr int kPfMinRows = 256;      // query heads per KV head for this path
 constexpr int kPfMaxB = 16;
 constexpr int kPfMaxF = 64;
 constexpr float kPfTarget = 1.5f;    // expected appended keys per row, in units of k
-constexpr int kPfSampleR = 200;      // samples expected above the threshold
+constexpr int kPfSampleR = 100;      // samples expected above the threshold
 constexpr int kPfStage = 512;        // staged appends per wave in the gather
 
 struct PfArgs {
