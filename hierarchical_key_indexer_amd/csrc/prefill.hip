@@ -442,27 +442,47 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
   const int sink = a.s.sink;
   const bf16_t* latb = (const bf16_t*)a.s.lat + (size_t)h * a.s.N * DL;
   const int* permb = a.s.perm + (size_t)h * a.s.N;
-  for (int it = ch * kPfNW + w; it < items; it += a.CH * kPfNW) {
-    int c = 0;
-    {
-      int lo = 0, hi = F;              // tpre[lo] <= it < tpre[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)tpre[mid] <= it) lo = mid; else hi = mid;
-      }
-      c = lo;
+  // item -> (leaf c of the parent, row tile i); this lane's entry (row,
+  // slot) of the leaf's list, or (-1, 0) past the end of the leaf's rows
+  auto item_of = [&](int itm, int* cc, int* ii) {
+    int lo = 0, hi = F;                // tpre[lo] <= itm < tpre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)tpre[mid] <= itm) lo = mid; else hi = mid;
     }
-    const int i = it - (int)tpre[c];
-    // this lane's row (lanes l and l + 32 share row l % 32)
-    const int r_in = i * 32 + l32;
-    // a lane past the end of the leaf's rows has no row: nothing reaches its
-    // threshold and it writes nothing
-    int row = -1, slot = 0, chi = -1;
+    *cc = lo;
+    *ii = itm - (int)tpre[lo];
+  };
+  auto entry_of = [&](int cc, int ii) {
+    const int r_in = ii * 32 + l32;
+    return r_in < (int)lcn[cc] ? a.Enext[lst[cc] + r_in] : make_int2(-1, 0);
+  };
+  // the next item's entries are loaded while the current item is scored
+  const int stride = a.CH * kPfNW;
+  int2 enext = make_int2(-1, 0);
+  {
+    const int it0 = ch * kPfNW + w;
+    if (it0 < items) {
+      int cc, ii;
+      item_of(it0, &cc, &ii);
+      enext = entry_of(cc, ii);
+    }
+  }
+  for (int it = ch * kPfNW + w; it < items; it += stride) {
+    int c, i;
+    item_of(it, &c, &i);
+    const int2 ecur = enext;
+    if (it + stride < items) {
+      int cn, in;
+      item_of(it + stride, &cn, &in);
+      enext = entry_of(cn, in);
+    }
+    // this lane's row (lanes l and l + 32 share row l % 32); a lane past the
+    // end of the leaf's rows has no row: nothing reaches its threshold and
+    // it writes nothing
+    int row = ecur.x, slot = ecur.y, chi = -1;
     float tau = __builtin_huge_valf();
-    if (r_in < (int)lcn[c]) {
-      const int2 e = a.Enext[lst[c] + r_in];
-      row = e.x;
-      slot = e.y;
+    if (row >= 0) {
       const int p = a.s.q_pos[row / a.s.Hq];
       chi = (p >= 0 && (int64_t)p < a.s.N) ? p - a.s.window : -1;
       if (!SAMPLE) tau = a.tauf[row];
