@@ -88,6 +88,7 @@ struct PfPlan {
   int nl[kMaxLevels + 1];      // slots per query head at each depth (nl[0] = 1)
   int nl_out;                  // out_leaves row width, b^L
   int spl;                     // samples per (query head, leaf)
+  int shalf;                   // 1: only leaves with an even child index are sampled
   int64_t cap;                 // appended keys per query head
   int merge_m;                 // merge buffer entries per thread
   int ch[kMaxLevels];          // workgroups per parent at each level

@@ -81,6 +81,7 @@ struct PfArgs {
   // gather
   int spl;                     // samples per (row, leaf)
   int spl4;                    // spl rounded up to a multiple of 4 (the stride of smp)
+  int shalf;                   // 1: only leaves with an even child index are sampled
   uint16_t* smp;               // [R][nl][spl4] top 16 bits of order(score), 0 = not a candidate
   float* tauf;                 // [R] score threshold, -inf = none
   int64_t cap;                 // append capacity per row
@@ -420,7 +421,9 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   if (w == 0) {
-    const uint32_t c = lane < F ? a.ccnt[cbase + lane] : 0u;
+    // the sample pass may skip the leaves with an odd child index
+    const bool skip = SAMPLE && a.shalf && (lane & 1);
+    const uint32_t c = (lane < F && !skip) ? a.ccnt[cbase + lane] : 0u;
     const uint32_t tl = (c + 31u) / 32u;
     uint32_t incl = tl;
 #pragma unroll
@@ -746,14 +749,22 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   const int* offL = a.s.off[lev] + (size_t)h * (Pe + 1);
   const int32_t* lfr = a.lf + (size_t)(live ? row : 0) * a.nl;
   const uint16_t* sm = a.smp + (size_t)(live ? row : 0) * a.nl * a.spl4;
-  int64_t tot = 0;
+  const int FL = a.s.F[lev];
+  auto sampled = [&](int leaf) { return !a.shalf || ((leaf % FL) & 1) == 0; };
+  int64_t tot = 0, tots = 0;                       // candidates of all / of the sampled leaves
   if (live)
     for (int sl = lane; sl < a.nl; sl += 64) {
       const int leaf = lfr[sl];
-      if (leaf >= 0) tot += offL[leaf + 1] - offL[leaf];
+      if (leaf < 0) continue;
+      const int sz = offL[leaf + 1] - offL[leaf];
+      tot += sz;
+      if (sampled(leaf)) tots += sz;
     }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) {
+    tot += __shfl_xor(tot, o, 64);
+    tots += __shfl_xor(tots, o, 64);
+  }
   const bool want = live && p >= 0 && (int64_t)p < a.s.N && tot > a.cap;
   const u64 target = (u64)((double)kPfTarget * a.s.k * 16.0);
   int d1 = -1, d2 = -1;
@@ -764,11 +775,13 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
     if (want && (pass == 0 || d1 >= 0))
       for (int sl = lane; sl < a.nl; sl += 64) {
         const int leaf = lfr[sl];
-        if (leaf < 0) continue;
+        if (leaf < 0 || !sampled(leaf)) continue;
         const int sz = offL[leaf + 1] - offL[leaf];
         const int se = sz < a.spl ? sz : a.spl;
         if (se == 0) continue;
-        const u64 wt = ((u64)sz << 4) / (u64)se;
+        // a sample stands for its share of the leaf, scaled up by the
+        // candidates of the leaves that were not sampled
+        const u64 wt = (u64)((double)sz * 16.0 * (double)tot / ((double)se * (double)tots));
         for (int q = 0; q < se; ++q) {
           const uint32_t v = sm[(size_t)sl * a.spl4 + q];
           if (v == 0u) continue;
@@ -1374,6 +1387,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
   a.nl = pl.nl[d.n_levels];
   a.spl = pl.spl;
   a.spl4 = (pl.spl + 3) / 4 * 4;
+  a.shalf = pl.shalf;
   a.smp = w.smp;
   a.tauf = w.tauf;
   a.cap = pl.cap;
@@ -1587,7 +1601,12 @@ PfPlan plan_prefill(const lsa_index_desc& d, const lsa_select_params& p, int32_t
   pl.merge_m = capl / kPfMergeBlock;
   if (pl.merge_m > 16) return pl;
   const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
-  pl.spl = clampi((int64_t)ceil(kPfSampleR * avg_leaf / (kPfTarget * p.k)), 1, 32);
+  // with many small leaves per row, only the leaves with an even child index
+  // are sampled (half the sample items), each with twice the samples; with
+  // large leaves a row's best keys sit in few leaves and skipping half of
+  // them would misplace the threshold
+  pl.shalf = (nl >= 64 && avg_leaf <= 64.0) ? 1 : 0;
+  pl.spl = clampi((int64_t)ceil(kPfSampleR * avg_leaf / (kPfTarget * p.k)) * (pl.shalf ? 2 : 1), 1, 32);
   for (int e = 0; e < d.n_levels; ++e) {
     const double parents = (double)d.n_kv_heads * (double)L.nodes[e];
     const double tiles = (double)R * pl.nl[e] / parents / 32.0;
