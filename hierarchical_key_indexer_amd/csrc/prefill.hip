@@ -315,7 +315,8 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   int64_t start;
   int n;
   pf_parent(a, gp, h, &start, &n);
-  const int ntiles = (n + 31) / 32;
+  // rows in tiles of 64, one per lane (the level kernel's tiles are 32 rows)
+  const int ntiles = (n + 63) / 64;
   const int64_t cbase = (int64_t)h * Pe + par * F;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (ch == 0 && ntiles == 0) {
@@ -341,8 +342,8 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   }
   __syncthreads();
   for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
-    const int r_in = ti * 32 + lane;
-    if (lane < 32 && r_in < n) {
+    const int r_in = ti * 64 + lane;
+    if (r_in < n) {
       u64 m = a.mask[start + r_in];
       while (m != 0ull) {
         atomicAdd(&lcnt[__ffsll((long long)m) - 1], 1u);
@@ -355,8 +356,8 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   __syncthreads();
   const bool last = a.lev == a.s.L - 1;
   for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
-    const int r_in = ti * 32 + lane;
-    if (lane < 32 && r_in < n) {
+    const int r_in = ti * 64 + lane;
+    if (r_in < n) {
       const int64_t pos = start + r_in;
       const int2 e = pf_entry(a, pos, h);
       u64 m = a.mask[pos];
