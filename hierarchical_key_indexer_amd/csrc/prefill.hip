@@ -166,17 +166,6 @@ __global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
 // descent, one level
 // ---------------------------------------------------------------------------
 
-// t[0..B) holds the B largest values seen so far, descending (with repeats).
-template <int B>
-__device__ __forceinline__ void topb_insert(uint32_t (&t)[B], uint32_t v) {
-#pragma unroll
-  for (int j = 0; j < B; ++j) {
-    const uint32_t hi = t[j] > v ? t[j] : v;
-    v = t[j] > v ? v : t[j];
-    t[j] = hi;
-  }
-}
-
 template <int DL, int NT, int BMAX>
 __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
   constexpr int KS = DL / 16;                    // k-steps of 16 latent dims
@@ -234,18 +223,27 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
       for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[t][s], Bv, acc[t], 0, 0, 0);
     }
     // lane holds row l32 against children 32t + 8(i/4) + 4 half + i%4
+    // the lane's BMAX best scores, descending: one v_med3 per entry and score
+    // (an empty child is -inf here and key 0 below)
     uint32_t key[NT][16];
-    uint32_t top[BMAX];
+    float tf[BMAX];
 #pragma unroll
-    for (int j = 0; j < BMAX; ++j) top[j] = 0u;
+    for (int j = 0; j < BMAX; ++j) tf[j] = -__builtin_huge_valf();
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
-        key[t][i] = ((ne_mask >> c) & 1ull) ? order_u32(acc[t][i]) : 0u;
-        topb_insert<BMAX>(top, key[t][i]);
+        const bool nec = (ne_mask >> c) & 1ull;
+        key[t][i] = nec ? order_u32(acc[t][i]) : 0u;
+        const float v = nec ? acc[t][i] : -__builtin_huge_valf();
+#pragma unroll
+        for (int j = BMAX - 1; j > 0; --j) tf[j] = __builtin_amdgcn_fmed3f(tf[j - 1], tf[j], v);
+        tf[0] = fmaxf(tf[0], v);
       }
+    uint32_t top[BMAX];
+#pragma unroll
+    for (int j = 0; j < BMAX; ++j) top[j] = tf[j] == -__builtin_huge_valf() ? 0u : order_u32(tf[j]);
     // the partner lane (lane ^ 32) holds the other children of the row
     uint32_t cm[BMAX];
 #pragma unroll
