@@ -733,6 +733,7 @@ __device__ __forceinline__ int wave_find_bin(const u64* hist, u64 need, u64* abo
 // 16-bit sample value whose weight at or above it reaches 1.5k, found with two
 // 8-bit histogram passes.  A row whose leaves hold at most `cap` keys in all
 // takes every candidate (no threshold).
+template <int kTauCL>
 __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   __shared__ u64 hist[kPfNW][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -750,15 +751,27 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   const uint16_t* sm = a.smp + (size_t)(live ? row : 0) * a.nl * a.spl4;
   const int FL = a.s.F[lev];
   auto sampled = [&](int leaf) { return !a.shalf || ((leaf % FL) & 1) == 0; };
-  int64_t tot = 0, tots = 0;                       // candidates of all / of the sampled leaves
-  if (live)
-    for (int sl = lane; sl < a.nl; sl += 64) {
-      const int leaf = lfr[sl];
-      if (leaf < 0) continue;
-      const int sz = offL[leaf + 1] - offL[leaf];
-      tot += sz;
-      if (sampled(leaf)) tots += sz;
+  // a lane takes the row's slots lane, lane + 64, ... in chunks of kTauCL,
+  // whose loads are issued together: slot -> leaf -> CSR range
+  auto chunk = [&](int base, int* leaf, int* sz) {
+#pragma unroll
+    for (int j = 0; j < kTauCL; ++j) {
+      const int sl = base + lane + 64 * j;
+      leaf[j] = (live && sl < a.nl) ? lfr[sl] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < kTauCL; ++j) sz[j] = leaf[j] >= 0 ? offL[leaf[j] + 1] - offL[leaf[j]] : 0;
+  };
+  int64_t tot = 0, tots = 0;                       // candidates of all / of the sampled leaves
+  for (int base = 0; base < a.nl; base += 64 * kTauCL) {
+    int leaf[kTauCL], sz[kTauCL];
+    chunk(base, leaf, sz);
+#pragma unroll
+    for (int j = 0; j < kTauCL; ++j) {
+      tot += sz[j];
+      if (leaf[j] >= 0 && sampled(leaf[j])) tots += sz[j];
+    }
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     tot += __shfl_xor(tot, o, 64);
@@ -772,20 +785,33 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
     for (int b = lane; b < 256; b += 64) hist[w][b] = 0ull;
     __syncthreads();
     if (want && (pass == 0 || d1 >= 0))
-      for (int sl = lane; sl < a.nl; sl += 64) {
-        const int leaf = lfr[sl];
-        if (leaf < 0 || !sampled(leaf)) continue;
-        const int sz = offL[leaf + 1] - offL[leaf];
-        const int se = sz < a.spl ? sz : a.spl;
-        if (se == 0) continue;
-        // a sample stands for its share of the leaf, scaled up by the
-        // candidates of the leaves that were not sampled
-        const u64 wt = (u64)((double)sz * 16.0 * (double)tot / ((double)se * (double)tots));
-        for (int q = 0; q < se; ++q) {
-          const uint32_t v = sm[(size_t)sl * a.spl4 + q];
-          if (v == 0u) continue;
-          if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
-          else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
+      for (int base = 0; base < a.nl; base += 64 * kTauCL) {
+        int leaf[kTauCL], sz[kTauCL];
+        chunk(base, leaf, sz);
+        // samples in groups of four (one 8-byte load per leaf and group)
+        for (int g = 0; g < a.spl; g += 4) {
+          u64 s4[kTauCL];
+#pragma unroll
+          for (int j = 0; j < kTauCL; ++j) {
+            const int sl = base + lane + 64 * j;
+            const bool use = leaf[j] >= 0 && sampled(leaf[j]) && g < min(sz[j], a.spl);
+            s4[j] = use ? *(const u64*)(sm + (size_t)sl * a.spl4 + g) : 0ull;
+          }
+#pragma unroll
+          for (int j = 0; j < kTauCL; ++j) {
+            if (s4[j] == 0ull) continue;
+            const int se = sz[j] < a.spl ? sz[j] : a.spl;
+            // a sample stands for its share of the leaf, scaled up by the
+            // candidates of the leaves that were not sampled
+            const u64 wt = (u64)((double)sz[j] * 16.0 * (double)tot / ((double)se * (double)tots));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t v = (uint32_t)(s4[j] >> (16 * c)) & 0xFFFFu;
+              if (v == 0u || g + c >= se) continue;
+              if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
+              else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
+            }
+          }
         }
       }
     __syncthreads();
@@ -1440,7 +1466,8 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     prof_begin(LSA_STAGE_SAMPLE, st);
     hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("sample pass");
-    hipLaunchKernelGGL(pf_tau_kernel, dim3(rgrid), dim3(kPfBlock), 0, st, a);
+    if (a.nl >= 512) hipLaunchKernelGGL(pf_tau_kernel<8>, dim3(rgrid), dim3(kPfBlock), 0, st, a);
+    else hipLaunchKernelGGL(pf_tau_kernel<4>, dim3(rgrid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("thresholds");
     prof_end(LSA_STAGE_SAMPLE, st);
     prof_begin(LSA_STAGE_GATHER, st);
