@@ -320,6 +320,7 @@ def main():
         "stages_ms": {name: stage_ms.get(st) for name, st in (("descend", _abi.STAGE_DESCEND),
                       ("sample", _abi.STAGE_SAMPLE), ("gather", _abi.STAGE_GATHER), ("merge", _abi.STAGE_MERGE))},
         "build_ms": build_ms,
+        "index_bytes": int(li.index.numel()),
         "graph_replay": graph,
     }
     if centroid is not None:
