@@ -349,14 +349,6 @@ __device__ void bitonic_sort_asc(u64* buf, int n, int cap) {
   }
 }
 
-// Write one output row from the n (<= k) rank keys in buf: sink positions,
-// the keys in ascending index order with their scores, the window positions.
-// buf[0..cap) is sort space; n <= cap / 2.  Every key's index lies in [0, p],
-// so the keys are bucketed by index over that span (1024 buckets; a bucket
-// index is a 32-bit multiply-high, monotone in the index), scattered to
-// buf[cap/2..) in bucket order and insertion-sorted inside every bucket.  A
-// bucket of more than 64 keys (a very uneven index spread) sends the whole
-// set to the bitonic sort instead.
 // LDS scratch of the bucket sort by key index.
 constexpr int kSortBuckets = 1024;
 struct SortScratch {
@@ -365,77 +357,164 @@ struct SortScratch {
   int big;
 };
 
-template <int BLOCK>
-__device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
-                                    int32_t* row, float* scores_row, SortScratch& ss) {
+// One output row from the n unique nonzero rank keys in buf[0..n) (n <=
+// BLOCK*M): the sink positions, the best k keys in ascending index order with
+// their scores (-1 / -inf past the last), the window positions.  The keys
+// stay in registers throughout: the MSB-first radix select of topk_compact
+// finds the k-th key, then the kept keys are re-keyed as (index << 32 |
+// order(score)), bucketed by index over [0, p] (1024 buckets; a bucket is a
+// 32-bit multiply-high of the index, monotone in it, clamped to the last),
+// scattered into buf in bucket order and insertion-sorted inside every
+// bucket.  A bucket of more than 64 keys (a very uneven index spread) sends
+// the kept set to the bitonic sort instead.  buf[0..cap) is scratch (cap >=
+// n, a power of two).  The caller's writes to buf must be visible (a barrier
+// before the call); all threads of the block call.
+template <int BLOCK, int M>
+__device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
+                                float* scores_row, RadixScratch* sc, SortScratch& ss) {
+  constexpr int NW = BLOCK / 64;
   constexpr int NB = kSortBuckets;
+  u64 v[M];
+  u64 lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int i = threadIdx.x + j * BLOCK;
+    v[j] = (i < n) ? buf[i] : 0ull;
+    if (v[j] != 0ull) {
+      lo = v[j] < lo ? v[j] : lo;
+      hi = v[j] > hi ? v[j] : hi;
+    }
+  }
+  u64 mask = 0ull, prefix = 0ull;                 // keep v with (v & mask) >= prefix
+  if (n > k) {
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    if ((threadIdx.x & 63) == 0) {
+      sc->wmin[threadIdx.x >> 6] = lo;
+      sc->wmax[threadIdx.x >> 6] = hi;
+    }
+    __syncthreads();
+    lo = sc->wmin[0];
+    hi = sc->wmax[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      lo = sc->wmin[i] < lo ? sc->wmin[i] : lo;
+      hi = sc->wmax[i] > hi ? sc->wmax[i] : hi;
+    }
+    const int top = (lo == hi) ? 0 : 64 - __clzll(lo ^ hi);
+    mask = top >= 64 ? 0ull : (~0ull << top);
+    prefix = lo & mask;
+    uint32_t need = (uint32_t)k;
+    for (int hb = top; hb > 0;) {
+      const int lb = hb > 8 ? hb - 8 : 0;
+      const u64 dmask = ((1ull << (hb - lb)) - 1ull);
+      for (int i = threadIdx.x; i < 256; i += BLOCK) sc->hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&sc->hist[(uint32_t)((v[j] >> lb) & dmask)], 1u);
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        const uint32_t h0 = sc->hist[4 * l], h1 = sc->hist[4 * l + 1], h2 = sc->hist[4 * l + 2],
+                       h3 = sc->hist[4 * l + 3];
+        const uint32_t s4 = h0 + h1 + h2 + h3;
+        uint32_t incl = s4;  // sum over lanes >= l
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          uint32_t o = __shfl_down(incl, off, 64);
+          if (l + off < 64) incl += o;
+        }
+        const uint32_t above = incl - s4;
+        if (above < need && need <= incl) {
+          uint32_t acc = above;
+          int d;
+          uint32_t hd;
+          if (acc + h3 >= need) { d = 4 * l + 3; hd = h3; }
+          else if ((acc += h3) + h2 >= need) { d = 4 * l + 2; hd = h2; }
+          else if ((acc += h2) + h1 >= need) { d = 4 * l + 1; hd = h1; }
+          else { acc += h1; d = 4 * l; hd = h0; }
+          sc->digit = d;
+          sc->above = acc;
+          sc->hd = hd;
+        }
+      }
+      __syncthreads();
+      const int d = sc->digit;
+      need -= sc->above;
+      const uint32_t hdv = sc->hd;
+      prefix |= (u64)d << lb;
+      mask |= dmask << lb;
+      __syncthreads();
+      if (hdv == need) break;
+      hb = lb;
+    }
+  }
+  // re-key the kept keys so an ascending sort orders by index, and count
+  // the buckets
   const uint64_t span = (uint64_t)(p > 0 ? p : 0) + 1;
   const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
-  auto bucket = [&](u64 key) {      // clamped, so an index past p still stays in range
+  auto bucket = [&](u64 key) {
     const uint32_t d = (uint32_t)(key >> 32);
     return (int)min(scale == 0u ? d : __umulhi(d, scale), (uint32_t)(NB - 1));
   };
   for (int b = threadIdx.x; b < NB; b += BLOCK) ss.cnt[b] = 0u;
   if (threadIdx.x == 0) ss.big = 0;
   __syncthreads();
-  // re-key as (index << 32 | order(score)) so an ascending sort orders by
-  // index, and count the buckets
-  for (int i = threadIdx.x; i < n; i += BLOCK) {
-    const u64 key = buf[i];
-    const u64 rk = ((u64)(uint32_t)rank_key_index(key) << 32) | (key >> 32);
-    buf[i] = rk;
-    atomicAdd(&ss.cnt[bucket(rk)], 1u);
-  }
-  __syncthreads();
-  u64* sorted = buf;
-  if (n > 1) {
-    constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
-    int mine = 0, mx = 0;
-    if ((int)threadIdx.x * PER < NB)
-      for (int j = 0; j < PER; ++j) {
-        const int c = (int)ss.cnt[threadIdx.x * PER + j];
-        mine += c;
-        mx = c > mx ? c : mx;
-      }
-    if (mx > 64) ss.big = 1;
-    int total;
-    int run = block_exclusive_scan<BLOCK>(mine, ss.wsum, &total);
-    if ((int)threadIdx.x * PER < NB)
-      for (int j = 0; j < PER; ++j) {
-        const int c = (int)ss.cnt[threadIdx.x * PER + j];
-        ss.cnt[threadIdx.x * PER + j] = (uint32_t)run;
-        run += c;
-      }
-    __syncthreads();
-    if (ss.big) {
-      bitonic_sort_asc<BLOCK>(buf, n, cap);
-    } else {
-      u64* out = buf + cap / 2;
-      for (int i = threadIdx.x; i < n; i += BLOCK) {
-        const u64 key = buf[i];
-        out[atomicAdd(&ss.cnt[bucket(key)], 1u)] = key;
-      }
-      __syncthreads();
-      // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
-      for (int b = threadIdx.x; b < NB; b += BLOCK) {
-        const int e = (int)ss.cnt[b], st = b == 0 ? 0 : (int)ss.cnt[b - 1];
-        for (int i = st + 1; i < e; ++i) {
-          const u64 x = out[i];
-          int j = i - 1;
-          while (j >= st && out[j] > x) {
-            out[j + 1] = out[j];
-            --j;
-          }
-          out[j + 1] = x;
-        }
-      }
-      __syncthreads();
-      sorted = out;
+  bool keep[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    keep[j] = v[j] != 0ull && (v[j] & mask) >= prefix;
+    if (keep[j]) {
+      v[j] = ((u64)(uint32_t)rank_key_index(v[j]) << 32) | (v[j] >> 32);
+      atomicAdd(&ss.cnt[bucket(v[j])], 1u);
     }
   }
+  __syncthreads();
+  constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
+  int mine = 0, mx = 0;
+  if ((int)threadIdx.x * PER < NB)
+    for (int j = 0; j < PER; ++j) {
+      const int c = (int)ss.cnt[threadIdx.x * PER + j];
+      mine += c;
+      mx = c > mx ? c : mx;
+    }
+  if (mx > 64) ss.big = 1;
+  int nk;
+  int run = block_exclusive_scan<BLOCK>(mine, ss.wsum, &nk);
+  if ((int)threadIdx.x * PER < NB)
+    for (int j = 0; j < PER; ++j) {
+      const int c = (int)ss.cnt[threadIdx.x * PER + j];
+      ss.cnt[threadIdx.x * PER + j] = (uint32_t)run;
+      run += c;
+    }
+  __syncthreads();
+  // buf is free: every key is in registers
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+    if (keep[j]) buf[atomicAdd(&ss.cnt[bucket(v[j])], 1u)] = v[j];
+  __syncthreads();
+  if (ss.big) {
+    bitonic_sort_asc<BLOCK>(buf, nk, cap);
+  } else {
+    // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
+    for (int b = threadIdx.x; b < NB; b += BLOCK) {
+      const int e = (int)ss.cnt[b], st = b == 0 ? 0 : (int)ss.cnt[b - 1];
+      for (int i = st + 1; i < e; ++i) {
+        const u64 x = buf[i];
+        int jj = i - 1;
+        while (jj >= st && buf[jj] > x) {
+          buf[jj + 1] = buf[jj];
+          --jj;
+        }
+        buf[jj + 1] = x;
+      }
+    }
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < k; i += BLOCK) {
-    if (i < n) {
-      const u64 key = sorted[i];
+    if (i < nk) {
+      const u64 key = buf[i];
       row[sink + i] = (int32_t)(key >> 32);
       if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
     } else {
@@ -451,11 +530,11 @@ __device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, i
 }
 
 // The same, with the sort scratch in a static LDS block of its own.
-template <int BLOCK>
-__device__ void write_selection_row(u64* buf, int n, int cap, int p, int sink, int k, int window,
-                                    int32_t* row, float* scores_row) {
+template <int BLOCK, int M>
+__device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
+                                float* scores_row, RadixScratch* sc) {
   __shared__ SortScratch ss;
-  write_selection_row<BLOCK>(buf, n, cap, p, sink, k, window, row, scores_row, ss);
+  write_top_k_row<BLOCK, M>(buf, n, k, cap, p, sink, window, row, scores_row, sc, ss);
 }
 
 // A row for a query whose position is outside [0, N): all -1.

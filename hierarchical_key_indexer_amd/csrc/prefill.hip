@@ -931,12 +931,8 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
       }
     }
   }
-  if (n > k) {
-    topk_compact<BLOCK, M>(buf, n, k, &rs);
-    n = k;
-  }
   __syncthreads();                                 // the lists are dead; the block becomes sort scratch
-  write_selection_row<BLOCK>(buf, n, CAP, p, a.s.sink, k, a.s.window, orow, srow, sort_ss);
+  write_top_k_row<BLOCK, M>(buf, n, k, CAP, p, a.s.sink, a.s.window, orow, srow, &rs, sort_ss);
 }
 
 // ---------------------------------------------------------------------------

@@ -431,15 +431,15 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
     // the sampled threshold let fewer than k keys through: redo without it
     n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs);
   }
-  if (n > a.k) {
-    topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-    n = a.k;
-  }
   if (a.S > 1) {
+    if (n > a.k) {
+      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+      n = a.k;
+    }
     append_part<BLOCK>(a, qh, buf, n, &base_sh);
   } else {
-    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
   }
 }
 
@@ -604,12 +604,8 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
     const int h = (int)(qh % a.Hq) / a.G;
     int n = gather_stream<LT, DL, M, 4, BLOCK>(a, qh, h, a.sink, p - a.window, lpre, lrow, 1, 0, a.N, 0ull, buf,
                                                &n_sh, &rs);
-    if (n > a.k) {
-      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-      n = a.k;
-    }
-    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     return;
   }
   if (n_in < a.k && thr0 != 0ull && a.nleaf) {
@@ -624,12 +620,8 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
     const int h = (int)(qh % a.Hq) / a.G;
     int n = gather_stream<LT, DL, M, 4, BLOCK>(a, qh, h, a.sink, p - a.window, lpre, lrow, nl, 0, lpre[nl], 0ull,
                                                buf, &n_sh, &rs);
-    if (n > a.k) {
-      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-      n = a.k;
-    }
-    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     return;
   }
   const u64* src = a.part_keys + qh * a.part_cap;
@@ -638,12 +630,8 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
     for (int i = threadIdx.x; i < n_in; i += BLOCK) buf[i] = src[i];
     __syncthreads();
     int n = n_in;
-    if (n > a.k) {
-      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-      n = a.k;
-    }
-    write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                               a.out_scores ? a.out_scores + qh * a.k : nullptr);
+    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     return;
   }
   u64 lowest = 0ull;                         // keys below this are never needed
@@ -701,12 +689,8 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   }
   __syncthreads();
   int n = n_sh;
-  if (n > a.k) {
-    topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-    n = a.k;
-  }
-  write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                             a.out_scores ? a.out_scores + qh * a.k : nullptr);
+  write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                            a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,15 +798,15 @@ __global__ __launch_bounds__(1024) void flat_kernel(SelArgs a) {
     const int64_t qh = qh_base + j;
     u64* buf = bufs + j * CAP;
     int n = n_sh[j];
-    if (n > a.k) {
-      topk_compact<BLOCK, M>(buf, n, a.k, &rs);
-      n = a.k;
-    }
     if (a.S > 1) {
+      if (n > a.k) {
+        topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+        n = a.k;
+      }
       append_part<BLOCK>(a, qh, buf, n, &base_sh);
     } else {
-      write_selection_row<BLOCK>(buf, n, CAP, p, a.sink, a.k, a.window, a.out_idx + qh * a.width,
-                                 a.out_scores ? a.out_scores + qh * a.k : nullptr);
+      write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                                a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     }
     __syncthreads();
   }
