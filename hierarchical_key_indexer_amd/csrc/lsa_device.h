@@ -216,6 +216,7 @@ struct RadixScratch {
   int digit;
   uint32_t above;
   uint32_t hd;
+  uint32_t sel[2][4];          // digit, keys above it, keys in it: two passes in flight
 };
 
 __device__ __forceinline__ u64 wave_min_u64(u64 v) {
@@ -357,29 +358,33 @@ struct SortScratch {
   int big;
 };
 
-// One output row from the n unique nonzero rank keys in buf[0..n) (n <=
-// BLOCK*M): the sink positions, the best k keys in ascending index order with
-// their scores (-1 / -inf past the last), the window positions.  The keys
-// stay in registers throughout: the MSB-first radix select of topk_compact
-// finds the k-th key, then the kept keys are re-keyed as (index << 32 |
-// order(score)), bucketed by index over [0, p] (1024 buckets; a bucket is a
-// 32-bit multiply-high of the index, monotone in it, clamped to the last),
-// scattered into buf in bucket order and insertion-sorted inside every
-// bucket.  A bucket of more than 64 keys (a very uneven index spread) sends
-// the kept set to the bitonic sort instead.  buf[0..cap) is scratch (cap >=
-// n, a power of two).  The caller's writes to buf must be visible (a barrier
-// before the call); all threads of the block call.
+// One output row from the n unique nonzero rank keys in buf[0..n) (or in
+// global src[0..n) when src is given; n <= BLOCK*M): the sink positions, the
+// best k keys in ascending index order with their scores (-1 / -inf past the
+// last), the window positions.  The keys stay in registers throughout.  The
+// k-th key is found by an MSB-first radix select as in topk_compact (with two
+// histograms, so a pass takes two barriers).  The kept keys are re-keyed as
+// (index << 32 | order(score)), bucketed by index over [0, p] (1024 buckets;
+// a bucket is a 32-bit multiply-high of the index, monotone in it, clamped to
+// the last) and scattered into buf in bucket order; every key then counts the
+// smaller keys of its own bucket, which gives its position in the sorted
+// row.  A bucket of more than 64 keys (a very uneven index spread) sends the
+// kept set to the bitonic sort instead.  buf[0..cap) is scratch (cap >= n,
+// cap >= 2k, a power of two).  The caller's writes to buf must be visible (a barrier before the
+// call); all threads of the block call.
 template <int BLOCK, int M>
 __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
-                                float* scores_row, RadixScratch* sc, SortScratch& ss) {
+                                float* scores_row, RadixScratch* sc, SortScratch& ss,
+                                const u64* src = nullptr) {
   constexpr int NW = BLOCK / 64;
   constexpr int NB = kSortBuckets;
+  static_assert(NB >= 256, "the second radix histogram lives in the bucket counts");
   u64 v[M];
   u64 lo = ~0ull, hi = 0ull;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const int i = threadIdx.x + j * BLOCK;
-    v[j] = (i < n) ? buf[i] : 0ull;
+    v[j] = (i < n) ? (src ? src[i] : buf[i]) : 0ull;
     if (v[j] != 0ull) {
       lo = v[j] < lo ? v[j] : lo;
       hi = v[j] > hi ? v[j] : hi;
@@ -387,6 +392,10 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
   }
   u64 mask = 0ull, prefix = 0ull;                 // keep v with (v & mask) >= prefix
   if (n > k) {
+    for (int i = threadIdx.x; i < 256; i += BLOCK) {
+      sc->hist[i] = 0u;
+      ss.cnt[i] = 0u;
+    }
     lo = wave_min_u64(lo);
     hi = wave_max_u64(hi);
     if ((threadIdx.x & 63) == 0) {
@@ -405,19 +414,26 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
     mask = top >= 64 ? 0ull : (~0ull << top);
     prefix = lo & mask;
     uint32_t need = (uint32_t)k;
-    for (int hb = top; hb > 0;) {
+    // pass i counts into sc->hist (even i) or ss.cnt[0, 256) (odd i) and
+    // posts its result in sel[i & 1];
+    // wave 0 clears the histogram it has read, ready for pass i + 2, and
+    // every thread reads sel[i & 1] before it reaches the next pass's barrier
+    int par = 0;
+    for (int hb = top; hb > 0; par ^= 1) {
       const int lb = hb > 8 ? hb - 8 : 0;
       const u64 dmask = ((1ull << (hb - lb)) - 1ull);
-      for (int i = threadIdx.x; i < 256; i += BLOCK) sc->hist[i] = 0;
-      __syncthreads();
+      uint32_t* h = par ? ss.cnt : sc->hist;
 #pragma unroll
       for (int j = 0; j < M; ++j)
-        if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&sc->hist[(uint32_t)((v[j] >> lb) & dmask)], 1u);
+        if (v[j] != 0ull && (v[j] & mask) == prefix) atomicAdd(&h[(uint32_t)((v[j] >> lb) & dmask)], 1u);
       __syncthreads();
       if (threadIdx.x < 64) {
         const int l = threadIdx.x;
-        const uint32_t h0 = sc->hist[4 * l], h1 = sc->hist[4 * l + 1], h2 = sc->hist[4 * l + 2],
-                       h3 = sc->hist[4 * l + 3];
+        const uint32_t h0 = h[4 * l], h1 = h[4 * l + 1], h2 = h[4 * l + 2], h3 = h[4 * l + 3];
+        h[4 * l] = 0u;
+        h[4 * l + 1] = 0u;
+        h[4 * l + 2] = 0u;
+        h[4 * l + 3] = 0u;
         const uint32_t s4 = h0 + h1 + h2 + h3;
         uint32_t incl = s4;  // sum over lanes >= l
 #pragma unroll
@@ -434,24 +450,23 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
           else if ((acc += h3) + h2 >= need) { d = 4 * l + 2; hd = h2; }
           else if ((acc += h2) + h1 >= need) { d = 4 * l + 1; hd = h1; }
           else { acc += h1; d = 4 * l; hd = h0; }
-          sc->digit = d;
-          sc->above = acc;
-          sc->hd = hd;
+          sc->sel[par][0] = (uint32_t)d;
+          sc->sel[par][1] = acc;
+          sc->sel[par][2] = hd;
         }
       }
       __syncthreads();
-      const int d = sc->digit;
-      need -= sc->above;
-      const uint32_t hdv = sc->hd;
+      const uint32_t d = sc->sel[par][0];
+      need -= sc->sel[par][1];
+      const uint32_t hdv = sc->sel[par][2];
       prefix |= (u64)d << lb;
       mask |= dmask << lb;
-      __syncthreads();
       if (hdv == need) break;
       hb = lb;
     }
   }
   // re-key the kept keys so an ascending sort orders by index, and count
-  // the buckets
+  // the buckets (every thread has passed the last histogram read)
   const uint64_t span = (uint64_t)(p > 0 ? p : 0) + 1;
   const uint32_t scale = span <= (uint64_t)NB ? 0u : (uint32_t)(((uint64_t)NB << 32) / span);
   auto bucket = [&](u64 key) {
@@ -494,27 +509,30 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
   for (int j = 0; j < M; ++j)
     if (keep[j]) buf[atomicAdd(&ss.cnt[bucket(v[j])], 1u)] = v[j];
   __syncthreads();
+  const u64* sorted = buf;
   if (ss.big) {
     bitonic_sort_asc<BLOCK>(buf, nk, cap);
   } else {
-    // cnt[b] is now the end of bucket b; bucket b starts where b-1 ends
-    for (int b = threadIdx.x; b < NB; b += BLOCK) {
-      const int e = (int)ss.cnt[b], st = b == 0 ? 0 : (int)ss.cnt[b - 1];
-      for (int i = st + 1; i < e; ++i) {
-        const u64 x = buf[i];
-        int jj = i - 1;
-        while (jj >= st && buf[jj] > x) {
-          buf[jj + 1] = buf[jj];
-          --jj;
-        }
-        buf[jj + 1] = x;
+    // cnt[b] is now the end of bucket b and its start is the end of b - 1;
+    // a key's position is its bucket's start plus the smaller keys in it.
+    // The keys land in buf[cap/2, cap/2 + nk) in order, so the row is
+    // written with coalesced stores
+    u64* out = buf + cap / 2;
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (keep[j]) {
+        const int b = bucket(v[j]);
+        const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
+        int r = st;
+        for (int i = st; i < e; ++i) r += buf[i] < v[j] ? 1 : 0;
+        out[r] = v[j];
       }
-    }
     __syncthreads();
+    sorted = out;
   }
   for (int i = threadIdx.x; i < k; i += BLOCK) {
     if (i < nk) {
-      const u64 key = buf[i];
+      const u64 key = sorted[i];
       row[sink + i] = (int32_t)(key >> 32);
       if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
     } else {
@@ -532,9 +550,9 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
 // The same, with the sort scratch in a static LDS block of its own.
 template <int BLOCK, int M>
 __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
-                                float* scores_row, RadixScratch* sc) {
+                                float* scores_row, RadixScratch* sc, const u64* src = nullptr) {
   __shared__ SortScratch ss;
-  write_top_k_row<BLOCK, M>(buf, n, k, cap, p, sink, window, row, scores_row, sc, ss);
+  write_top_k_row<BLOCK, M>(buf, n, k, cap, p, sink, window, row, scores_row, sc, ss, src);
 }
 
 // A row for a query whose position is outside [0, N): all -1.

@@ -583,13 +583,14 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   u64* buf = (u64*)smem;
   const int64_t qh = a.qh0 + blockIdx.x;
   const int t = (int)(qh / a.Hq);
+  // the three loads are independent: issue them together
+  const int n_in = (int)a.part_n[qh];
+  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   const int p = a.q_pos[t];
   if (p < 0 || (int64_t)p >= a.N) {
     write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
   }
-  const int n_in = (int)a.part_n[qh];
-  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   if (n_in < a.k && thr0 != 0ull && !a.nleaf) {
     // full scan: the sampled threshold let fewer than k keys through; scan
     // every row of the KV head here, without it
@@ -626,12 +627,9 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   }
   const u64* src = a.part_keys + qh * a.part_cap;
   if (n_in <= CAP) {
-    // everything fits the buffer: one coalesced load and one selection
-    for (int i = threadIdx.x; i < n_in; i += BLOCK) buf[i] = src[i];
-    __syncthreads();
-    int n = n_in;
-    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
-                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
+    // everything fits the registers: one coalesced load and one selection
+    write_top_k_row<BLOCK, M>(buf, n_in, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs, src);
     return;
   }
   u64 lowest = 0ull;                         // keys below this are never needed
