@@ -151,7 +151,9 @@ __device__ __forceinline__ void wave_select_top32(const uint32_t* key, int need,
   }
 }
 
-template <typename KT, typename LT, int DL, int BLOCK>
+// SMALL: a per-parent beam and every fanout <= 64 (the only branch compiled
+// in; the general branches would raise the register count past the budget)
+template <typename KT, typename LT, int DL, int BLOCK, bool SMALL>
 __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   constexpr int NW = BLOCK / 64;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -181,53 +183,74 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
     const int F = a.F[lev];
     const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
     const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
-    if (a.beam == LSA_BEAM_PER_PARENT) {
-      const int NJ = (F + 63) / 64;
+    if constexpr (SMALL) {
+      // A parent's children are one contiguous block of centroid rows: LPK
+      // lanes read a row (16 bytes each, so a load instruction covers KPW
+      // whole rows) and reduce their partial dots with DPP; each lane then
+      // takes its own child's score and the wave ranks them.  A wave loads
+      // two parents' rows before it scores either (bf16 rows, or fp32 rows at
+      // d_l = 32), so their round trips overlap.  Loads past the last child re-read the last row (its score
+      // is dropped), so every load is unconditional.
+      constexpr int E = Lat<LT>::PER16;
+      constexpr int LPK = DL / E;           // lanes per centroid row
+      constexpr int KPW = 64 / LPK;         // rows per load instruction
+      constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
       const int bs = min(a.b, F);
-      if (F <= 64) {
-        // A parent's children are one contiguous block of centroid rows: LPK
-        // lanes read a row (16 bytes each, so a load instruction covers KPW
-        // whole rows) and reduce their partial dots with DPP; each lane then
-        // takes its own child's score and the wave ranks them.
-        constexpr int E = Lat<LT>::PER16;
-        constexpr int LPK = DL / E;           // lanes per centroid row
-        constexpr int KPW = 64 / LPK;         // rows per load instruction
-        constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
-        const int lig = lane % LPK, g = lane / LPK;
-        QSlice<LT> qv;
-        qv.load(q + lig * E);
-        for (int i = w; i < nf; i += NW) {
-          const int64_t node0 = (int64_t)fa[i] * F;
-          uint4 v[NR];
+      const int lig = lane % LPK, g = lane / LPK;
+      QSlice<LT> qv;
+      qv.load(q + lig * E);
+      auto load = [&](int i, uint4* v, int& o0, int& o1) {
+        const int64_t node0 = (int64_t)fa[i] * F;
 #pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const int c = r * KPW + g;
-            v[r] = make_uint4(0u, 0u, 0u, 0u);
-            if (c < F) v[r] = *(const uint4*)(cs + (node0 + c) * DL + lig * E);
-          }
-          int o0 = 0, o1 = 0;
-          if (lane < F) {
-            o0 = off[node0 + lane];
-            o1 = off[node0 + lane + 1];
-          }
-          float part[NR];
-#pragma unroll
-          for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
-          // child `lane` is row g' = lane % KPW of round lane / KPW, summed at lane g' * LPK
-          float sc = 0.f;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const float x = __shfl(part[r], (lane % KPW) * LPK, 64);
-            if (lane / KPW == r) sc = x;
-          }
-          const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
-          u64 in[1];
-          wave_select_top32<1>(&key, bs, in);
-          // kept in child order (ties went to the lower child id)
-          if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
-          for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
+        for (int r = 0; r < NR; ++r) {
+          const int c = min(r * KPW + g, F - 1);
+          v[r] = *(const uint4*)(cs + (node0 + c) * DL + lig * E);
         }
-      } else
+        const int c = min(lane, F - 1);
+        o0 = off[node0 + c];
+        o1 = off[node0 + c + 1];
+      };
+      auto pick = [&](int i, const uint4* v, int o0, int o1) {
+        float part[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
+        // child `lane` is row g' = lane % KPW of round lane / KPW, summed at lane g' * LPK
+        float sc = 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float x = __shfl(part[r], (lane % KPW) * LPK, 64);
+          if (lane / KPW == r) sc = x;
+        }
+        const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
+        u64 in[1];
+        wave_select_top32<1>(&key, bs, in);
+        // kept in child order (ties went to the lower child id)
+        if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
+        for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
+      };
+      if constexpr (NR <= 8) {
+        for (int i = w; i < nf; i += 2 * NW) {
+          const bool two = i + NW < nf;
+          uint4 va[NR], vb[NR];
+          int a0, a1, b0, b1;
+          load(i, va, a0, a1);
+          load(two ? i + NW : i, vb, b0, b1);
+          pick(i, va, a0, a1);
+          if (two) pick(i + NW, vb, b0, b1);
+        }
+      } else {
+        // fp32 rows at d_l = 64: two parents' rows would not fit the registers
+        for (int i = w; i < nf; i += NW) {
+          uint4 va[NR];
+          int a0, a1;
+          load(i, va, a0, a1);
+          pick(i, va, a0, a1);
+        }
+      }
+      __syncthreads();
+      nf = compact_ids<BLOCK>(fb, nf * bs, fa, wsum);
+    } else if (a.beam == LSA_BEAM_PER_PARENT) {
+      const int bs = min(a.b, F);
       for (int i = w; i < nf; i += NW) {
         const int par = fa[i];
         u64 key[4];
@@ -254,7 +277,6 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
           slot += __popcll(in[j]);
         }
         for (int r = min(nne, bs) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
-        (void)NJ;
       }
       __syncthreads();
       nf = compact_ids<BLOCK>(fb, nf * bs, fa, wsum);
@@ -958,7 +980,9 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
     constexpr int DB = 1024;
     const size_t dlds = ((size_t)(2 * pl.nl_cap + 1) * 4 + 7) / 8 * 8 +
                         (p.beam == LSA_BEAM_GLOBAL ? (size_t)p.b * 256 * 8 : 0) + (size_t)DB * 8;
-    auto dk = descend_kernel<KT, LT, DL, DB>;
+    bool small = p.beam == LSA_BEAM_PER_PARENT;
+    for (int l = 0; l < d.n_levels; ++l) small = small && d.fanout[l] <= 64;
+    auto dk = small ? descend_kernel<KT, LT, DL, DB, true> : descend_kernel<KT, LT, DL, DB, false>;
     allow_lds(dk, dlds);
     prof_begin(LSA_STAGE_DESCEND, st);
     for (int64_t q0 = 0; q0 < QH; q0 += chunk) {

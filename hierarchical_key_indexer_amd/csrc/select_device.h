@@ -58,14 +58,27 @@ template <typename KT, typename LT, int DL>
 __device__ __forceinline__ void query_latent(const SelArgs& a, int64_t qh, int h, float* qin, float* q_out) {
   const KT* qrow = (const KT*)a.queries + qh * a.d_head;
   float* part = qin + a.d_head;
+  const bool pj = threadIdx.x < kQSlices * DL;
+  const int j = threadIdx.x % DL, sl = threadIdx.x / DL;
+  const int per = a.d_head / kQSlices;
+  const float* Wh = a.W + (size_t)h * a.d_head * DL + j;
+  // the first 32 weights of the thread's slice do not depend on the query:
+  // their loads are issued first and overlap the query's round trip
+  constexpr int kW0 = 32;
+  const int n0 = per < kW0 ? per : kW0;
+  float w0[kW0];
+  if (pj) {
+#pragma unroll
+    for (int u = 0; u < kW0; ++u) w0[u] = Wh[(size_t)(sl * per + (u < n0 ? u : n0 - 1)) * DL];
+  }
   for (int i = threadIdx.x; i < a.d_head; i += blockDim.x) qin[i] = KeyLoad<KT>::get(qrow, i);
   __syncthreads();
-  if (threadIdx.x < kQSlices * DL) {
-    const int j = threadIdx.x % DL, sl = threadIdx.x / DL;
-    const int per = a.d_head / kQSlices;
-    const float* Wh = a.W + (size_t)h * a.d_head * DL + j;
+  if (pj) {
     float acc = 0.f;
-    for (int i = sl * per; i < (sl + 1) * per; i += 8) {   // per is a multiple of 8
+#pragma unroll
+    for (int u = 0; u < kW0; ++u)
+      if (u < n0) acc = fmaf(qin[sl * per + u], w0[u], acc);
+    for (int i = sl * per + n0; i < (sl + 1) * per; i += 8) {   // per is a multiple of 8
       float wv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) wv[u] = Wh[(size_t)(i + u) * DL];
