@@ -431,27 +431,52 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   int* lpre = (int*)(buf + CAP);
   int* lrow = lpre + a.nl_cap + 1;
 
+  __shared__ float qs[DL];
   const int64_t qh = a.qh0 + blockIdx.y;
   const int s = blockIdx.x;
   const int t = (int)(qh / a.Hq), hq = (int)(qh % a.Hq), h = hq / a.G;
+  // None of these loads depends on another (the leaf lists are read to
+  // their capacity, not to the list length), so they are all issued before
+  // the first LDS store and share one round trip.
   const int p = a.q_pos[t];
+  const int nl = a.nleaf[qh];
+  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
+  {
+    constexpr int R = 3;
+    const int np = a.nl_cap + 1;
+    const int* gp = a.leafpre + qh * np;
+    const int* gr = a.leafrow + qh * a.nl_cap;
+    int vp[R], vr[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = threadIdx.x + j * BLOCK;
+      vp[j] = i < np ? gp[i] : 0;
+      vr[j] = i < a.nl_cap ? gr[i] : 0;
+    }
+    const float qv = threadIdx.x < DL ? a.qlat[qh * DL + threadIdx.x] : 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = threadIdx.x + j * BLOCK;
+      if (i < np) lpre[i] = vp[j];
+      if (i < a.nl_cap) lrow[i] = vr[j];
+    }
+    if (threadIdx.x < DL) qs[threadIdx.x] = qv;
+    for (int i = threadIdx.x + R * BLOCK; i < np; i += BLOCK) lpre[i] = gp[i];
+    for (int i = threadIdx.x + R * BLOCK; i < a.nl_cap; i += BLOCK) lrow[i] = gr[i];
+  }
   if (p < 0 || (int64_t)p >= a.N) {
     if (a.S == 1)
       write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
   }
   const int clo = a.sink, chi = p - a.window;
-  const int nl = a.nleaf[qh];
-  for (int i = threadIdx.x; i <= nl; i += BLOCK) lpre[i] = a.leafpre[qh * (a.nl_cap + 1) + i];
-  for (int i = threadIdx.x; i < nl; i += BLOCK) lrow[i] = a.leafrow[qh * a.nl_cap + i];
   __syncthreads();
   const int64_t total = lpre[nl];
   const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
-  const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
-  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs);
+  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs, qs);
   if (a.S == 1 && n < a.k && thr0 != 0ull) {
     // the sampled threshold let fewer than k keys through: redo without it
-    n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs);
+    n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs, qs);
   }
   if (a.S > 1) {
     if (n > a.k) {

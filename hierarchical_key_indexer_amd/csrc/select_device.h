@@ -156,11 +156,13 @@ __device__ void append_part(const SelArgs& a, int64_t qh, const u64* buf, int n,
 // Score candidates [lo, hi) of a query head's leaf list (CSR rows of KV head
 // h; lpre / lrow in LDS) and append the rank keys above thr to buf, keeping
 // at most the best k when the buffer fills (streaming radix-select
-// compaction).  Returns the number of keys left in buf.  Block-wide.
+// compaction).  Returns the number of keys left in buf.  The query latent is
+// read from qsrc when given (visible to the block), else from a.qlat.
+// Block-wide.
 template <typename LT, int DL, int M, int U, int BLOCK>
 __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int chi, const int* lpre,
                              const int* lrow, int nl, int64_t lo, int64_t hi, u64 thr, u64* buf, int* n_sh,
-                             RadixScratch* rs) {
+                             RadixScratch* rs, const float* qsrc = nullptr) {
   constexpr int NW = BLOCK / 64;
   constexpr int CAP = M * BLOCK;
   constexpr int E = Lat<LT>::PER16;              // latent elements per lane load
@@ -174,7 +176,7 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
   const int64_t wlen = (hi - lo + NW - 1) / NW;
   const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
   QSlice<LT> qv;
-  qv.load(a.qlat + qh * DL + lig * E);
+  qv.load((qsrc ? qsrc : a.qlat + qh * DL) + lig * E);   // qsrc: the latent already in LDS
   // first leaf of this wave's range (largest i with lpre[i] <= wlo)
   int cur = 0;
   {
