@@ -886,7 +886,8 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   float* srow = a.s.out_scores ? a.s.out_scores + (size_t)row * a.s.k : nullptr;
   const bool valid_p = p >= 0 && (int64_t)p < a.s.N;
   const int k = a.s.k;
-  const int n_in = valid_p ? (int)*pf_count_of(a, row) : 0;
+  const int n_raw = (int)*pf_count_of(a, row);     // loaded with p, not after it
+  const int n_in = valid_p ? n_raw : 0;
   const float tau = a.tauf[row];
   const bool rescore = valid_p && ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf()));
   int nlv = 0, total = 0;
@@ -915,6 +916,13 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
     // score every candidate of the row
     n = gather_stream<bf16_t, DL, M, 4, BLOCK>(a.s, row, h, a.s.sink, p - a.s.window, lpre, lrow, nlv, 0, total,
                                                0ull, buf, &n_sh, &rs);
+  } else if (n_in <= CAP) {
+    // the appended keys fit the registers: they are read from the list by
+    // the selection itself
+    __syncthreads();                               // the lists are dead; the block becomes sort scratch
+    write_top_k_row<BLOCK, M>(buf, n_in, k, CAP, p, a.s.sink, a.s.window, orow, srow, &rs, sort_ss,
+                              a.s.part_keys + (size_t)row * a.cap);
+    return;
   } else {
     // stream the appended keys through the buffer (CAP >= 2k), keeping the
     // best k whenever it fills before the end
