@@ -455,13 +455,17 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     *cc = lo;
     *ii = itm - (int)tpre[lo];
   };
+  // this lane's entry of the item's row tile; a lane past the end of the
+  // leaf's rows reads the leaf's last entry (dropped where it is used), so
+  // the load is unconditional and may stay in flight
   auto entry_of = [&](int cc, int ii) {
-    const int r_in = ii * 32 + l32;
-    return r_in < (int)lcn[cc] ? a.Enext[lst[cc] + r_in] : make_int2(-1, 0);
+    const int r_in = min(ii * 32 + l32, (int)lcn[cc] - 1);
+    return a.Enext[lst[cc] + r_in];
   };
   // the next item's entries are loaded while the current item is scored
+  // (past the last item, the current item's again)
   const int stride = a.CH * kPfNW;
-  int2 enext = make_int2(-1, 0);
+  int2 enext = make_int2(0, 0);
   {
     const int it0 = ch * kPfNW + w;
     if (it0 < items) {
@@ -474,21 +478,16 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     int c, i;
     item_of(it, &c, &i);
     const int2 ecur = enext;
-    if (it + stride < items) {
+    {
       int cn, in;
-      item_of(it + stride, &cn, &in);
+      item_of(it + stride < items ? it + stride : it, &cn, &in);
       enext = entry_of(cn, in);
     }
     // this lane's row (lanes l and l + 32 share row l % 32); a lane past the
     // end of the leaf's rows has no row: nothing reaches its threshold and
     // it writes nothing
-    int row = ecur.x, slot = ecur.y, chi = -1;
-    float tau = __builtin_huge_valf();
-    if (row >= 0) {
-      const int p = a.s.q_pos[row / a.s.Hq];
-      chi = (p >= 0 && (int64_t)p < a.s.N) ? p - a.s.window : -1;
-      if (!SAMPLE) tau = a.tauf[row];
-    }
+    const int row = i * 32 + l32 < (int)lcn[c] ? ecur.x : -1;
+    const int slot = ecur.y;
     const int o0 = o0s[c], o1 = o1s[c];
     // key tile kt: A operand (key l32's dims) and the key's index (INT_MAX
     // for a missing key or one inside the sink)
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int q = 0; q < PL; ++q) {
         const int c = lane + 64 * q;
-        const int krow = min(o0 + 32 * kt + c / RP, o1 - 1);
+        const int krow = max(0, min(o0 + 32 * kt + c / RP, o1 - 1));   // in range for an empty leaf too
         P[q] = *(const u32x4*)(latb + (size_t)krow * DL + (c % RP) * 8);
       }
     };
@@ -523,6 +522,20 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
         A[s] = as_v8s(*(const uint4*)(kl + l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16));
       }
     };
+    // key l32's position, raw (read early) and as a candidate test value:
+    // INT_MAX for a missing key or one inside the sink
+    auto pos_raw = [&](int kt) { return permb[max(0, min(o0 + 32 * kt + l32, o1 - 1))]; };
+    auto pos_of = [&](int kt, int jraw) { return (o0 + 32 * kt + l32 < o1 && jraw >= sink) ? jraw : INT_MAX; };
+    // The first key tile depends only on the leaf's range and the row data
+    // only on the entry: every load below is unconditional (a lane with no
+    // row reads row 0's data and drops it), so they all share one round
+    // trip.
+    u32x4 PK[PL];
+    load_parts(0, PK);
+    int jr = pos_raw(0);
+    const int rq = row >= 0 ? row : 0;
+    const int pq = a.s.q_pos[rq / a.s.Hq];
+    const float tq = SAMPLE ? 0.f : a.tauf[rq];
     // the rows' latents (the B operand, a missing row as zeros).  The sample
     // pass scores one key tile per item, so its row load matters as much as
     // the key load: it comes coalesced through the LDS tile as well.  The
@@ -534,29 +547,25 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int q = 0; q < PL; ++q) {
         const int cq = lane + 64 * q;
         const int rr = __shfl(row, cq / RP, 64);
-        P[q] = rr >= 0 ? *(const u32x4*)(a.qlat16 + (size_t)rr * DL + (cq % RP) * 8) : u32x4{0u, 0u, 0u, 0u};
+        P[q] = *(const u32x4*)(a.qlat16 + (size_t)(rr >= 0 ? rr : 0) * DL + (cq % RP) * 8);
+        if (rr < 0) P[q] = u32x4{0u, 0u, 0u, 0u};
       }
       put_parts(P);
       get_a(Bq);
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
-        if (row >= 0) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+        uint4 u = *(const uint4*)(a.qlat16 + (size_t)rq * DL + 16 * s + 8 * half);
+        if (row < 0) u = make_uint4(0u, 0u, 0u, 0u);
         Bq[s] = as_v8s(u);
       }
     }
-    // key l32's position, raw (read early) and as a candidate test value:
-    // INT_MAX for a missing key or one inside the sink
-    auto pos_raw = [&](int kt) { return permb[min(o0 + 32 * kt + l32, o1 - 1)]; };
-    auto pos_of = [&](int kt, int jraw) { return (o0 + 32 * kt + l32 < o1 && jraw >= sink) ? jraw : INT_MAX; };
+    const int chi = (row >= 0 && pq >= 0 && (int64_t)pq < a.s.N) ? pq - a.s.window : -1;
+    const float tau = (row >= 0 && !SAMPLE) ? tq : __builtin_huge_valf();
     // results: lane holds row l32 against keys m = 8(r/4) + 4 half + r%4
     if (SAMPLE) {
       if (o1 <= o0) continue;
-      u32x4 P[PL];
-      load_parts(0, P);
-      const int jr = pos_raw(0);
-      put_parts(P);
+      put_parts(PK);
       v8s A[KS];
       get_a(A);
       v16f acc;
@@ -618,16 +627,11 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       wave_lds_sync();
       cnt = 0;
     };
-    u32x4 P[PL];
-    int jr = 0, jrn = 0;
-    if (nkt > 0) {
-      load_parts(0, P);
-      jr = pos_raw(0);
-    }
+    int jrn = 0;
     for (int kt = 0; kt < nkt; ++kt) {
-      put_parts(P);
+      put_parts(PK);
       if (kt + 1 < nkt) {
-        load_parts(kt + 1, P);
+        load_parts(kt + 1, PK);
         jrn = pos_raw(kt + 1);
       }
       v8s A[KS];
