@@ -523,8 +523,17 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
       if (keep[j]) {
         const int b = bucket(v[j]);
         const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
+        // indices are unique, so the high words alone order the keys; four
+        // independent reads per step (entries past e, still inside buf since
+        // nk + 3 < cap, are masked)
+        const uint32_t xi = (uint32_t)(v[j] >> 32);
+        const uint32_t* hw = (const uint32_t*)buf + 1;
         int r = st;
-        for (int i = st; i < e; ++i) r += buf[i] < v[j] ? 1 : 0;
+        for (int i = st; i < e; i += 4) {
+          const uint32_t y0 = hw[2 * i], y1 = hw[2 * i + 2], y2 = hw[2 * i + 4], y3 = hw[2 * i + 6];
+          r += (y0 < xi ? 1 : 0) + (i + 1 < e && y1 < xi ? 1 : 0) + (i + 2 < e && y2 < xi ? 1 : 0) +
+               (i + 3 < e && y3 < xi ? 1 : 0);
+        }
         out[r] = v[j];
       }
     __syncthreads();
