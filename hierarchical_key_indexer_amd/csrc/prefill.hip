@@ -386,10 +386,11 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
 // Items of a workgroup: (leaf c of the parent, tile i of 32 of the leaf's
 // rows).  Keys are the A operand and rows the B operand, so a lane holds one
 // row (its threshold and causal limit stay in registers) against 16 keys of
-// every 32-key tile.  Main mode runs over the leaf's key tiles twice: once to
-// count each row's keys at or above its threshold (one atomic per row and
-// item reserves their places), once to write them.  Sample mode scores the
-// first key tile and keeps the first spl scores of every row.
+// every 32-key tile.  Main mode runs once over the leaf's key tiles and
+// stages the keys at or above their row's threshold in the wave's LDS; at
+// the end of the item one atomic per row reserves their places in the rows'
+// lists.  Sample mode scores the first key tile and keeps the first spl
+// scores of every row.
 template <int DL, bool SAMPLE>
 __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) void pf_gather(PfArgs a) {
   constexpr int KS = DL / 16;
