@@ -150,7 +150,8 @@ def graph_replay(step, steps, qheads):
 def cpu_baseline(wl, keys, W, queries, pos):
     """The CPU oracle, untuned, on KV head 0 of the workload: its index build
     (reported, not in the value) and the selection of that head's G query
-    heads for every token (sampled to at most 64 query heads)."""
+    heads for every token (sampled to at most 64 query heads), repeated
+    until about ten seconds of selection have been timed."""
     import numpy as np
     from oracle import lsa_oracle as O
     try:
@@ -167,14 +168,19 @@ def cpu_baseline(wl, keys, W, queries, pos):
     if len(pairs) > 64:
         rng = np.random.default_rng(0)
         pairs = [pairs[i] for i in sorted(rng.choice(len(pairs), 64, replace=False))]
-    t = time.perf_counter()
-    O.select(oidx, queries, pos, prm, pairs=pairs)
-    sel_s = time.perf_counter() - t
+    # the same selection is repeated until it has run for about ten seconds
+    reps, sel_s = 0, 0.0
+    while sel_s < 10.0:
+        t = time.perf_counter()
+        O.select(oidx, queries, pos, prm, pairs=pairs)
+        sel_s += time.perf_counter() - t
+        reps += 1
     return {
-        "value": len(pairs) / sel_s, "unit": "query-heads/s", "cores": blas_threads, "kind": "oracle",
-        "sample": (f"KV head 0 of {wl.name} (N={wl.n_keys}): oracle select of {len(pairs)} query heads "
-                   f"in {sel_s:.2f} s on the oracle's own index of that head (index build {build_s:.1f} s, "
-                   f"not in the value); float64 numpy, BLAS threads={blas_threads}, host cpus={os.cpu_count()}"),
+        "value": reps * len(pairs) / sel_s, "unit": "query-heads/s", "cores": blas_threads, "kind": "oracle",
+        "sample": (f"KV head 0 of {wl.name} (N={wl.n_keys}): oracle select of {len(pairs)} query heads, "
+                   f"{reps} times in {sel_s:.1f} s, on the oracle's own index of that head (index build "
+                   f"{build_s:.1f} s, not in the value); float64 numpy, BLAS threads={blas_threads}, "
+                   f"host cpus={os.cpu_count()}"),
         "build_s_one_head": build_s,
     }
 
