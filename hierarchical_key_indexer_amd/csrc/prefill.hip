@@ -475,6 +475,50 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       enext = entry_of(cc, ii);
     }
   }
+  // Staged entries -> the rows' append lists: per-row counts in LDS, one
+  // global atomic per row reserves their places.  A flush is split so that
+  // the atomics' round trip overlaps the next item's loads: flush_start (the
+  // counts, the atomics issued, not awaited) ends an item, flush_finish (the
+  // writes) runs in the next item once its loads are issued.  Until then the
+  // staging buffers and row slots keep the finished item's entries.
+  int pcnt = 0;                                    // entries of the pending flush (wave-uniform)
+  uint32_t plp[SE];                                // their places among their row's entries
+  uint32_t pc = 0u, graw = 0u;                     // this lane's row: its entries, the reserved base
+  auto flush_start = [&](int cnt, int row) {
+    if (half == 0) scnt[w][l32] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < SE; ++q) {
+      const int e = lane + 64 * q;
+      plp[q] = e < cnt ? atomicAdd(&scnt[w][srl[w][e]], 1u) : 0u;
+    }
+    wave_lds_sync();
+    pc = half == 0 ? scnt[w][l32] : 0u;
+    // a lane with nothing to reserve leaves its value undefined (it is not
+    // read), so no merge with an older value has to wait for the atomic
+    uint32_t got;
+    if (pc != 0u) got = atomicAdd(pf_count_of(a, row), pc);
+    graw = got;
+    pcnt = cnt;
+  };
+  auto flush_finish = [&]() {
+    if (half == 0) scnt[w][l32] = pc != 0u ? graw : 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < SE; ++q) {
+      const int e = lane + 64 * q;
+      if (e < pcnt) {
+        const int rl = srl[w][e];
+        const uint32_t pos = scnt[w][rl] + plp[q];
+        if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)srow[w][rl] * a.cap + pos] = skey[w][e];
+      }
+    }
+    wave_lds_sync();
+    pcnt = 0;
+  };
+  // the first entry is in before the loop, so at the top of an item only
+  // the previous item's atomics can be outstanding
+  __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0) only
   for (int it = ch * kPfNW + w; it < items; it += stride) {
     int c, i;
     item_of(it, &c, &i);
@@ -597,35 +641,14 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     int chimin = row >= 0 ? chi : INT_MAX;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) chimin = min(chimin, __shfl_xor(chimin, o, 64));
+    // the previous item's appends, now that this item's loads are in flight;
+    // then this item's rows take the row slots
+    if (pcnt > 0) flush_finish();
     if (half == 0) srow[w][l32] = row;
     int cnt = 0;                                   // staged entries (wave-uniform)
-    // staged entries -> the rows' append lists: per-row counts in LDS, one
-    // global atomic per row reserves their places
     auto flush = [&]() {
-      if (half == 0) scnt[w][l32] = 0u;
-      wave_lds_sync();
-      uint32_t lp[SE];
-#pragma unroll
-      for (int q = 0; q < SE; ++q) {
-        const int e = lane + 64 * q;
-        lp[q] = e < cnt ? atomicAdd(&scnt[w][srl[w][e]], 1u) : 0u;
-      }
-      wave_lds_sync();
-      if (half == 0) {
-        const uint32_t c = scnt[w][l32];
-        scnt[w][l32] = c != 0u ? atomicAdd(pf_count_of(a, row), c) : 0u;
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int q = 0; q < SE; ++q) {
-        const int e = lane + 64 * q;
-        if (e < cnt) {
-          const int rl = srl[w][e];
-          const uint32_t pos = scnt[w][rl] + lp[q];
-          if (pos < (uint32_t)a.cap) a.s.part_keys[(size_t)srow[w][rl] * a.cap + pos] = skey[w][e];
-        }
-      }
-      wave_lds_sync();
+      flush_start(cnt, row);
+      flush_finish();
       cnt = 0;
     };
     int jrn = 0;
@@ -688,8 +711,14 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
         }
       }
     }
-    if (cnt > 0) flush();
+    // Everything this item issued (the next item's entry among it) is
+    // complete before the atomics go out: the next item's loads then wait
+    // for nothing, and the atomics' results, awaited in order behind no
+    // other access, stay in flight under those loads.
+    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0) only
+    if (cnt > 0) flush_start(cnt, row);             // finished in the next item
   }
+  if (pcnt > 0) flush_finish();
 }
 
 // ---------------------------------------------------------------------------
