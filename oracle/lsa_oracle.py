@@ -222,6 +222,61 @@ def lloyd_objective(x: np.ndarray, cent: np.ndarray, a: np.ndarray) -> float:
 
 
 # ----------------------------------------------------------------------------
+# training-free latent map (PCA)
+# ----------------------------------------------------------------------------
+# [WPN] "How does LSA work?" lists, next to the distilled map, a training-free
+# option that builds the latent map from a PCA.  The page gives no detail; the
+# plainest reading: per KV head, the d_l leading eigenvectors of the keys'
+# (mean-centred) covariance are the columns of W_h.  Centring does not change
+# a ranking by q~ . k~ (it shifts every key's score of one query by the same
+# amount).  Eigenvalues are reported in descending order; each eigenvector is
+# signed so that its entry of largest magnitude (lowest index on a tie) is
+# positive.
+
+
+def key_covariance(keys: np.ndarray, key_dtype: str) -> np.ndarray:
+    """Per KV head the covariance (1/N) sum_j (k_j - mean)(k_j - mean)^T of the
+    keys [N, Hkv, d_head], in float64: [Hkv, d_head, d_head]."""
+    x = stored_to_f64(keys, key_dtype)
+    n, hk, d = x.shape
+    out = np.empty((hk, d, d))
+    for h in range(hk):
+        xc = x[:, h, :] - x[:, h, :].mean(axis=0)
+        out[h] = xc.T @ xc / n
+    return out
+
+
+def sign_fix(v: np.ndarray) -> np.ndarray:
+    """Columns of v signed so the entry of largest magnitude (lowest row on a
+    tie) is positive."""
+    v = v.copy()
+    for c in range(v.shape[1]):
+        r = int(np.argmax(np.abs(v[:, c])))
+        if v[r, c] < 0:
+            v[:, c] = -v[:, c]
+    return v
+
+
+def pca_from_covariance(cov: np.ndarray, d_latent: int):
+    """W [Hkv, d_head, d_latent] float64 (leading eigenvectors as columns) and
+    their eigenvalues [Hkv, d_latent], descending."""
+    hk, d, _ = cov.shape
+    W = np.empty((hk, d, d_latent))
+    lam = np.empty((hk, d_latent))
+    for h in range(hk):
+        w, v = np.linalg.eigh(cov[h])           # ascending
+        order = np.argsort(-w, kind="stable")[:d_latent]
+        lam[h] = w[order]
+        W[h] = sign_fix(v[:, order])
+    return W, lam
+
+
+def pca_map(keys: np.ndarray, key_dtype: str, d_latent: int):
+    """The training-free latent map of the keys: (W, eigenvalues)."""
+    return pca_from_covariance(key_covariance(keys, key_dtype), d_latent)
+
+
+# ----------------------------------------------------------------------------
 # the index
 # ----------------------------------------------------------------------------
 
