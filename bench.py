@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer query-heads/s and keys-scored/s at 1M/10M keys; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3                 # fp32 vector FMA: 256 CUs x 128 FMA/clk x 2 x 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_key_indexer_amd", "csrc", f)
                   for f in ("select.hip", "select_device.h", "prefill.hip", "lsa_device.h")]
@@ -185,6 +186,35 @@ def cpu_baseline(wl, keys, W, queries, pos):
     }
 
 
+def pca_leg(abi, desc, kd, reps=3):
+    """The training-free latent map of the workload's keys: the device
+    covariance (two kernels, timed with events on the stream they run on) and
+    the host eigenvectors."""
+    import numpy as np
+    import torch
+    d, hk = desc.d_head, desc.n_kv_heads
+    cov = torch.empty((hk, d, d), dtype=torch.float64, device="cuda")
+    ws = torch.empty(abi.pca_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    abi.lsa_pca_covariance(desc, kd, cov, ws)      # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        abi.lsa_pca_covariance(desc, kd, cov, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    cov_ms = e0.elapsed_time(e1) / reps
+    c = cov.cpu().numpy()
+    t = time.perf_counter()
+    W, lam = abi.lsa_pca_map(desc, c)
+    eig_ms = (time.perf_counter() - t) * 1e3
+    flops = 2.0 * desc.n_keys * hk * d * d          # every product of the d x d sums
+    return {"covariance_ms": cov_ms, "eigensolve_ms": eig_ms, "kernels": "pca_gram_kernel + pca_reduce_kernel",
+            "bound": "alu", "algorithmic_flops": flops, "achieved_TFLOPs": flops / (cov_ms * 1e-3) / 1e12,
+            "peak_TFLOPs": FP32_PEAK_TFLOPS, "frac": flops / (cov_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS,
+            "variance_kept": float(lam.sum() / np.trace(c, axis1=1, axis2=2).sum())}
+
+
 def recall_rows(tree_out, flat_out, sink, k):
     """Per query head |tree top-k & flat top-k| / |flat top-k|, computed on
     the device from the two output tensors [T, Hq, width]."""
@@ -208,6 +238,7 @@ def main():
     ap.add_argument("--flat-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat", action="store_true")
+    ap.add_argument("--no-pca", action="store_true", help="skip the training-free latent map leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -247,6 +278,11 @@ def main():
     build_ms = e0.elapsed_time(e1)
     li.release_build_workspace()
     log(f"index build {build_ms:.1f} ms")
+    pca = None
+    if not args.no_pca:
+        pca = pca_leg(_abi, desc, kd)
+        log(f"training-free latent map: covariance {pca['covariance_ms']:.2f} ms, "
+            f"eigenvectors {pca['eigensolve_ms']:.0f} ms on the host")
 
     prm = _abi.SelectParams.make(wl.b, wl.k, wl.sink, wl.window)
     out = li.alloc_select_outputs(wl.n_tokens, wl.n_q_heads, prm, scores=True, leaves=True)
@@ -399,6 +435,9 @@ def main():
         }
         result["recall_at_k_vs_flat"] = {"mean": float(np.mean(rec)), "p5": float(np.percentile(rec, 5))}
         result["speedup_vs_flat"] = flat_ms / ms_step
+
+    if pca is not None:
+        result["pca_map"] = pca
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

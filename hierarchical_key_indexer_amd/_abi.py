@@ -21,7 +21,7 @@ BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
 EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
            "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
-           "lsa_set_profile_events")
+           "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map")
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
 PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
 
@@ -89,6 +89,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_last_error.argtypes, lib.lsa_last_error.restype = [], ctypes.c_char_p
     lib.lsa_abi_version.argtypes, lib.lsa_abi_version.restype = [], I32
     lib.lsa_set_profile_events.argtypes, lib.lsa_set_profile_events.restype = [I32, VP, VP], ctypes.c_int
+    lib.lsa_pca_workspace_bytes.argtypes, lib.lsa_pca_workspace_bytes.restype = [D], SZ
+    lib.lsa_pca_covariance.argtypes = [D, VP, VP, VP, SZ, VP]
+    lib.lsa_pca_covariance.restype = ctypes.c_int
+    lib.lsa_pca_map.argtypes = [D, VP, VP, VP]
+    lib.lsa_pca_map.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -189,6 +194,35 @@ def lsa_flat_select(desc, index, queries, q_pos, params, out_idx, out_scores=Non
     _check(load().lsa_flat_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
                                   ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(workspace),
                                   0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+# ---- training-free latent map ----------------------------------------------------
+
+def pca_workspace_bytes(desc: IndexDesc) -> int:
+    n = load().lsa_pca_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def lsa_pca_covariance(desc, keys, cov, workspace, stream=None) -> None:
+    """keys [N, Hkv, d] (fp32 or bf16) and cov [Hkv, d, d] float64 on the GPU;
+    workspace a uint8 GPU tensor of pca_workspace_bytes(desc) bytes."""
+    _check(load().lsa_pca_covariance(ctypes.byref(desc), _ptr(keys), _ptr(cov), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
+
+
+def lsa_pca_map(desc, cov):
+    """Host: cov [Hkv, d, d] float64 (numpy) -> (W [Hkv, d, d_latent] float32,
+    eigenvalues [Hkv, d_latent] float64)."""
+    import numpy as np
+    cov = np.ascontiguousarray(cov, dtype=np.float64)
+    hk, d, dl = desc.n_kv_heads, desc.d_head, desc.d_latent
+    assert cov.shape == (hk, d, d), cov.shape
+    W = np.empty((hk, d, dl), dtype=np.float32)
+    lam = np.empty((hk, dl), dtype=np.float64)
+    _check(load().lsa_pca_map(ctypes.byref(desc), cov.ctypes.data, W.ctypes.data, lam.ctypes.data))
+    return W, lam
 
 
 def set_profile_events(stage: int, start, stop) -> None:

@@ -222,4 +222,34 @@ int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* q
                        workspace, workspace_bytes, stream, true);
 }
 
+size_t lsa_pca_workspace_bytes(const lsa_index_desc* desc) {
+  clear_err();
+  if (check_desc(desc) != LSA_OK) return 0;
+  return lsa::pca_workspace_bytes(*desc);
+}
+
+int lsa_pca_covariance(const lsa_index_desc* desc, const void* keys, double* cov, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc != LSA_OK) return rc;
+  if (!keys || !cov || !workspace) return fail(LSA_ERR_INVALID_ARG, "keys, cov and workspace must be non-NULL");
+  const size_t need = lsa::pca_workspace_bytes(*desc);
+  if (workspace_bytes < need)
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  char err[256] = {0};
+  rc = lsa::launch_pca_covariance(*desc, keys, cov, workspace, (hipStream_t)stream, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
+int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double* eigenvalues) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc != LSA_OK) return rc;
+  if (!cov || !W) return fail(LSA_ERR_INVALID_ARG, "cov and W must be non-NULL");
+  lsa::pca_map_host(*desc, cov, W, eigenvalues);
+  return LSA_OK;
+}
+
 }  // extern "C"

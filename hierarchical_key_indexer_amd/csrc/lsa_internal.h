@@ -74,6 +74,12 @@ size_t build_workspace_bytes(const lsa_index_desc& d);
 int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void* index, void* ws,
                  hipStream_t stream, char* err, size_t errlen);
 
+// ---- training-free latent map (pca.hip) ---------------------------------------
+size_t pca_workspace_bytes(const lsa_index_desc& d);
+int launch_pca_covariance(const lsa_index_desc& d, const void* keys, double* cov, void* ws, hipStream_t stream,
+                          char* err, size_t errlen);
+void pca_map_host(const lsa_index_desc& d, const double* cov, float* W, double* eig);
+
 // ---- instrumentation ---------------------------------------------------------
 void prof_begin(int stage, hipStream_t st);
 void prof_end(int stage, hipStream_t st);

@@ -216,6 +216,41 @@ int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* q
                     const lsa_select_params* params, int32_t* out_idx, float* out_scores,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- training-free latent map ------------------------------------------------
+ * "Latent Sparse Attention (LSA): The 72.4x and 22.7x Speedups, and What They
+ * Compare Against", section "How does LSA work?", lists a PCA map as the option
+ * that needs no training.  Reading: for every KV head h, the d_latent leading
+ * eigenvectors of the covariance of the keys of h (mean-centred, divided by N)
+ * are the columns of W_h, in descending order of eigenvalue, each signed so
+ * that its entry of largest magnitude (the lowest row on a tie) is positive.
+ * The result is the W that lsa_build_index takes.  Two calls: the covariance on
+ * the device, then the eigenvectors on the host (the caller copies the
+ * covariance to host memory in between). */
+
+/* Bytes of device workspace lsa_pca_covariance needs; 0 if the descriptor is
+ * invalid.  Only n_keys, n_kv_heads, d_head and key_dtype matter. */
+size_t lsa_pca_workspace_bytes(const lsa_index_desc* desc);
+
+/* Per KV head the key covariance, into cov: DEVICE float64 [Hkv][d_head][d_head],
+ * row-major, caller-owned.  keys: DEVICE [N][Hkv][d_head] of desc->key_dtype.
+ * Sums of products are fp32 over chunks of at most max(4096, N / 256) keys of
+ * one head (each key shifted by the head's first key), chunks are added in
+ * fp64.  Asynchronous on `stream`; the workspace is scratch for the call.
+ * Errors: LSA_ERR_INVALID_ARG (NULL pointer), LSA_ERR_UNSUPPORTED (descriptor),
+ * LSA_ERR_BUFFER_TOO_SMALL, LSA_ERR_HIP (launch); nothing is enqueued on a
+ * validation error. */
+int lsa_pca_covariance(const lsa_index_desc* desc, const void* keys, double* cov, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* The latent map from a covariance, on the host: cov HOST float64
+ * [Hkv][d_head][d_head] (as lsa_pca_covariance writes it; it is symmetrised
+ * first), W HOST fp32 [Hkv][d_head][d_latent] (out), eigenvalues HOST float64
+ * [Hkv][d_latent] (out, descending; NULL to skip).  Eigenvectors come from
+ * cyclic Jacobi rotations in float64.  Synchronous; touches no device.
+ * Errors: LSA_ERR_INVALID_ARG (NULL cov or W), LSA_ERR_UNSUPPORTED
+ * (descriptor). */
+int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double* eigenvalues);
+
 /* Stages of a select call that can be timed by the caller. */
 typedef enum {
   LSA_STAGE_PROJECT = 1, /* query latent projection                         */
