@@ -662,4 +662,34 @@ def dot_scale(qlat: np.ndarray, klat: np.ndarray) -> np.ndarray:
     score tolerances relative to it."""
     return np.abs(klat) @ np.abs(qlat)
 
+# ----------------------------------------------------------------------------
+# exact sparse attention over the selected keys
+# ----------------------------------------------------------------------------
+# [WPN] "How does LSA work?", step 3: the query attends to the selected
+# long-range keys plus the attention sink and the local window, and the
+# attention kernel itself is unchanged.  So the step after the indexer is
+# ordinary softmax attention restricted to the row's listed keys:
+#   out = sum_j softmax_j(scale * q . k_j) v_j  over the entries j >= 0 of the
+# row (an entry listed twice counts twice; a row with no entry gives zeros).
 
+
+def sparse_attention(queries: np.ndarray, keys: np.ndarray, values: np.ndarray, idx: np.ndarray,
+                     key_dtype: str, scale: float) -> np.ndarray:
+    """queries [T, Hq, d], keys / values [N, Hkv, d] (stored, key_dtype), idx
+    [T, Hq, width] int -> out [T, Hq, d] float64."""
+    q = stored_to_f64(queries, key_dtype)
+    k = stored_to_f64(keys, key_dtype)
+    v = stored_to_f64(values, key_dtype)
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros((T, Hq, d))
+    for t in range(T):
+        for hq in range(Hq):
+            h = hq // G
+            sel = idx[t, hq][idx[t, hq] >= 0]
+            if sel.size == 0:
+                continue
+            s = scale * (k[sel, h, :] @ q[t, hq])
+            w = np.exp(s - s.max())
+            out[t, hq] = (w / w.sum()) @ v[sel, h, :]
+    return out
