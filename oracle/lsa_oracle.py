@@ -669,8 +669,9 @@ def dot_scale(qlat: np.ndarray, klat: np.ndarray) -> np.ndarray:
 # long-range keys plus the attention sink and the local window, and the
 # attention kernel itself is unchanged.  So the step after the indexer is
 # ordinary softmax attention restricted to the row's listed keys:
-#   out = sum_j softmax_j(scale * q . k_j) v_j  over the entries j >= 0 of the
-# row (an entry listed twice counts twice; a row with no entry gives zeros).
+#   out = sum_j softmax_j(scale * q . k_j) v_j  over the entries j of the row
+# that name a key, i.e. lie in [0, N) (anything else is padding; an entry
+# listed twice counts twice; a row with no key gives zeros).
 
 
 def sparse_attention(queries: np.ndarray, keys: np.ndarray, values: np.ndarray, idx: np.ndarray,
@@ -686,7 +687,8 @@ def sparse_attention(queries: np.ndarray, keys: np.ndarray, values: np.ndarray, 
     for t in range(T):
         for hq in range(Hq):
             h = hq // G
-            sel = idx[t, hq][idx[t, hq] >= 0]
+            r = idx[t, hq]
+            sel = r[(r >= 0) & (r < k.shape[0])]
             if sel.size == 0:
                 continue
             s = scale * (k[sel, h, :] @ q[t, hq])

@@ -40,6 +40,14 @@ def test_zero_scale_is_the_mean_and_padding_is_ignored():
     assert np.allclose(out[0, 0], v[sel, 0, :].astype(np.float64).mean(0), atol=1e-15)
 
 
+def test_entries_outside_the_cache_are_padding():
+    k = _f32([[[1.0]], [[2.0]]])
+    v = _f32([[[3.0]], [[4.0]]])
+    q = _f32([[[0.0]]])
+    out = O.sparse_attention(q, k, v, np.array([[[1, 2, 7, -5]]]), "f32", 1.0)
+    assert np.array_equal(out[0, 0], [4.0])
+
+
 def test_empty_row_gives_zeros_and_gqa_reads_its_kv_head():
     # two KV heads, G = 2: query heads 2 and 3 read KV head 1
     k = _f32(np.zeros((3, 2, 2)))
