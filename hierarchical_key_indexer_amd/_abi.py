@@ -21,7 +21,8 @@ BEAMS = {"per_parent": LSA_BEAM_PER_PARENT, "global": LSA_BEAM_GLOBAL}
 EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "lsa_select_out_width",
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
            "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
-           "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map")
+           "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map",
+           "lsa_sparse_attention")
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
 PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
 
@@ -94,6 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_pca_covariance.restype = ctypes.c_int
     lib.lsa_pca_map.argtypes = [D, VP, VP, VP]
     lib.lsa_pca_map.restype = ctypes.c_int
+    lib.lsa_sparse_attention.argtypes = [D, VP, VP, VP, VP, I32, I32, I32, ctypes.c_float, VP, VP]
+    lib.lsa_sparse_attention.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -223,6 +226,16 @@ def lsa_pca_map(desc, cov):
     lam = np.empty((hk, dl), dtype=np.float64)
     _check(load().lsa_pca_map(ctypes.byref(desc), cov.ctypes.data, W.ctypes.data, lam.ctypes.data))
     return W, lam
+
+
+# ---- exact sparse attention ----------------------------------------------------------
+
+def lsa_sparse_attention(desc, queries, keys, values, idx, scale, out, stream=None) -> None:
+    """queries [T, Hq, d], keys / values [N, Hkv, d] (key dtype), idx [T, Hq,
+    width] int32, out [T, Hq, d] float32, all on the GPU."""
+    t, hq, width = idx.shape
+    _check(load().lsa_sparse_attention(ctypes.byref(desc), _ptr(queries), _ptr(keys), _ptr(values), _ptr(idx),
+                                       width, t, hq, float(scale), _ptr(out), _stream(stream)))
 
 
 def set_profile_events(stage: int, start, stop) -> None:

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblsa.so")
-SOURCES = ["api.hip", "build.hip", "select.hip", "prefill.hip", "pca.hip"]
+SOURCES = ["api.hip", "build.hip", "select.hip", "prefill.hip", "pca.hip", "attention.hip"]
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

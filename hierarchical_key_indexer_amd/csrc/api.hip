@@ -252,4 +252,24 @@ int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double*
   return LSA_OK;
 }
 
+int lsa_sparse_attention(const lsa_index_desc* desc, const void* queries, const void* keys, const void* values,
+                         const int32_t* idx, int32_t width, int32_t n_tokens, int32_t n_q_heads, float scale,
+                         float* out, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc != LSA_OK) return rc;
+  rc = check_shape(desc, n_tokens, n_q_heads, false);
+  if (rc != LSA_OK) return rc;
+  if (!queries || !keys || !values || !idx || !out)
+    return fail(LSA_ERR_INVALID_ARG, "queries, keys, values, idx and out must be non-NULL");
+  if (width < 1 || width > lsa::kMaxAttWidth)
+    return fail(LSA_ERR_UNSUPPORTED, "width = %d outside [1, %d]", width, lsa::kMaxAttWidth);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(LSA_ERR_INVALID_ARG, "scale is not finite");
+  char err[256] = {0};
+  rc = lsa::launch_sparse_attention(*desc, queries, keys, values, idx, width, n_tokens, n_q_heads, scale, out,
+                                    (hipStream_t)stream, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
 }  // extern "C"

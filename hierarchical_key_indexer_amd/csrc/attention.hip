@@ -1,0 +1,212 @@
+// Exact sparse attention over the selected keys.  The page "Latent Sparse
+// Attention (LSA): The 72.4x and 22.7x Speedups, and What They Compare
+// Against" (section "How does LSA work?", step 3) has the query attend to the
+// selected long-range keys plus the attention sink and the local window, with
+// the attention itself unchanged: softmax attention restricted to the keys
+// that an lsa_select row lists,
+//   out = sum_j softmax_j(scale * q . k_j) v_j   over the entries j >= 0,
+// an entry listed twice counting twice, an entry outside [0, N) counting as
+// padding and a row with no key giving zeros.
+//
+// One workgroup per (token, query head).  Pass 1 scores the listed keys: LPK
+// lanes read a key row with 16-byte loads (a load instruction covers KPW whole
+// rows, four instructions in flight per lane) and reduce their partial dots;
+// the scores go to LDS.  The row's maximum and the exponentials follow in LDS.
+// Pass 2 reads the value rows the same way: a group of lanes owns one value
+// row at a time and accumulates p_j v_j for its slice of the dims; the groups'
+// partial outputs are added in LDS.  Everything is fp32 (keys, queries and
+// values widened from their stored format).
+#include <math.h>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace {
+
+constexpr int kAttBlock = 256;
+constexpr int kAttNW = kAttBlock / 64;
+constexpr int kAttU = 4;                     // key rows in flight per lane in pass 1
+
+template <typename KT>
+struct Row16;
+template <>
+struct Row16<float> {
+  static constexpr int E = 4;                 // elements per 16 bytes
+  __device__ static __forceinline__ void widen(const uint4& u, float* x) {
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
+  }
+};
+template <>
+struct Row16<bf16_t> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void widen(const uint4& u, float* x) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <int G>
+__device__ __forceinline__ float group_sum_all(float v) {   // every lane of the aligned group of G
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kAttNW; ++i) m = fmaxf(m, red[i]);
+  __syncthreads();
+  return m;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAttNW; ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+
+template <typename KT, int D>
+__global__ __launch_bounds__(kAttBlock) void sparse_attention_kernel(const KT* queries, const KT* keys,
+                                                                     const KT* values, const int32_t* idx,
+                                                                     int64_t N, int width, int Hq, int Hkv,
+                                                                     float scale, float* out) {
+  constexpr int E = Row16<KT>::E;
+  constexpr int LPK = D / E;                  // lanes per row
+  constexpr int KPW = 64 / LPK;               // rows per wave and load instruction
+  constexpr int NG = kAttBlock / LPK;         // row groups of the block in pass 2
+  extern __shared__ __align__(16) float sm[];
+  float* s = sm;                              // [width] scores, then weights
+  float* po = sm + ((width + 3) & ~3);        // [NG][D] partial outputs
+  __shared__ float red[kAttNW];
+  const int64_t row = blockIdx.x;
+  const int hq = (int)(row % Hq), h = hq / (Hq / Hkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lig = lane % LPK, g = lane / LPK;
+  const int32_t* ir = idx + row * width;
+  // this lane's slice of the query
+  float qv[E];
+  Row16<KT>::widen(*(const uint4*)(queries + row * D + lig * E), qv);
+  const size_t rstride = (size_t)Hkv * D;
+  const KT* kb = keys + (size_t)h * D + lig * E;
+  const KT* vb = values + (size_t)h * D;
+  // pass 1: scores (-inf for a padding entry)
+  for (int j0 = w * KPW; j0 < width; j0 += kAttNW * KPW * kAttU) {
+    int id[kAttU];
+    uint4 kr[kAttU];
+#pragma unroll
+    for (int u = 0; u < kAttU; ++u) {
+      const int j = j0 + u * kAttNW * KPW + g;
+      const int x = j < width ? ir[j] : -1;
+      id[u] = (x >= 0 && (int64_t)x < N) ? x : -1;   // outside [0, N): padding
+    }
+#pragma unroll
+    for (int u = 0; u < kAttU; ++u)     // a padding entry reads row 0 (dropped)
+      kr[u] = *(const uint4*)(kb + (size_t)(id[u] >= 0 ? id[u] : 0) * rstride);
+#pragma unroll
+    for (int u = 0; u < kAttU; ++u) {
+      float x[E];
+      Row16<KT>::widen(kr[u], x);
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) p = fmaf(qv[e], x[e], p);
+      p = group_sum_all<LPK>(p);
+      const int j = j0 + u * kAttNW * KPW + g;
+      if (lig == 0 && j < width) s[j] = id[u] >= 0 ? scale * p : -__builtin_huge_valf();
+    }
+  }
+  __syncthreads();
+  float m = -__builtin_huge_valf();
+  for (int j = threadIdx.x; j < width; j += kAttBlock) m = fmaxf(m, s[j]);
+  m = block_max(m, red);
+  float z = 0.f;
+  for (int j = threadIdx.x; j < width; j += kAttBlock) {
+    const float p = s[j] == -__builtin_huge_valf() ? 0.f : expf(s[j] - m);
+    s[j] = p;
+    z += p;
+  }
+  z = block_sum(z, red);                      // its barriers publish s
+  // pass 2: group gr of LPK lanes owns rows gr, gr + NG, ...; lane lig owns
+  // dims [lig * E, lig * E + E)
+  const int gr = threadIdx.x / LPK;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int j = gr; j < width; j += NG) {
+    const float p = s[j];
+    if (p == 0.f) continue;
+    float x[E];
+    Row16<KT>::widen(*(const uint4*)(vb + (size_t)ir[j] * rstride + lig * E), x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(p, x[e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) po[gr * D + lig * E + e] = acc[e];
+  __syncthreads();
+  float* o = out + row * D;
+  for (int i = threadIdx.x; i < D; i += kAttBlock) {
+    float t = 0.f;
+    for (int q = 0; q < NG; ++q) t += po[q * D + i];
+    o[i] = z > 0.f ? t / z : 0.f;
+  }
+}
+
+template <typename KT, int D>
+int launch_att(const void* q, const void* k, const void* v, const int32_t* idx, int64_t N, int width, int64_t rows,
+               int Hq, int Hkv, float scale, float* out, hipStream_t st, char* err, size_t errlen) {
+  constexpr int E = Row16<KT>::E;
+  constexpr int NG = kAttBlock / (D / E);
+  const size_t lds = (size_t)((width + 3) & ~3) * 4 + (size_t)NG * D * 4;
+  auto kern = sparse_attention_kernel<KT, D>;
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // rows <= 2^30 (validated), one workgroup per row
+  hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kAttBlock), lds, st, (const KT*)q, (const KT*)k, (const KT*)v,
+                     idx, N, width, Hq, Hkv, scale, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(err, errlen, "sparse_attention_kernel launch failed: %s", hipGetErrorString(e));
+    return LSA_ERR_HIP;
+  }
+  return LSA_OK;
+}
+
+}  // namespace
+
+int launch_sparse_attention(const lsa_index_desc& d, const void* q, const void* k, const void* v,
+                            const int32_t* idx, int32_t width, int32_t T, int32_t Hq, float scale, float* out,
+                            hipStream_t st, char* err, size_t errlen) {
+  const int64_t rows = (int64_t)T * Hq;
+  if (rows == 0) return LSA_OK;
+  const bool bf = d.key_dtype == LSA_BF16;
+  switch (d.d_head) {
+    case 64:
+      return bf ? launch_att<bf16_t, 64>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
+                : launch_att<float, 64>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
+    case 128:
+      return bf ? launch_att<bf16_t, 128>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
+                : launch_att<float, 128>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
+    default:
+      return bf ? launch_att<bf16_t, 256>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
+                : launch_att<float, 256>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
+  }
+}
+
+}  // namespace lsa

@@ -251,6 +251,28 @@ int lsa_pca_covariance(const lsa_index_desc* desc, const void* keys, double* cov
  * (descriptor). */
 int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double* eigenvalues);
 
+/* ---- exact sparse attention over the selected keys ------------------------------
+ * "Latent Sparse Attention (LSA): The 72.4x and 22.7x Speedups, and What They
+ * Compare Against", section "How does LSA work?", step 3: the query attends to
+ * the selected long-range keys plus the attention sink and the local window,
+ * with the attention itself unchanged.  For every (token t, query head hq):
+ *   out[t][hq] = sum_j softmax_j(scale * q . k_j) v_j
+ * over the entries j of row idx[t][hq] (an lsa_select output row, or any list);
+ * an entry outside [0, N) is padding, an entry listed twice counts twice, and a
+ * row with no key gives zeros.  Query head hq reads KV head hq / G.
+ *   queries  DEVICE [T][Hq][d_head], desc->key_dtype
+ *   keys     DEVICE [N][Hkv][d_head], desc->key_dtype (the KV cache's keys)
+ *   values   DEVICE [N][Hkv][d_head], desc->key_dtype (the KV cache's values)
+ *   idx      DEVICE int32 [T][Hq][width], 1 <= width <= 32768
+ *   out      DEVICE fp32 [T][Hq][d_head]
+ * Only n_keys, n_kv_heads, d_head and key_dtype of desc are used.  Scores,
+ * softmax and the weighted sum are fp32.  Asynchronous on `stream`; no
+ * workspace.  Errors: LSA_ERR_INVALID_ARG (NULL pointer, shape, scale not
+ * finite), LSA_ERR_UNSUPPORTED (descriptor, width), LSA_ERR_HIP (launch). */
+int lsa_sparse_attention(const lsa_index_desc* desc, const void* queries, const void* keys, const void* values,
+                         const int32_t* idx, int32_t width, int32_t n_tokens, int32_t n_q_heads, float scale,
+                         float* out, void* stream);
+
 /* Stages of a select call that can be timed by the caller. */
 typedef enum {
   LSA_STAGE_PROJECT = 1, /* query latent projection                         */
