@@ -215,6 +215,38 @@ def pca_leg(abi, desc, kd, reps=3):
             "variance_kept": float(lam.sum() / np.trace(c, axis1=1, axis2=2).sum())}
 
 
+def attention_leg(abi, desc, wl, qd, kd, idx, reps=20):
+    """Exact sparse attention over the rows a select call returned (the step
+    after the indexer): seeded bf16 values made on the device, keys and
+    queries of the workload, scale 1/sqrt(d); timed with events on the stream
+    it runs on.  Bytes: one key row and one value row per listed key."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261030)
+    vals = torch.randn(tuple(kd.shape), generator=g, device="cuda",
+                       dtype=torch.bfloat16 if wl.key_dtype == "bf16" else torch.float32)
+    T, Hq, width = idx.shape
+    out = torch.empty((T, Hq, desc.d_head), dtype=torch.float32, device="cuda")
+    scale = 1.0 / float(desc.d_head) ** 0.5
+    ws = torch.empty(max(abi.sparse_attention_workspace_bytes(desc, width, T, Hq), 1), dtype=torch.uint8,
+                     device="cuda")
+    abi.lsa_sparse_attention(desc, qd, kd, vals, idx, scale, out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        abi.lsa_sparse_attention(desc, qd, kd, vals, idx, scale, out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    listed = int(((idx >= 0) & (idx < desc.n_keys)).sum().item())
+    nbytes = listed * 2 * desc.d_head * (2 if wl.key_dtype == "bf16" else 4) + idx.numel() * 4
+    del vals
+    return {"ms_per_call": ms, "rows": T * Hq, "keys_per_row": listed / (T * Hq), "kernel": "sparse_attention_kernel",
+            "bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def recall_rows(tree_out, flat_out, sink, k):
     """Per query head |tree top-k & flat top-k| / |flat top-k|, computed on
     the device from the two output tensors [T, Hq, width]."""
@@ -239,6 +271,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-pca", action="store_true", help="skip the training-free latent map leg")
+    ap.add_argument("--no-attention", action="store_true", help="skip the sparse attention leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -438,6 +471,10 @@ def main():
 
     if pca is not None:
         result["pca_map"] = pca
+    if not args.no_attention:
+        log("exact sparse attention over the selected rows")
+        result["sparse_attention"] = attention_leg(_abi, desc, wl, qd, kd, out[0],
+                                                   reps=20 if wl.n_tokens == 1 else 2)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

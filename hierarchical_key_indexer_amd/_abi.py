@@ -22,7 +22,7 @@ EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "l
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
            "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
            "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map",
-           "lsa_sparse_attention")
+           "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention")
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
 PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
 
@@ -95,7 +95,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_pca_covariance.restype = ctypes.c_int
     lib.lsa_pca_map.argtypes = [D, VP, VP, VP]
     lib.lsa_pca_map.restype = ctypes.c_int
-    lib.lsa_sparse_attention.argtypes = [D, VP, VP, VP, VP, I32, I32, I32, ctypes.c_float, VP, VP]
+    lib.lsa_sparse_attention_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.lsa_sparse_attention_workspace_bytes.restype = SZ
+    lib.lsa_sparse_attention.argtypes = [D, VP, VP, VP, VP, I32, I32, I32, ctypes.c_float, VP, VP, SZ, VP]
     lib.lsa_sparse_attention.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -230,12 +232,22 @@ def lsa_pca_map(desc, cov):
 
 # ---- exact sparse attention ----------------------------------------------------------
 
-def lsa_sparse_attention(desc, queries, keys, values, idx, scale, out, stream=None) -> None:
+def sparse_attention_workspace_bytes(desc, width, n_tokens, n_q_heads) -> int:
+    return load().lsa_sparse_attention_workspace_bytes(ctypes.byref(desc), width, n_tokens, n_q_heads)
+
+
+def lsa_sparse_attention(desc, queries, keys, values, idx, scale, out, workspace=None, stream=None) -> None:
     """queries [T, Hq, d], keys / values [N, Hkv, d] (key dtype), idx [T, Hq,
-    width] int32, out [T, Hq, d] float32, all on the GPU."""
+    width] int32, out [T, Hq, d] float32, all on the GPU; workspace a uint8 GPU
+    tensor of sparse_attention_workspace_bytes bytes (allocated here if None)."""
     t, hq, width = idx.shape
+    if workspace is None:
+        import torch
+        n = sparse_attention_workspace_bytes(desc, width, t, hq)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=out.device)
     _check(load().lsa_sparse_attention(ctypes.byref(desc), _ptr(queries), _ptr(keys), _ptr(values), _ptr(idx),
-                                       width, t, hq, float(scale), _ptr(out), _stream(stream)))
+                                       width, t, hq, float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
 
 
 def set_profile_events(stage: int, start, stop) -> None:

@@ -252,9 +252,17 @@ int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double*
   return LSA_OK;
 }
 
+size_t lsa_sparse_attention_workspace_bytes(const lsa_index_desc* desc, int32_t width, int32_t n_tokens,
+                                            int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) != LSA_OK || check_shape(desc, n_tokens, n_q_heads, false) != LSA_OK) return 0;
+  if (width < 1 || width > lsa::kMaxAttWidth) return 0;
+  return lsa::attention_workspace_bytes(*desc, width, n_tokens, n_q_heads);
+}
+
 int lsa_sparse_attention(const lsa_index_desc* desc, const void* queries, const void* keys, const void* values,
                          const int32_t* idx, int32_t width, int32_t n_tokens, int32_t n_q_heads, float scale,
-                         float* out, void* stream) {
+                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
   clear_err();
   int rc = check_desc(desc);
   if (rc != LSA_OK) return rc;
@@ -265,9 +273,12 @@ int lsa_sparse_attention(const lsa_index_desc* desc, const void* queries, const 
   if (width < 1 || width > lsa::kMaxAttWidth)
     return fail(LSA_ERR_UNSUPPORTED, "width = %d outside [1, %d]", width, lsa::kMaxAttWidth);
   if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return fail(LSA_ERR_INVALID_ARG, "scale is not finite");
+  const size_t need = lsa::attention_workspace_bytes(*desc, width, n_tokens, n_q_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
   char err[256] = {0};
   rc = lsa::launch_sparse_attention(*desc, queries, keys, values, idx, width, n_tokens, n_q_heads, scale, out,
-                                    (hipStream_t)stream, err, sizeof(err));
+                                    workspace, (hipStream_t)stream, err, sizeof(err));
   if (rc != LSA_OK) return fail(rc, "%s", err);
   return LSA_OK;
 }

@@ -16,6 +16,12 @@
 // row at a time and accumulates p_j v_j for its slice of the dims; the groups'
 // partial outputs are added in LDS.  Everything is fp32 (keys, queries and
 // values widened from their stored format).
+//
+// Few rows (decode) would leave most of the chip idle, so a row's entries are
+// then split over S workgroups.  Each writes its partial result (maximum
+// score m_s, sum of exp(s_j - m_s), and the unnormalised weighted sum of
+// values) to the workspace, and attention_combine_kernel rescales the parts to
+// the common maximum M: out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) z_s.
 #include <math.h>
 
 #include "lsa_device.h"
@@ -88,20 +94,24 @@ template <typename KT, int D>
 __global__ __launch_bounds__(kAttBlock) void sparse_attention_kernel(const KT* queries, const KT* keys,
                                                                      const KT* values, const int32_t* idx,
                                                                      int64_t N, int width, int Hq, int Hkv,
-                                                                     float scale, float* out) {
+                                                                     float scale, float* out, int split,
+                                                                     float* part) {
   constexpr int E = Row16<KT>::E;
   constexpr int LPK = D / E;                  // lanes per row
   constexpr int KPW = 64 / LPK;               // rows per wave and load instruction
   constexpr int NG = kAttBlock / LPK;         // row groups of the block in pass 2
   extern __shared__ __align__(16) float sm[];
-  float* s = sm;                              // [width] scores, then weights
-  float* po = sm + ((width + 3) & ~3);        // [NG][D] partial outputs
   __shared__ float red[kAttNW];
   const int64_t row = blockIdx.x;
+  const int sp = blockIdx.y;                  // this workgroup's share of the row
   const int hq = (int)(row % Hq), h = hq / (Hq / Hkv);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lig = lane % LPK, g = lane / LPK;
-  const int32_t* ir = idx + row * width;
+  const int jlo = (int)((int64_t)width * sp / split), jhi = (int)((int64_t)width * (sp + 1) / split);
+  const int32_t* ir = idx + row * width + jlo;
+  width = jhi - jlo;                          // from here on: this share of the row
+  float* s = sm;                              // [width] scores, then weights
+  float* po = sm + ((width + 3) & ~3);        // [NG][D] partial outputs
   // this lane's slice of the query
   float qv[E];
   Row16<KT>::widen(*(const uint4*)(queries + row * D + lig * E), qv);
@@ -161,28 +171,68 @@ __global__ __launch_bounds__(kAttBlock) void sparse_attention_kernel(const KT* q
 #pragma unroll
   for (int e = 0; e < E; ++e) po[gr * D + lig * E + e] = acc[e];
   __syncthreads();
-  float* o = out + row * D;
+  if (split == 1) {
+    float* o = out + row * D;
+    for (int i = threadIdx.x; i < D; i += kAttBlock) {
+      float t = 0.f;
+      for (int q = 0; q < NG; ++q) t += po[q * D + i];
+      o[i] = z > 0.f ? t / z : 0.f;
+    }
+    return;
+  }
+  float* pp = part + ((size_t)row * split + sp) * (D + 2);
   for (int i = threadIdx.x; i < D; i += kAttBlock) {
     float t = 0.f;
     for (int q = 0; q < NG; ++q) t += po[q * D + i];
-    o[i] = z > 0.f ? t / z : 0.f;
+    pp[i] = t;
+  }
+  if (threadIdx.x == 0) {
+    pp[D] = m;                                // -inf for a share with no key
+    pp[D + 1] = z;
+  }
+}
+
+// Parts of a row -> its output (see the file comment).
+template <int D>
+__global__ __launch_bounds__(kAttBlock) void attention_combine_kernel(const float* part, int split, float* out) {
+  const int64_t row = blockIdx.x;
+  const float* pr = part + (size_t)row * split * (D + 2);
+  float M = -__builtin_huge_valf();
+  for (int sp = 0; sp < split; ++sp) M = fmaxf(M, pr[(size_t)sp * (D + 2) + D]);
+  float Z = 0.f;
+  for (int sp = 0; sp < split; ++sp) {
+    const float ms = pr[(size_t)sp * (D + 2) + D];
+    if (ms != -__builtin_huge_valf()) Z += expf(ms - M) * pr[(size_t)sp * (D + 2) + D + 1];
+  }
+  for (int i = threadIdx.x; i < D; i += kAttBlock) {
+    float t = 0.f;
+    for (int sp = 0; sp < split; ++sp) {
+      const float ms = pr[(size_t)sp * (D + 2) + D];
+      if (ms != -__builtin_huge_valf()) t += expf(ms - M) * pr[(size_t)sp * (D + 2) + i];
+    }
+    out[row * D + i] = Z > 0.f ? t / Z : 0.f;
   }
 }
 
 template <typename KT, int D>
 int launch_att(const void* q, const void* k, const void* v, const int32_t* idx, int64_t N, int width, int64_t rows,
-               int Hq, int Hkv, float scale, float* out, hipStream_t st, char* err, size_t errlen) {
+               int Hq, int Hkv, float scale, float* out, int split, float* part, hipStream_t st, char* err,
+               size_t errlen) {
   constexpr int E = Row16<KT>::E;
   constexpr int NG = kAttBlock / (D / E);
-  const size_t lds = (size_t)((width + 3) & ~3) * 4 + (size_t)NG * D * 4;
+  const int wmax = (width + split - 1) / split;
+  const size_t lds = (size_t)((wmax + 3) & ~3) * 4 + (size_t)NG * D * 4;
   auto kern = sparse_attention_kernel<KT, D>;
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  // rows <= 2^30 (validated), one workgroup per row
-  hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kAttBlock), lds, st, (const KT*)q, (const KT*)k, (const KT*)v,
-                     idx, N, width, Hq, Hkv, scale, out);
+  // rows <= 2^30 (validated), split workgroups per row
+  hipLaunchKernelGGL(kern, dim3((unsigned)rows, (unsigned)split), dim3(kAttBlock), lds, st, (const KT*)q,
+                     (const KT*)k, (const KT*)v, idx, N, width, Hq, Hkv, scale, out, split, part);
+  if (split > 1)
+    hipLaunchKernelGGL(attention_combine_kernel<D>, dim3((unsigned)rows), dim3(kAttBlock), 0, st, (const float*)part,
+                       split, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    snprintf(err, errlen, "sparse_attention_kernel launch failed: %s", hipGetErrorString(e));
+    snprintf(err, errlen, "sparse attention launch failed: %s", hipGetErrorString(e));
     return LSA_ERR_HIP;
   }
   return LSA_OK;
@@ -190,23 +240,36 @@ int launch_att(const void* q, const void* k, const void* v, const int32_t* idx, 
 
 }  // namespace
 
+int attention_split(int64_t rows, int width) {
+  if (rows >= 768) return 1;
+  int64_t sp = (768 + rows - 1) / rows;               // one round of workgroups
+  const int64_t by_work = width / 64 > 1 ? width / 64 : 1;   // at least 64 entries each
+  sp = sp < by_work ? sp : by_work;
+  return (int)(sp < 1 ? 1 : (sp > 64 ? 64 : sp));
+}
+
+size_t attention_workspace_bytes(const lsa_index_desc& d, int32_t width, int32_t T, int32_t Hq) {
+  const int64_t rows = (int64_t)T * Hq;
+  const int sp = attention_split(rows, width);
+  return sp > 1 ? align_up((size_t)rows * sp * (d.d_head + 2) * 4) : 0;
+}
+
 int launch_sparse_attention(const lsa_index_desc& d, const void* q, const void* k, const void* v,
                             const int32_t* idx, int32_t width, int32_t T, int32_t Hq, float scale, float* out,
-                            hipStream_t st, char* err, size_t errlen) {
+                            void* ws, hipStream_t st, char* err, size_t errlen) {
   const int64_t rows = (int64_t)T * Hq;
   if (rows == 0) return LSA_OK;
+  const int sp = attention_split(rows, width);
+  float* part = (float*)ws;
   const bool bf = d.key_dtype == LSA_BF16;
+#define LSA_ATT(KT, D) \
+  launch_att<KT, D>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, sp, part, st, err, errlen)
   switch (d.d_head) {
-    case 64:
-      return bf ? launch_att<bf16_t, 64>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
-                : launch_att<float, 64>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
-    case 128:
-      return bf ? launch_att<bf16_t, 128>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
-                : launch_att<float, 128>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
-    default:
-      return bf ? launch_att<bf16_t, 256>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen)
-                : launch_att<float, 256>(q, k, v, idx, d.n_keys, width, rows, Hq, d.n_kv_heads, scale, out, st, err, errlen);
+    case 64: return bf ? LSA_ATT(bf16_t, 64) : LSA_ATT(float, 64);
+    case 128: return bf ? LSA_ATT(bf16_t, 128) : LSA_ATT(float, 128);
+    default: return bf ? LSA_ATT(bf16_t, 256) : LSA_ATT(float, 256);
   }
+#undef LSA_ATT
 }
 
 }  // namespace lsa

@@ -82,9 +82,10 @@ void pca_map_host(const lsa_index_desc& d, const double* cov, float* W, double* 
 
 // ---- exact sparse attention over the selected keys (attention.hip) --------------
 constexpr int kMaxAttWidth = 32768;
+size_t attention_workspace_bytes(const lsa_index_desc& d, int32_t width, int32_t T, int32_t Hq);
 int launch_sparse_attention(const lsa_index_desc& d, const void* q, const void* k, const void* v,
                             const int32_t* idx, int32_t width, int32_t T, int32_t Hq, float scale, float* out,
-                            hipStream_t stream, char* err, size_t errlen);
+                            void* ws, hipStream_t stream, char* err, size_t errlen);
 
 // ---- instrumentation ---------------------------------------------------------
 void prof_begin(int stage, hipStream_t st);

@@ -265,13 +265,19 @@ int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double*
  *   values   DEVICE [N][Hkv][d_head], desc->key_dtype (the KV cache's values)
  *   idx      DEVICE int32 [T][Hq][width], 1 <= width <= 32768
  *   out      DEVICE fp32 [T][Hq][d_head]
+ *   workspace DEVICE, lsa_sparse_attention_workspace_bytes bytes (0 for many
+ *            rows; few rows split each row over several workgroups, whose
+ *            partial results go here); scratch for the call
  * Only n_keys, n_kv_heads, d_head and key_dtype of desc are used.  Scores,
- * softmax and the weighted sum are fp32.  Asynchronous on `stream`; no
- * workspace.  Errors: LSA_ERR_INVALID_ARG (NULL pointer, shape, scale not
- * finite), LSA_ERR_UNSUPPORTED (descriptor, width), LSA_ERR_HIP (launch). */
+ * softmax and the weighted sum are fp32.  Asynchronous on `stream`.
+ * Errors: LSA_ERR_INVALID_ARG (NULL pointer, shape, scale not finite),
+ * LSA_ERR_UNSUPPORTED (descriptor, width), LSA_ERR_BUFFER_TOO_SMALL,
+ * LSA_ERR_HIP (launch); nothing is enqueued on a validation error. */
+size_t lsa_sparse_attention_workspace_bytes(const lsa_index_desc* desc, int32_t width, int32_t n_tokens,
+                                            int32_t n_q_heads);
 int lsa_sparse_attention(const lsa_index_desc* desc, const void* queries, const void* keys, const void* values,
                          const int32_t* idx, int32_t width, int32_t n_tokens, int32_t n_q_heads, float scale,
-                         float* out, void* stream);
+                         float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages of a select call that can be timed by the caller. */
 typedef enum {

@@ -3,8 +3,9 @@
 Tolerance, from the fp32 arithmetic: a score is a dot of d fp32 products, off
 by at most ds = (d + 2) u scale sum_i |q_i k_i| (u = 2^-24); the weights
 exp(s_j - max) are then off by a relative 2 ds + 4u, and the normalised sum by
-at most (4 max ds + (width + 16) u) sum_j w_j |v_j| per dim (w the oracle's
-weights; the (width + 16) u term covers the two-level fp32 sum of p_j v_j).
+at most (4 max ds + (width + 32) u) sum_j w_j |v_j| per dim (w the oracle's
+weights; the (width + 32) u term covers the fp32 sums of p_j v_j and, for a
+row split over workgroups, the rescaling of its parts).
 The test allows twice that, entry by entry."""
 import numpy as np
 import pytest
@@ -50,7 +51,7 @@ def _bound(q, k, v, idx, scale, G):
             w = np.exp(s - s.max())
             w /= w.sum()
             ds = (d + 2) * u * abs(scale) * (np.abs(k[sel, h]) @ np.abs(q[t, hq])).max()
-            out[t, hq] = (4 * ds + (width + 16) * u) * (w @ np.abs(v[sel, h]))
+            out[t, hq] = (4 * ds + (width + 32) * u) * (w @ np.abs(v[sel, h]))
     return out
 
 
@@ -61,6 +62,7 @@ CASES = [  # N, T, Hkv, G, d, width, dtype
     (3_000, 2, 1, 1, 256, 40, "f32"),
     (100, 4, 1, 4, 128, 1, "bf16"),
     (200_000, 1, 8, 4, 128, 2_564, "bf16"),     # a 1M-decode row shape: sink 4 + k 2048 + window 512
+    (20_000, 32, 8, 4, 128, 700, "bf16"),       # 1024 rows: one workgroup per row, no split
 ]
 
 
@@ -102,10 +104,15 @@ def test_attention_validation():
     desc = A.IndexDesc.make(100, 1, 128, 32, "bf16", "bf16", (4,), 1, 0)
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     p = buf.data_ptr()
-    assert lib.lsa_sparse_attention(desc, p, p, p, p, 0, 1, 1, 1.0, p, None) == A.LSA_ERR_UNSUPPORTED
-    assert lib.lsa_sparse_attention(desc, p, p, p, p, 40000, 1, 1, 1.0, p, None) == A.LSA_ERR_UNSUPPORTED
-    assert lib.lsa_sparse_attention(desc, None, p, p, p, 4, 1, 1, 1.0, p, None) == A.LSA_ERR_INVALID_ARG
-    assert lib.lsa_sparse_attention(desc, p, p, p, p, 4, 1, 1, float("nan"), p, None) == A.LSA_ERR_INVALID_ARG
+    assert lib.lsa_sparse_attention(desc, p, p, p, p, 0, 1, 1, 1.0, p, p, 1 << 16, None) == A.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_sparse_attention(desc, p, p, p, p, 40000, 1, 1, 1.0, p, p, 1 << 16, None) == \
+        A.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_sparse_attention(desc, None, p, p, p, 4, 1, 1, 1.0, p, p, 1 << 16, None) == A.LSA_ERR_INVALID_ARG
+    assert lib.lsa_sparse_attention(desc, p, p, p, p, 4, 1, 1, float("nan"), p, p, 1 << 16, None) == \
+        A.LSA_ERR_INVALID_ARG
+    # a split row needs its workspace
+    assert A.sparse_attention_workspace_bytes(desc, 2564, 1, 1) > 0
+    assert lib.lsa_sparse_attention(desc, p, p, p, p, 2564, 1, 1, 1.0, p, p, 16, None) == A.LSA_ERR_BUFFER_TOO_SMALL
     # query heads not a multiple of the KV heads
     desc2 = A.IndexDesc.make(100, 2, 128, 32, "bf16", "bf16", (4,), 1, 0)
-    assert lib.lsa_sparse_attention(desc2, p, p, p, p, 4, 1, 3, 1.0, p, None) == A.LSA_ERR_INVALID_ARG
+    assert lib.lsa_sparse_attention(desc2, p, p, p, p, 4, 1, 3, 1.0, p, p, 1 << 16, None) == A.LSA_ERR_INVALID_ARG
