@@ -192,24 +192,35 @@ __global__ __launch_bounds__(kAttBlock) void sparse_attention_kernel(const KT* q
   }
 }
 
-// Parts of a row -> its output (see the file comment).
+// Parts of a row -> its output (see the file comment).  Wave 0 reads every
+// part's maximum and sum once (split <= 64: one lane each) and leaves the
+// rescale factors in LDS; every thread then sums its dims over the parts.
 template <int D>
 __global__ __launch_bounds__(kAttBlock) void attention_combine_kernel(const float* part, int split, float* out) {
+  __shared__ float f[64];
+  __shared__ float zsum;
   const int64_t row = blockIdx.x;
   const float* pr = part + (size_t)row * split * (D + 2);
-  float M = -__builtin_huge_valf();
-  for (int sp = 0; sp < split; ++sp) M = fmaxf(M, pr[(size_t)sp * (D + 2) + D]);
-  float Z = 0.f;
-  for (int sp = 0; sp < split; ++sp) {
-    const float ms = pr[(size_t)sp * (D + 2) + D];
-    if (ms != -__builtin_huge_valf()) Z += expf(ms - M) * pr[(size_t)sp * (D + 2) + D + 1];
+  if (threadIdx.x < 64) {
+    const int sp = threadIdx.x;
+    const float ms = sp < split ? pr[(size_t)sp * (D + 2) + D] : -__builtin_huge_valf();
+    const float zs = sp < split ? pr[(size_t)sp * (D + 2) + D + 1] : 0.f;
+    float M = ms;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float fs = ms == -__builtin_huge_valf() ? 0.f : expf(ms - M);
+    float Z = fs * zs;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o, 64);
+    f[sp] = fs;
+    if (sp == 0) zsum = Z;
   }
+  __syncthreads();
+  const float Z = zsum;
   for (int i = threadIdx.x; i < D; i += kAttBlock) {
     float t = 0.f;
-    for (int sp = 0; sp < split; ++sp) {
-      const float ms = pr[(size_t)sp * (D + 2) + D];
-      if (ms != -__builtin_huge_valf()) t += expf(ms - M) * pr[(size_t)sp * (D + 2) + i];
-    }
+#pragma unroll 8
+    for (int sp = 0; sp < split; ++sp) t += f[sp] * pr[(size_t)sp * (D + 2) + i];
     out[row * D + i] = Z > 0.f ? t / Z : 0.f;
   }
 }
