@@ -18,7 +18,8 @@
  *    caller; the library never allocates or frees device memory and never
  *    synchronises: every call only enqueues work on `stream` (a hipStream_t
  *    passed as void*, NULL = the null stream) and returns.  Calls are
- *    therefore capturable in a HIP graph.
+ *    therefore capturable in a HIP graph.  (lsa_pca_map is the exception: it
+ *    works on host memory only, synchronously, and touches no device.)
  *  - Every argument is validated on the host before anything is enqueued.
  *    On any error nothing is enqueued, the status is returned and
  *    lsa_last_error() describes it.  No call aborts, exits or throws.
