@@ -22,7 +22,7 @@ for 10M-token context" (bayesiansapien wiki), TL;DR and flowchart: the query
 scores cluster centroids and descends into the best few buckets instead of a
 full key scan; the full key scan is ``flat_select``.
 
-Readings taken where the pages are silent (all are listed in the design doc):
+Readings taken where the pages are silent:
 per-parent beam (every kept node keeps its top-b children), inner-product
 scores, top-down Lloyd k-means with seeded Forgy init (splitmix64), empty
 clusters keep their centroid and score -inf, ties to the lowest id/index,
