@@ -116,3 +116,37 @@ def test_attention_validation():
     # query heads not a multiple of the KV heads
     desc2 = A.IndexDesc.make(100, 2, 128, 32, "bf16", "bf16", (4,), 1, 0)
     assert lib.lsa_sparse_attention(desc2, p, p, p, p, 4, 1, 3, 1.0, p, p, 1 << 16, None) == A.LSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("tokens", [1, 48])
+def test_attention_over_select_rows(tokens):
+    # the two entry points chained as a caller would: lsa_select's rows feed
+    # lsa_sparse_attention; the oracle attends over the same rows
+    from hierarchical_key_indexer_amd import _abi as A
+    from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
+    from tests.gpu_helpers import _dev as dev_keys, _li, _params
+    wl = get_workload("decode_1m").scaled(n_keys=30000, n_kv_heads=2, group=4, n_centers=300, n_tokens=tokens,
+                                          kmeans_iters=3, fanout=(16, 16), b=4, k=256, window=64)
+    log(f"[attention] select rows: N={wl.n_keys} T={tokens}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc_o = O.IndexDesc.of(wl)
+    li = _li(desc_o, O.index_blob(O.build_index(keys, W, desc_o)))
+    queries, pos = gen_queries(wl, keys), gen_positions(wl)
+    qd = dev_keys(queries)
+    pd = torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).cuda()
+    prm = _params(O.SelectParams(wl.b, wl.k, wl.sink, wl.window))
+    idx, _, _ = li.select(qd, pd, prm, scores=False)
+    rng = np.random.default_rng(11)
+    vals = _store(rng.standard_normal(keys.shape), "bf16")
+    out = torch.empty((tokens, wl.n_q_heads, wl.d_head), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(wl.d_head)
+    A.lsa_sparse_attention(li.desc, qd, dev_keys(keys), _dev(vals), idx, scale, out)
+    torch.cuda.synchronize()
+    rows = idx.cpu().numpy()
+    assert (rows >= 0).any()
+    got = out.cpu().numpy().astype(np.float64)
+    want = O.sparse_attention(queries, keys, vals, rows, "bf16", scale)
+    bound = 2 * _bound(O.stored_to_f64(queries, "bf16"), O.stored_to_f64(keys, "bf16"),
+                       O.stored_to_f64(vals, "bf16"), rows, scale, wl.group)
+    err = np.abs(got - want)
+    assert np.all(err <= bound + 1e-30), f"worst ratio {np.max(err / (bound + 1e-30)):.3g}"
