@@ -31,11 +31,13 @@ namespace lsa {
 // X [nrows][nheads][dh]; W [heads/group][dh][DL]; the output row of (row, head)
 // is out + ((head_major ? head * nrows + row : row * nheads + head) * DL).
 // OUT_BF16: store bf16 bits (uint16) of the RNE rounding; otherwise store
-// fp32, rounded to bf16 first when ROUND_BF16.
-template <typename KT, int DL, bool OUT_BF16, bool ROUND_BF16>
+// fp32.  maxabs (if set) receives, by an atomic max over the bit patterns,
+// the largest magnitude of the stored values (a NaN orders above +inf).
+template <typename KT, int DL, bool OUT_BF16>
 __global__ __launch_bounds__(256) void project_kernel(const KT* __restrict__ X, int64_t nrows, int nheads,
                                                       int dh, int group, const float* __restrict__ W,
-                                                      void* __restrict__ out, int head_major) {
+                                                      void* __restrict__ out, int head_major,
+                                                      unsigned int* __restrict__ maxabs) {
   constexpr int TR = 64, TK = 64, CPT = DL / 16;
   __shared__ float xs[TR][TK + 1];
   __shared__ float ws[TK][DL];
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(256) void project_kernel(const KT* __restrict__ X, 
     }
     __syncthreads();
   }
+  unsigned int mx = 0u;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = row0 + ty * 4 + r;
@@ -78,12 +81,19 @@ __global__ __launch_bounds__(256) void project_kernel(const KT* __restrict__ X, 
     const int64_t o = (head_major ? (int64_t)head * nrows + row : row * nheads + head) * DL + tx * CPT;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
+      const float v = OUT_BF16 ? round_to_bf16(acc[r][c]) : acc[r][c];
       if (OUT_BF16) {
-        ((bf16_t*)out)[o + c] = (bf16_t)f32_to_bf16_bits(acc[r][c]);
+        ((bf16_t*)out)[o + c] = (bf16_t)(__float_as_uint(v) >> 16);
       } else {
-        ((float*)out)[o + c] = ROUND_BF16 ? round_to_bf16(acc[r][c]) : acc[r][c];
+        ((float*)out)[o + c] = v;
       }
+      mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
     }
+  }
+  if (maxabs) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (unsigned int)__shfl_xor((int)mx, o, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(maxabs, mx);
   }
 }
 
@@ -165,6 +175,39 @@ __global__ void init_centroids_kernel(LevelArgs a, int DL, const int* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// fixed-point scale of the k-means member sums
+// ---------------------------------------------------------------------------
+
+// A member's latent x enters its centroid's sum as round(x * 2^shift), a
+// 64-bit integer, so the sums are exact and independent of the order of
+// addition (the build is deterministic).  With every |x| < 2^e and at most
+// 2^c members (N <= 2^c), shift = 61 - c - e keeps every sum below 2^61 in
+// magnitude, whatever the data's scale, and each value is quantised to a step
+// of 2^-(61-c) of the largest magnitude (2^-37 at 10M keys).  A non-finite
+// latent leaves the sums meaningless; the header then marks the index bad.
+struct FixedPoint {
+  unsigned int maxabs;    // largest |latent| (fp32 bits), atomic max target
+  int shift;
+  int nonfinite;          // 1 if some latent value is inf or NaN
+  float scale;            // 2^shift
+  double inv_scale;       // 2^-shift
+};
+
+__global__ void fixed_point_kernel(FixedPoint* fx, int c) {
+  if (threadIdx.x != 0) return;
+  const unsigned int b = fx->maxabs;
+  const int nonfinite = b >= 0x7F800000u;
+  // |x| < 2^e: e = biased exponent - 126 (subnormals and zero: -126)
+  const int e = (b >> 23) == 0u ? -126 : (int)(b >> 23) - 126;
+  int shift = nonfinite ? 0 : 61 - c - e;
+  shift = shift > 100 ? 100 : (shift < -100 ? -100 : shift);
+  fx->shift = shift;
+  fx->nonfinite = nonfinite;
+  fx->scale = ldexpf(1.f, shift);
+  fx->inv_scale = ldexp(1.0, -shift);
+}
+
+// ---------------------------------------------------------------------------
 // k-means assignment (+ fixed-point accumulation of the member sums)
 // ---------------------------------------------------------------------------
 
@@ -176,7 +219,7 @@ struct AssignArgs {
   uint8_t* child;                   // [Hkv][N] child id by position
   unsigned long long* gsum;         // [Hkv][Pprev*F][DL] fixed point
   unsigned int* gcnt;               // [Hkv][Pprev*F]
-  float fx_scale;                   // 2^shift
+  const FixedPoint* fx;             // scale of the member sums
 };
 
 template <typename LT, int DL, bool ACC, bool LDS_ACC>
@@ -215,6 +258,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
   __syncthreads();
 
   const LT* lat = (const LT*)a.lat + (size_t)h * a.lv.N * DL;
+  const float fx_scale = ACC ? a.fx->scale : 0.f;
   for (int64_t pos = lo + threadIdx.x; pos < hi; pos += 256) {
     const int key = key_at(a.lv, h, pos);
     float x[DL];
@@ -254,12 +298,12 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
       if (LDS_ACC) {
 #pragma unroll
         for (int j = 0; j < DL; ++j)
-          atomicAdd(&lsum[bc * DL + j], (unsigned long long)__float2ll_rn(x[j] * a.fx_scale));
+          atomicAdd(&lsum[bc * DL + j], (unsigned long long)__float2ll_rn(x[j] * fx_scale));
         atomicAdd(&lcnt[bc], 1u);
       } else {
         unsigned long long* gs = a.gsum + (node0 + bc) * DL;
 #pragma unroll
-        for (int j = 0; j < DL; ++j) atomicAdd(&gs[j], (unsigned long long)__float2ll_rn(x[j] * a.fx_scale));
+        for (int j = 0; j < DL; ++j) atomicAdd(&gs[j], (unsigned long long)__float2ll_rn(x[j] * fx_scale));
         atomicAdd(&a.gcnt[node0 + bc], 1u);
       }
     }
@@ -277,10 +321,12 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
 // accumulators are cleared for the next round.
 __global__ __launch_bounds__(256) void kmeans_update_kernel(int64_t nodes, int DL, float* __restrict__ cent,
                                                             unsigned long long* __restrict__ gsum,
-                                                            unsigned int* __restrict__ gcnt, double inv_scale) {
+                                                            unsigned int* __restrict__ gcnt,
+                                                            const FixedPoint* __restrict__ fx) {
   const int64_t node = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (node >= nodes) return;
+  const double inv_scale = fx->inv_scale;
   const unsigned int cnt = gcnt[node];
   __builtin_amdgcn_wave_barrier();
   if (cnt != 0u) {
@@ -426,8 +472,10 @@ __global__ void cscore_kernel(const float* cent, void* out, int64_t n, int bf16)
   }
 }
 
-__global__ void header_kernel(BlobHeader hdr, uint32_t* out) {
-  if (threadIdx.x < 64) out[threadIdx.x] = hdr.w[threadIdx.x];
+// Word 15 of the header is the build status: 0, or 1 when a latent value was
+// not finite (select then refuses the index).
+__global__ void header_kernel(BlobHeader hdr, const FixedPoint* fx, uint32_t* out) {
+  if (threadIdx.x < 64) out[threadIdx.x] = threadIdx.x == 15 ? (uint32_t)fx->nonfinite : hdr.w[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
@@ -447,13 +495,6 @@ int ceil_log2(int64_t n) {
   return b;
 }
 
-// Fixed-point scale of the centroid sums: |latent| < 256 and at most N
-// members keep every sum below 2^52, so it converts to double exactly.
-int fx_shift(int64_t n) {
-  int s = 44 - ceil_log2(n);
-  return s > 30 ? 30 : (s < 8 ? 8 : s);
-}
-
 int splits_for(int64_t n, int64_t parents, int64_t per_wg) {
   int64_t s = (n + parents * per_wg - 1) / (parents * per_wg);
   return (int)(s < 1 ? 1 : (s > 4096 ? 4096 : s));
@@ -467,6 +508,7 @@ struct BuildWsPtrs {
   unsigned long long* gsum;
   unsigned int* gcnt;
   int* csr_cnt;
+  FixedPoint* fx;
 };
 
 size_t carve_build(const lsa_index_desc& d, void* base, BuildWsPtrs* w) {
@@ -488,6 +530,7 @@ size_t carve_build(const lsa_index_desc& d, void* base, BuildWsPtrs* w) {
   t.gsum = c.take<unsigned long long>((size_t)(hk * L.nodes[d.n_levels] * dl));
   t.gcnt = c.take<unsigned int>((size_t)(hk * L.nodes[d.n_levels]));
   t.csr_cnt = c.take<int>((size_t)(hk * csr_items));
+  t.fx = c.take<FixedPoint>(1);
   if (w) *w = t;
   return align_up(c.used);
 }
@@ -518,16 +561,19 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(nb)), dim3(256), 0, st, (uint32_t*)blob, 0u, nb);
     LSA_LAUNCH_CHECK();
   }
-  // latent keys [Hkv][N][DL]
+  // latent keys [Hkv][N][DL], their largest magnitude, the fixed-point scale
   {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.fx, 0u, (int64_t)1);
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)hk);
+    unsigned int* mx = &w.fx->maxabs;
     if (DL == 64) {
-      if (lat_bf16) hipLaunchKernelGGL((project_kernel<KT, 64, true, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1);
-      else hipLaunchKernelGGL((project_kernel<KT, 64, false, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1);
+      if (lat_bf16) hipLaunchKernelGGL((project_kernel<KT, 64, true>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1, mx);
+      else hipLaunchKernelGGL((project_kernel<KT, 64, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1, mx);
     } else {
-      if (lat_bf16) hipLaunchKernelGGL((project_kernel<KT, 32, true, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1);
-      else hipLaunchKernelGGL((project_kernel<KT, 32, false, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1);
+      if (lat_bf16) hipLaunchKernelGGL((project_kernel<KT, 32, true>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1, mx);
+      else hipLaunchKernelGGL((project_kernel<KT, 32, false>), grid, dim3(256), 0, st, (const KT*)keys, N, (int)hk, d.d_head, 1, W, w.lat, 1, mx);
     }
+    hipLaunchKernelGGL(fixed_point_kernel, dim3(1), dim3(64), 0, st, w.fx, ceil_log2(N));
     LSA_LAUNCH_CHECK();
   }
   // the latent map travels with the index
@@ -543,10 +589,6 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(nc)), dim3(256), 0, st, (uint32_t*)w.gcnt, 0u, nc);
     LSA_LAUNCH_CHECK();
   }
-  const int shift = fx_shift(N);
-  const float fx_scale = ldexpf(1.f, shift);
-  const double inv_scale = ldexp(1.0, -shift);
-
   for (int l = 1; l <= d.n_levels; ++l) {
     LevelArgs lv;
     lv.N = N;
@@ -573,7 +615,7 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
     aa.child = w.child;
     aa.gsum = w.gsum;
     aa.gcnt = w.gcnt;
-    aa.fx_scale = fx_scale;
+    aa.fx = w.fx;
     const size_t base_lds = align_up((size_t)lv.F * DL * 4 + lv.F * 4, 16);
     const size_t lds_acc = base_lds + (size_t)lv.F * DL * 8 + lv.F * 4;
     const bool use_lds_acc = lds_acc <= 64 * 1024;
@@ -593,7 +635,7 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
       if (acc) {
         const int64_t nodes = hk * nchild;
         hipLaunchKernelGGL(kmeans_update_kernel, dim3((unsigned)((nodes + 3) / 4)), dim3(256), 0, st, nodes, DL, cent,
-                           w.gsum, w.gcnt, inv_scale);
+                           w.gsum, w.gcnt, (const FixedPoint*)w.fx);
         LSA_LAUNCH_CHECK();
       }
     }
@@ -639,7 +681,7 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
     u64[13 + l] = l < d.n_levels ? L.offsets[l] : 0;
   }
   memcpy(hb + 64, u64, sizeof(u64));
-  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, st, hdr, (uint32_t*)blob);
+  hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, st, hdr, (const FixedPoint*)w.fx, (uint32_t*)blob);
   LSA_LAUNCH_CHECK();
   return LSA_OK;
 }
@@ -655,26 +697,6 @@ int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void
   if (kb && !lb) return run_build<bf16_t, float>(d, keys, W, index, ws, stream, err, errlen);
   if (!kb && lb) return run_build<float, bf16_t>(d, keys, W, index, ws, stream, err, errlen);
   return run_build<float, float>(d, keys, W, index, ws, stream, err, errlen);
-}
-
-// query latents: q~ [T*Hq][DL] fp32 holding latent-dtype values
-int launch_project_queries(const lsa_index_desc& d, const void* queries, int32_t T, int32_t Hq, const float* W,
-                           float* out, hipStream_t st) {
-  const int G = Hq / d.n_kv_heads;
-  dim3 grid((unsigned)((T + 63) / 64), (unsigned)Hq);
-  const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
-#define LSA_PQ(KT, DLV)                                                                                      \
-  if (lb) hipLaunchKernelGGL((project_kernel<KT, DLV, false, true>), grid, dim3(256), 0, st, (const KT*)queries, \
-                             (int64_t)T, Hq, d.d_head, G, W, (void*)out, 0);                                 \
-  else hipLaunchKernelGGL((project_kernel<KT, DLV, false, false>), grid, dim3(256), 0, st, (const KT*)queries,   \
-                          (int64_t)T, Hq, d.d_head, G, W, (void*)out, 0);
-  if (kb) {
-    if (d.d_latent == 64) { LSA_PQ(bf16_t, 64) } else { LSA_PQ(bf16_t, 32) }
-  } else {
-    if (d.d_latent == 64) { LSA_PQ(float, 64) } else { LSA_PQ(float, 32) }
-  }
-#undef LSA_PQ
-  return hipGetLastError() == hipSuccess ? LSA_OK : LSA_ERR_HIP;
 }
 
 }  // namespace lsa

@@ -34,9 +34,14 @@
  * 2 <= fanout <= 256; at most 65535 nodes above the leaf level; product of
  * fanouts <= 2^22; per-parent beam: b <= fanout at every level and
  * b^n_levels <= 4096; global beam: b <= 64; 1 <= k <= 4096; n_q_heads <=
- * 65535; the flat scan needs n_q_heads / n_kv_heads in {1, 2, 4}.  Latent
- * values must stay below 256 in magnitude (the k-means centroid sums use
- * 64-bit fixed point).
+ * 65535; the flat scan needs n_q_heads / n_kv_heads in {1, 2, 4}.
+ *
+ * The k-means member sums are 64-bit fixed point: a latent value x enters as
+ * round(x * 2^s) with s = 61 - c - e, where every |latent| < 2^e and
+ * N <= 2^c (s clamped to [-100, 100]).  No sum can overflow whatever the
+ * data's scale; each value is quantised to 2^-(61-c) of the largest magnitude
+ * (2^-37 at 10M keys).  A non-finite latent value marks the index bad (header
+ * word 15), and select then refuses it.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -95,7 +100,8 @@ typedef struct {
  *     0  char[4]   "LSA1"            4  uint32  version = 1
  *     8  int64     n_keys
  *    16  int32     n_kv_heads, d_head, d_latent, key_dtype, latent_dtype,
- *                  n_levels, fanout[4], kmeans_iters, 0
+ *                  n_levels, fanout[4], kmeans_iters, build status (0 = good,
+ *                  1 = a latent value was not finite)
  *    64  uint64    seed              72  uint64  total bytes
  *    80  uint64    offset of W       88  uint64  offset of perm
  *    96  uint64    offset of latent

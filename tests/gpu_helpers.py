@@ -52,3 +52,25 @@ def gpu_build(desc_o, keys, W):
 
 def _blob_of(li):
     return li.index.cpu().numpy()
+
+
+def one_head_index(li, desc_o: O.IndexDesc, h: int) -> O.OracleIndex:
+    """KV head h of a device-resident index as a one-head oracle index: every
+    section of head h is copied from the device into a one-head blob of the
+    same layout, which the oracle's reader then decodes."""
+    import dataclasses
+    d1 = dataclasses.replace(desc_o, n_kv_heads=1)
+    lay, lay1 = O.blob_layout(desc_o), O.blob_layout(d1)
+    ls = 2 if desc_o.latent_dtype == "bf16" else 4
+    dl, n = desc_o.d_latent, desc_o.n_keys
+    sizes = {"W": desc_o.d_head * dl * 4, "perm": n * 4, "latent": n * dl * ls}
+    for lev in range(1, desc_o.n_levels + 1):
+        p = desc_o.nodes(lev)
+        sizes[f"cent{lev}"] = p * dl * 4
+        sizes[f"cscore{lev}"] = p * dl * ls
+        sizes[f"off{lev}"] = (p + 1) * 4
+    blob1 = np.zeros(lay1["total"], dtype=np.uint8)
+    for name, sz in sizes.items():
+        src = lay[name] + h * sz
+        blob1[lay1[name]:lay1[name] + sz] = li.index[src:src + sz].cpu().numpy()
+    return O.index_from_blob(blob1, d1)

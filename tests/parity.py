@@ -190,3 +190,88 @@ def check_build(gidx, keys, W, desc: O.IndexDesc, sample=None, log=None):
                 assert ok.all(), f"head {h} level {lev + 1}: {np.sum(~ok)} keys not at their nearest centroid"
     if log:
         log("build properties hold")
+
+
+def fixed_point_step(lat_all: np.ndarray, n_keys: int) -> float:
+    """Quantisation step of the GPU build's fixed-point centroid sums, from
+    the rule include/lsa.h states: every |latent| < 2^e (e the smallest such
+    exponent, at least -126), at most 2^c members with 2^c >= N, and step
+    2^-(61 - c - e) (the shift clamped to [-100, 100])."""
+    m = float(np.max(np.abs(lat_all))) if lat_all.size else 0.0
+    e = max(int(np.frexp(m)[1]), -126) if m > 0 else -126
+    c = int(np.ceil(np.log2(n_keys))) if n_keys > 1 else 0
+    while (1 << c) < n_keys:
+        c += 1
+    shift = min(100, max(-100, 61 - c - e))
+    return float(np.ldexp(1.0, -shift))
+
+
+def check_lloyd_update(gidx, desc: O.IndexDesc, step: float, log=None, tie_rel=2e-5):
+    """One Lloyd round (kmeans_iters = 1), at every level of every head: the
+    stored centroids are the update that follows the first assignment.
+
+    For every parent, its members are read from the index's own partition of
+    the level above (ascending key order).  The oracle draws the parent's
+    initial centroids (seeded Forgy), assigns each member to the nearest one in
+    float64 and takes each child's member mean.  An initialised child must then
+    hold that mean rounded to fp32, within the fixed-point step of the sums
+    (``step``) plus one fp32 ulp; a child that received no member keeps its
+    initial centroid exactly; a void child stays zero.  A member whose two
+    nearest initial centroids lie within ``tie_rel`` of each other, relative to
+    S = |x|^2 + |mu_a|^2 + |mu_b|^2, may go either way in fp32, so the two
+    children it touches are not compared.  The GPU evaluates |mu|^2 - 2 x.mu
+    with fp32 sums of at most 64 and 33 products; the standard bound
+    gamma_n sum|a_i b_i| puts the error of a difference of two such distances
+    below 99 * 2^-24 * S = 5.9e-6 S, so 2e-5 S leaves a margin.  Returns
+    (children compared, children skipped)."""
+    assert desc.kmeans_iters == 1
+    compared = skipped = 0
+    for h, hh in enumerate(gidx.heads):
+        lat = np.empty_like(hh.csr_latent)
+        lat[hh.perm] = hh.csr_latent
+        for lev, f in enumerate(desc.fanout):
+            if lev == 0:
+                members = [np.arange(desc.n_keys)]
+            else:
+                order = np.argsort(hh.assign[lev - 1], kind="stable")
+                cuts = np.searchsorted(hh.assign[lev - 1][order], np.arange(desc.nodes(lev) + 1))
+                members = [order[cuts[p]:cuts[p + 1]] for p in range(desc.nodes(lev))]
+            got = hh.centroids[lev]
+            for p, mem in enumerate(members):
+                pos = O.kmeans_init_positions(desc.seed, h, lev + 1, p, len(mem), f)
+                nv = len(pos)
+                g = got[p * f:(p + 1) * f]
+                assert np.all(g[nv:] == 0.0), f"head {h} level {lev + 1} node {p}: void child not zero"
+                if nv == 0:
+                    continue
+                x = lat[mem]
+                init = O.round_f32(x[np.asarray(pos)])
+                xx = np.einsum("ij,ij->i", x, x)
+                d2 = O.sq_dists(x, init, xx)
+                a = np.argmin(d2, axis=1)
+                unsure = np.zeros(nv, dtype=bool)
+                if nv > 1:
+                    part = np.partition(d2, 1, axis=1)
+                    mm = np.einsum("ij,ij->i", init, init)
+                    second = np.argsort(d2, axis=1, kind="stable")[:, 1]
+                    near = (part[:, 1] - part[:, 0]) <= tie_rel * (xx + mm[a] + mm[second])
+                    unsure[a[near]] = True
+                    unsure[second[near]] = True
+                cnt, sums = O.member_means(x, a, nv)
+                for c in range(nv):
+                    if unsure[c]:
+                        skipped += 1
+                        continue
+                    compared += 1
+                    if cnt[c] == 0:
+                        assert np.array_equal(g[c], init[c]), \
+                            f"head {h} level {lev + 1} node {p} child {c}: empty child moved"
+                        continue
+                    mean = sums[c] / cnt[c]
+                    tol = step + np.spacing(np.abs(mean).astype(np.float32)).astype(np.float64)
+                    bad = np.abs(g[c] - mean) > tol
+                    assert not bad.any(), (f"head {h} level {lev + 1} node {p} child {c}: centroid is not the "
+                                           f"member mean (max err {np.max(np.abs(g[c] - mean)):.3g})")
+    if log:
+        log(f"Lloyd update: {compared} children equal their member means, {skipped} skipped at near-ties")
+    return compared, skipped

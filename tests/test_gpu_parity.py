@@ -10,7 +10,7 @@ import pytest
 from oracle import lsa_oracle as O
 from synth import gen_keys, gen_positions, gen_queries, gen_W, get_workload
 from tests.gpu_helpers import _abi, _blob_of, _dev, _li, _params, gpu_build, gpu_select
-from tests.parity import check_build, compare_select, log
+from tests.parity import check_build, check_lloyd_update, compare_select, fixed_point_step, log
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -110,6 +110,28 @@ def test_kmeans_init_draws_match_the_oracle(case):
                 want[p * f:p * f + len(pos)] = lat[mem[pos]]
             assert np.array_equal(hh.centroids[lev], want), f"head {h} level {lev + 1}: initial centroids"
     log(f"[init draws] {case}: initial centroids match the oracle's draws")
+
+
+LLOYD_CASES = {name: SMALL_CASES[name] for name in ("2lvl_bf16_g2", "3lvl_bf16_g4", "2lvl_tiny_nodes")}
+LLOYD_CASES["1lvl_f32_dl32"] = SMALL_CASES["1lvl_f32_dl32"]
+LLOYD_CASES["tiny_flat_65k"] = get_workload("tiny_flat_65k")
+
+
+@pytest.mark.parametrize("case", list(LLOYD_CASES))
+def test_kmeans_update_matches_the_oracle(case):
+    """One Lloyd round at every level: the centroids the GPU stores are the
+    member means of the oracle's first assignment to the seeded initial
+    centroids (parents' members from the GPU's own partition of the level
+    above), within the fixed-point step of the sums and one fp32 ulp."""
+    wl = LLOYD_CASES[case].scaled(kmeans_iters=1)
+    log(f"[Lloyd update] case={case} N={wl.n_keys} fanout={wl.fanout}")
+    keys, W = gen_keys(wl), gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    gidx = O.index_from_blob(_blob_of(gpu_build(desc, keys, W)), desc)
+    step = fixed_point_step(np.stack([hh.csr_latent for hh in gidx.heads]), desc.n_keys)
+    compared, skipped = check_lloyd_update(gidx, desc, step, log=log)
+    assert compared >= 0.75 * (compared + skipped), f"{skipped} of {compared + skipped} children skipped"
+    check_build(gidx, keys, W, desc, sample=20000)
 
 
 def test_tree_with_all_buckets_equals_flat_gpu():

@@ -450,3 +450,80 @@ def test_generator_distributions():
     assert x.shape == (200000, 128) and c.shape == (65536, 128)
     q = S.gen_queries(wl.scaled(n_tokens=3), S.gen_keys(wl))
     assert q.shape == (3, 4, 128) and q.dtype == np.uint16
+
+
+def test_lloyd_update_checker_accepts_the_definition_and_catches_wrong_updates():
+    """The checker the GPU build is held to (tests/parity.check_lloyd_update)
+    accepts the oracle's own one-round index and fails an index whose update
+    was skipped, moved to another subset's mean, or nudged by more than the
+    fixed-point step: a no-op or wrong update kernel cannot pass it."""
+    from tests.parity import check_lloyd_update, fixed_point_step
+    wl = S.get_workload("decode_1m").scaled(n_keys=3000, n_kv_heads=2, group=1, n_centers=40, fanout=(8, 8),
+                                            kmeans_iters=1)
+    keys, W = S.gen_keys(wl), S.gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    blob = O.index_blob(O.build_index(keys, W, desc))
+
+    def fresh():
+        return O.index_from_blob(blob.copy(), desc)
+
+    idx = fresh()
+    step = fixed_point_step(np.stack([hh.csr_latent for hh in idx.heads]), desc.n_keys)
+    compared, skipped = check_lloyd_update(idx, desc, step)
+    assert compared > 0.9 * (compared + skipped) and compared > 100
+
+    # no update: the initial centroids stay
+    idx0 = O.index_from_blob(O.index_blob(O.build_index(keys, W, O.IndexDesc.of(wl.scaled(kmeans_iters=0)))),
+                             O.IndexDesc.of(wl.scaled(kmeans_iters=0)))
+    bad = fresh()
+    bad.heads[0].centroids[0] = idx0.heads[0].centroids[0].copy()
+    with pytest.raises(AssertionError):
+        check_lloyd_update(bad, desc, step)
+    # a child moved to its neighbour's mean
+    bad = fresh()
+    c = bad.heads[1].centroids[1]
+    c[[3, 4]] = c[[4, 3]]
+    with pytest.raises(AssertionError):
+        check_lloyd_update(bad, desc, step)
+    # a nudge well beyond the fixed-point step and one fp32 ulp
+    bad = fresh()
+    bad.heads[0].centroids[1][10, 5] += 1e-3
+    with pytest.raises(AssertionError):
+        check_lloyd_update(bad, desc, step)
+
+
+def test_fixed_point_step_rule():
+    """The step follows |x| < 2^e and N <= 2^c: shift = 61 - c - e."""
+    from tests.parity import fixed_point_step
+    assert fixed_point_step(np.array([3.0]), 1 << 20) == 2.0 ** -(61 - 20 - 2)
+    assert fixed_point_step(np.array([4.0]), (1 << 20) + 1) == 2.0 ** -(61 - 21 - 3)
+    assert fixed_point_step(np.array([0.0]), 10) == 2.0 ** -100
+    assert fixed_point_step(np.array([-1e30]), 10_000_000) == 2.0 ** -(61 - 24 - 100)
+
+
+def test_one_head_readback_matches_the_full_blob():
+    """The helper that reads one KV head of a device blob (used at 10M keys,
+    where the whole blob is too large to decode) gives that head exactly as
+    the reader of the full blob does; run here on a host tensor."""
+    import types
+
+    import torch
+
+    from tests.gpu_helpers import one_head_index
+    wl = S.get_workload("decode_1m").scaled(n_keys=1500, n_kv_heads=3, group=1, n_centers=20, fanout=(4, 8),
+                                            kmeans_iters=2)
+    keys, W = S.gen_keys(wl), S.gen_W(wl)
+    desc = O.IndexDesc.of(wl)
+    blob = O.index_blob(O.build_index(keys, W, desc))
+    full = O.index_from_blob(blob, desc)
+    li = types.SimpleNamespace(index=torch.from_numpy(blob))
+    for h in range(3):
+        one = one_head_index(li, desc, h).heads[0]
+        ref = full.heads[h]
+        assert np.array_equal(one.W, ref.W) and np.array_equal(one.perm, ref.perm)
+        assert np.array_equal(one.csr_latent, ref.csr_latent)
+        for lev in range(2):
+            assert np.array_equal(one.centroids[lev], ref.centroids[lev])
+            assert np.array_equal(one.cscore[lev], ref.cscore[lev])
+            assert np.array_equal(one.offsets[lev], ref.offsets[lev])
+            assert np.array_equal(one.assign[lev], ref.assign[lev])
