@@ -250,6 +250,12 @@ def lsa_sparse_attention(desc, queries, keys, values, idx, scale, out, workspace
                                        _stream(stream)))
 
 
+def device_status(workspace) -> int:
+    """The device status a finished select call left in its workspace (bytes
+    [0, 4)): LSA_OK or LSA_ERR_BAD_INDEX.  Synchronises with the device."""
+    return int(workspace[:4].view(__import__("torch").int32).item())
+
+
 def set_profile_events(stage: int, start, stop) -> None:
     """Record raw hipEvent_t handles around one stage of later select calls
     (None, None switches it off)."""

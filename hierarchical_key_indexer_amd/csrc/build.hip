@@ -662,25 +662,7 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
   }
   LSA_LAUNCH_CHECK();
 
-  BlobHeader hdr;
-  memset(&hdr, 0, sizeof(hdr));
-  char* hb = (char*)hdr.w;
-  memcpy(hb, "LSA1", 4);
-  const uint32_t version = 1;
-  memcpy(hb + 4, &version, 4);
-  memcpy(hb + 8, &d.n_keys, 8);
-  const int32_t i32[12] = {d.n_kv_heads, d.d_head, d.d_latent, d.key_dtype, d.latent_dtype, d.n_levels,
-                           d.n_levels > 0 ? d.fanout[0] : 0, d.n_levels > 1 ? d.fanout[1] : 0,
-                           d.n_levels > 2 ? d.fanout[2] : 0, d.n_levels > 3 ? d.fanout[3] : 0,
-                           d.kmeans_iters, 0};
-  memcpy(hb + 16, i32, sizeof(i32));
-  uint64_t u64[17] = {d.seed, L.total, L.W, L.perm, L.latent};
-  for (int l = 0; l < 4; ++l) {
-    u64[5 + l] = l < d.n_levels ? L.cent[l] : 0;
-    u64[9 + l] = l < d.n_levels ? L.cscore[l] : 0;
-    u64[13 + l] = l < d.n_levels ? L.offsets[l] : 0;
-  }
-  memcpy(hb + 64, u64, sizeof(u64));
+  const BlobHeader hdr = make_header(d, L);
   hipLaunchKernelGGL(header_kernel, dim3(1), dim3(64), 0, st, hdr, (const FixedPoint*)w.fx, (uint32_t*)blob);
   LSA_LAUNCH_CHECK();
   return LSA_OK;

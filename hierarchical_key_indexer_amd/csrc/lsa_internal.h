@@ -56,6 +56,37 @@ struct BlobHeader {
   uint32_t w[64];
 };
 
+// The header lsa.h specifies for a descriptor (build status word 15 = 0).
+inline BlobHeader make_header(const lsa_index_desc& d, const Layout& L) {
+  BlobHeader hdr;
+  memset(&hdr, 0, sizeof(hdr));
+  char* hb = (char*)hdr.w;
+  memcpy(hb, "LSA1", 4);
+  const uint32_t version = 1;
+  memcpy(hb + 4, &version, 4);
+  memcpy(hb + 8, &d.n_keys, 8);
+  const int32_t i32[12] = {d.n_kv_heads, d.d_head, d.d_latent, d.key_dtype, d.latent_dtype, d.n_levels,
+                           d.n_levels > 0 ? d.fanout[0] : 0, d.n_levels > 1 ? d.fanout[1] : 0,
+                           d.n_levels > 2 ? d.fanout[2] : 0, d.n_levels > 3 ? d.fanout[3] : 0,
+                           d.kmeans_iters, 0};
+  memcpy(hb + 16, i32, sizeof(i32));
+  uint64_t u64[17] = {d.seed, L.total, L.W, L.perm, L.latent};
+  for (int l = 0; l < 4; ++l) {
+    u64[5 + l] = l < d.n_levels ? L.cent[l] : 0;
+    u64[9 + l] = l < d.n_levels ? L.cscore[l] : 0;
+    u64[13 + l] = l < d.n_levels ? L.offsets[l] : 0;
+  }
+  memcpy(hb + 64, u64, sizeof(u64));
+  return hdr;
+}
+
+// What a select call compares before it reads anything else of a blob: the
+// first kHeaderCheckWords header words, except kmeans_iters (word 14) and the
+// seed (words 16-17), which select does not depend on.  Word 15, the build
+// status, must be 0.
+constexpr int kHeaderCheckWords = 20;
+constexpr uint32_t kHeaderCheckMask = 0xFFFFFu & ~((1u << 14) | (1u << 16) | (1u << 17));
+
 // Bump allocator over a caller workspace; with base == nullptr it only sizes.
 struct Carver {
   char* base;

@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
   __shared__ float q[DL];
   const int64_t row = blockIdx.x;
   const int h = (int)(row % a.s.Hq) / a.s.G;
+  if (!check_index_first(a.s)) return;       // nothing past the header is read
   query_latent<KT, bf16_t, DL>(a.s, row, h, qin, q);
   if (threadIdx.x < DL) a.qlat16[row * DL + threadIdx.x] = (uint16_t)(__float_as_uint(q[threadIdx.x]) >> 16);
   if (threadIdx.x == 0) *pf_count_of(a, row) = 0u;
@@ -170,6 +171,7 @@ template <int DL, int NT, int BMAX>
 __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
   constexpr int KS = DL / 16;                    // k-steps of 16 latent dims
   __shared__ uint32_t lcnt[kPfMaxF];
+  if (*a.s.status != LSA_OK) return;
   int64_t gp;
   int ch;
   pf_block(a, &gp, &ch);
@@ -303,6 +305,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
 
 __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   __shared__ uint32_t lcnt[kPfMaxF], lbase[kPfMaxF], lfill[kPfMaxF], cst[kPfMaxF];
+  if (*a.s.status != LSA_OK) return;
   int64_t gp;
   int ch;
   pf_block(a, &gp, &ch);
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ uint32_t tpre[kPfMaxF + 1];
   __shared__ uint32_t lst[kPfMaxF], lcn[kPfMaxF];
   __shared__ int o0s[kPfMaxF], o1s[kPfMaxF];
+  if (*a.s.status != LSA_OK) return;
   const int lev = a.s.L - 1;
   int64_t gp;
   int ch;
@@ -770,6 +774,7 @@ __device__ __forceinline__ int wave_find_bin(const u64* hist, u64 need, u64* abo
 template <int kTauCL>
 __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   __shared__ u64 hist[kPfNW][256];
+  if (*a.s.status != LSA_OK) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kPfNW + w;
   const bool live = row < a.R;
@@ -877,6 +882,13 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   const int64_t row = blockIdx.x;
   const int t = (int)(row / a.s.Hq), h = (int)(row % a.s.Hq) / a.s.G;
   const int p = a.s.q_pos[t];
+  if (*a.s.status != LSA_OK) {
+    write_invalid_row<BLOCK>(a.s.width, a.s.k, a.s.out_idx + (size_t)row * a.s.width,
+                             a.s.out_scores ? a.s.out_scores + (size_t)row * a.s.k : nullptr);
+    if (a.s.out_leaves)
+      for (int i = threadIdx.x; i < a.s.nl_cap; i += BLOCK) a.s.out_leaves[(size_t)row * a.s.nl_cap + i] = -1;
+    return;
+  }
   const int lev = a.s.L - 1;
   const int* offL = a.s.off[lev] + (size_t)h * (a.s.P[lev] + 1);
   const int32_t* lfr = a.lf + (size_t)row * a.nl;
@@ -1006,6 +1018,7 @@ __device__ __forceinline__ int fs_row(const PfArgs& a, int h, int64_t i) {
 template <int DL>
 __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
   constexpr int KS = DL / 16;
+  if (*a.s.status != LSA_OK) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t tiles = (a.TG + 31) / 32;          // row tiles per KV head
@@ -1089,6 +1102,7 @@ __global__ __launch_bounds__(kFsBlock) void fs_tau_kernel(PfArgs a) {
 template <int DL>
 __global__ __launch_bounds__(kFsBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void fs_scan_kernel(PfArgs a) {
   constexpr int KS = DL / 16;
+  if (*a.s.status != LSA_OK) return;
   constexpr int NW = kFsBlock / 64;
   constexpr int SE = kFsStage / 64;
   constexpr int TB = 32 * DL * 2;                  // bytes of a 32-key tile
@@ -1341,6 +1355,7 @@ __global__ void pf_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 // ---------------------------------------------------------------------------
 
 struct PfWs {
+  int* status;
   float* qlat;
   uint16_t* qlat16;
   int2* E[kMaxLevels];
@@ -1361,6 +1376,7 @@ size_t carve_prefill(const lsa_index_desc& d, const PfPlan& pl, int64_t R, void*
   PfWs w;
   memset(&w, 0, sizeof(w));
   const int DL = d.d_latent;
+  w.status = c.take<int>(64);                 // byte 0 of the workspace (lsa.h)
   w.qlat = c.take<float>((size_t)(R * DL));
   w.qlat16 = c.take<uint16_t>((size_t)(R * DL));
   for (int e = 0; e < d.n_levels; ++e) {
@@ -1451,6 +1467,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
   a.spl = pl.spl;
   a.spl4 = (pl.spl + 3) / 4 * 4;
   a.shalf = pl.shalf;
+  set_header_check(s, d, L, index, w.status);
   a.smp = w.smp;
   a.tauf = w.tauf;
   a.cap = pl.cap;
@@ -1528,6 +1545,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
 }
 
 struct FsWs {
+  int* status;
   float* qlat;
   uint16_t* qlat16;
   float* tauf;
@@ -1538,6 +1556,7 @@ struct FsWs {
 size_t carve_flat_tiled(const lsa_index_desc& d, const FsPlan& pl, int64_t R, void* base, FsWs* out) {
   Carver c(base);
   FsWs w;
+  w.status = c.take<int>(64);                 // byte 0 of the workspace (lsa.h)
   w.qlat = c.take<float>((size_t)(R * d.d_latent));
   w.qlat16 = c.take<uint16_t>((size_t)(R * d.d_latent));
   w.tauf = c.take<float>((size_t)R);
@@ -1592,6 +1611,7 @@ int run_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, const Fs
   a.fs_keys = pl.keys;
   a.fs_split = pl.split;
   a.fs_rb = pl.rb;
+  set_header_check(s, d, L, index, w.status);
 
 #define FS_CHECK(what)                                                               \
   do {                                                                               \

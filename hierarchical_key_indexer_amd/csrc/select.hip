@@ -172,6 +172,11 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   const int hq = (int)(qh % a.Hq);
   const int h = hq / a.G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (!check_index_first(a)) {               // block-uniform: nothing past the header is read
+    if (a.out_leaves)
+      for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) a.out_leaves[qh * a.nl_cap + i] = -1;
+    return;
+  }
   query_latent<KT, LT, DL>(a, qh, h, qin, q);
   if (threadIdx.x == 0) {
     fa[0] = 0;
@@ -417,6 +422,7 @@ __global__ __launch_bounds__(256) void qproj_kernel(SelArgs a) {
   __shared__ float q[DL];
   const int64_t qh = a.qh0 + blockIdx.x;
   const int h = (int)(qh % a.Hq) / a.G;
+  if (!check_index_first(a)) return;
   query_latent<KT, LT, DL>(a, qh, h, qin, q);
   if (threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;
 }
@@ -439,6 +445,7 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   // their capacity, not to the list length), so they are all issued before
   // the first LDS store and share one round trip.
   const int p = a.q_pos[t];
+  const int bad = *a.status;
   const int nl = a.nleaf[qh];
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   {
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
     for (int i = threadIdx.x + R * BLOCK; i < np; i += BLOCK) lpre[i] = gp[i];
     for (int i = threadIdx.x + R * BLOCK; i < a.nl_cap; i += BLOCK) lrow[i] = gr[i];
   }
-  if (p < 0 || (int64_t)p >= a.N) {
+  if (bad || p < 0 || (int64_t)p >= a.N) {
     if (a.S == 1)
       write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
@@ -564,6 +571,7 @@ __global__ __launch_bounds__(1024) void flat_tau_kernel(SelArgs a, int NS, int t
   __shared__ uint32_t asel;
   const int64_t qh = a.qh0 + blockIdx.x;
   const int h = (int)(qh % a.Hq) / a.G;
+  if (!check_index_first(a)) return;
   query_latent<KT, LT, DL>(a, qh, h, qin, q);
   if (threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;
   const int p = a.q_pos[qh / a.Hq];
@@ -634,7 +642,8 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   const int n_in = (int)a.part_n[qh];
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   const int p = a.q_pos[t];
-  if (p < 0 || (int64_t)p >= a.N) {
+  const int bad = *a.status;
+  if (bad || p < 0 || (int64_t)p >= a.N) {
     write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
   }
@@ -759,8 +768,9 @@ __global__ __launch_bounds__(1024) void flat_kernel(SelArgs a) {
   const int s = blockIdx.x;
   const int t = blockIdx.y / a.Hkv, h = blockIdx.y % a.Hkv;
   const int p = a.q_pos[t];
+  const int bad = *a.status;
   const int64_t qh_base = (int64_t)t * a.Hq + (int64_t)h * a.G;
-  if (p < 0 || (int64_t)p >= a.N) {
+  if (bad || p < 0 || (int64_t)p >= a.N) {
     if (a.S == 1)
       for (int j = 0; j < NQ; ++j) {
         const int64_t qh = qh_base + j;
@@ -882,6 +892,7 @@ constexpr int kFlatU = 4;
 constexpr int kFlatR = 40;                 // samples expected above a full-scan threshold
 
 struct SelWs {
+  int* status;
   float* qlat;
   int* leafrow;
   int* leafpre;
@@ -896,6 +907,7 @@ size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const S
   Carver c(base);
   SelWs w;
   const int64_t qh = (int64_t)T * Hq;
+  w.status = c.take<int>(64);                 // byte 0 of the workspace (lsa.h)
   w.qlat = c.take<float>((size_t)(qh * d.d_latent));
   w.leafrow = w.leafpre = w.nleaf = nullptr;
   if (!flat) {
@@ -987,6 +999,7 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   a.out_idx = out_idx;
   a.out_scores = out_scores;
   a.qh0 = 0;
+  set_header_check(a, d, L, index, w.status);
   const int64_t QH = (int64_t)T * Hq;
 
 #define LSA_CHECK(what)                                                              \

@@ -36,7 +36,42 @@ struct SelArgs {
   int32_t* out_idx;            // [QH][width]
   float* out_scores;           // [QH][k] or null
   int64_t qh0;                 // first query head of this launch
+  const uint32_t* hdr;         // the blob's header
+  uint32_t hx[kHeaderCheckWords];   // header words the descriptor implies
+  int* status;                 // the call's device status (LSA_OK / LSA_ERR_BAD_INDEX)
 };
+
+// Wave-wide: does the blob's header hold what the call's descriptor implies
+// (magic, version, shape fields, total size, a zero build status)?  Reads the
+// first kHeaderCheckWords words of the blob and nothing else.
+__device__ __forceinline__ bool header_matches(const SelArgs& a) {
+  const int lane = lane_id();
+  uint32_t want = 0u;
+#pragma unroll
+  for (int i = 0; i < kHeaderCheckWords; ++i)
+    if (lane == i) want = a.hx[i];
+  const bool cmp = lane < kHeaderCheckWords && ((kHeaderCheckMask >> lane) & 1u);
+  const uint32_t got = cmp ? a.hdr[lane] : want;
+  return __ballot(got != want) == 0ull;
+}
+
+// Host: what the kernels of a call compare the blob's header with, and where
+// the call's status word lives.
+inline void set_header_check(SelArgs& a, const lsa_index_desc& d, const Layout& L, const void* index,
+                             int* status) {
+  const BlobHeader want = make_header(d, L);
+  a.hdr = (const uint32_t*)index;
+  for (int i = 0; i < kHeaderCheckWords; ++i) a.hx[i] = want.w[i];
+  a.status = status;
+}
+
+// First kernel of a select call: the header check, whose result workgroup 0
+// leaves in the status word for the kernels that follow.
+__device__ __forceinline__ bool check_index_first(const SelArgs& a) {
+  const bool ok = header_matches(a);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.status = ok ? LSA_OK : LSA_ERR_BAD_INDEX;
+  return ok;
+}
 
 template <typename LT, int DL>
 __device__ __forceinline__ float row_dot(const LT* row, const float* q) {

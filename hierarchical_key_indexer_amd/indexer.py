@@ -61,6 +61,12 @@ class LatentIndex:
         sec = self.index[off:off + hk * (nodes + 1) * 4].view(torch.int32).view(hk, nodes + 1)
         return np.diff(sec.cpu().numpy().astype(np.int64), axis=1)
 
+    def device_status(self, which: str = "select") -> int:
+        """Device status of the last select ("select") or flat select
+        ("flat") call on this index, read after it finished: LSA_OK, or
+        LSA_ERR_BAD_INDEX when the blob did not match the descriptor."""
+        return _abi.device_status(self._ws[which])
+
     def flat_select(self, queries, q_pos, params, scores=True, out=None, stream=None):
         t, hq = queries.shape[0], queries.shape[1]
         ws = self.workspace("flat", _abi.flat_workspace_bytes(self.desc, params, t, hq))

@@ -25,6 +25,16 @@
  *    lsa_last_error() describes it.  No call aborts, exits or throws.
  *  - Status codes: lsa_status.  LSA_ERR_HIP reports a launch failure; faults
  *    inside kernels surface at the caller's next synchronisation.
+ *  - Device status of a select call (lsa_select, lsa_flat_select): the host
+ *    cannot read the device-resident blob without a synchronisation, so the
+ *    first kernel of the call compares the blob's header (magic, version,
+ *    n_keys, n_kv_heads, d_head, d_latent, dtypes, n_levels, fanouts, build
+ *    status, total bytes) with what `desc` implies, before it reads anything
+ *    else of the blob.  The result, an int32 lsa_status, lands in bytes
+ *    [0, 4) of the workspace: LSA_OK, or LSA_ERR_BAD_INDEX on a mismatch.  On
+ *    LSA_ERR_BAD_INDEX no kernel reads past the header, every output row is
+ *    all -1, scores are -inf and leaves -1.  The caller reads the word after
+ *    synchronising.  The blob must hold at least its 256-byte header.
  *  - Query head hq reads KV head hq / G with G = n_q_heads / n_kv_heads.
  *  - Dtypes: keys and queries are fp32 or bf16 (the same for both); the
  *    latent store is fp32 or bf16.  All dot products accumulate in fp32.
