@@ -22,7 +22,8 @@ EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "l
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
            "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
            "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map",
-           "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention")
+           "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention", "lsa_select_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
 PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
 
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_flat_select_path.argtypes, lib.lsa_flat_select_path.restype = [D, S, I32, I32], I32
     lib.lsa_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
     lib.lsa_select.restype = ctypes.c_int
+    lib.lsa_select_noalloc.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP]
+    lib.lsa_select_noalloc.restype = ctypes.c_int
     lib.lsa_flat_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, SZ, VP]
     lib.lsa_flat_select.restype = ctypes.c_int
     lib.lsa_last_error.argtypes, lib.lsa_last_error.restype = [], ctypes.c_char_p
@@ -191,6 +194,15 @@ def lsa_select(desc, index, queries, q_pos, params, out_idx, out_scores=None, ou
     _check(load().lsa_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
                              ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(out_leaves),
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def lsa_select_noalloc(desc, index, queries, q_pos, params, out_idx, out_scores=None, out_leaves=None,
+                       stream=None) -> None:
+    """lsa_select on the library's static device scratch (no workspace)."""
+    t, hq = queries.shape[0], queries.shape[1]
+    _check(load().lsa_select_noalloc(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
+                                     ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(out_leaves),
+                                     _stream(stream)))
 
 
 def lsa_flat_select(desc, index, queries, q_pos, params, out_idx, out_scores=None, workspace=None,

@@ -4,7 +4,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lsa_internal.h"
+
+// Device scratch of lsa_select_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in); it uses the device address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[LSA_NOALLOC_SCRATCH_BYTES];
 
 namespace lsa {
 size_t build_workspace_bytes(const lsa_index_desc& d);
@@ -213,6 +221,60 @@ int lsa_select(const lsa_index_desc* desc, const void* index, const void* querie
                float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes, void* stream) {
   return select_common(desc, index, queries, q_pos, n_tokens, n_q_heads, params, out_idx, out_scores, out_leaves,
                        workspace, workspace_bytes, stream, false);
+}
+
+// Device address of `scratch` on the current device, found once per device.
+static int scratch_on_current_device(void** out, char* err, size_t errlen) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    snprintf(err, errlen, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return LSA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= 64) {
+    snprintf(err, errlen, "device %d outside the 64 devices the static scratch supports", dev);
+    return LSA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      snprintf(err, errlen, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return LSA_ERR_HIP;
+    }
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return LSA_OK;
+}
+
+int lsa_select_noalloc(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+                       int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+                       float* out_scores, int32_t* out_leaves, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc == LSA_OK) rc = check_params(desc, params, false);
+  if (rc == LSA_OK) rc = check_shape(desc, n_tokens, n_q_heads, false);
+  if (rc != LSA_OK) return rc;
+  if (n_tokens == 0) return LSA_OK;
+  if (!index || !queries || !q_pos || !out_idx)
+    return fail(LSA_ERR_INVALID_ARG, "index, queries, q_pos and out_idx must be non-NULL");
+  const lsa::SelectPlan plan = lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false);
+  if (plan.bytes > (size_t)LSA_NOALLOC_SCRATCH_BYTES)
+    return fail(LSA_ERR_UNSUPPORTED,
+                "this batch needs %zu bytes of workspace; the static scratch holds %u (call lsa_select with a "
+                "workspace)", plan.bytes, (unsigned)LSA_NOALLOC_SCRATCH_BYTES);
+  char err[256] = {0};
+  void* ws = nullptr;
+  rc = scratch_on_current_device(&ws, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  rc = lsa::launch_select(*desc, *params, plan, index, queries, q_pos, n_tokens, n_q_heads, out_idx, out_scores,
+                          out_leaves, ws, (hipStream_t)stream, false, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
 }
 
 int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,

@@ -190,6 +190,27 @@ int lsa_select(const lsa_index_desc* desc, const void* index, const void* querie
                float* out_scores, int32_t* out_leaves, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* lsa_select without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a fixed scratch buffer of
+ * LSA_NOALLOC_SCRATCH_BYTES inside the library: one copy per GPU, set up on
+ * the first call on that device and held until the process ends.  The call
+ * allocates nothing.  Same arguments (minus the workspace), kernels and
+ * results as lsa_select.
+ * Errors: those of lsa_select; LSA_ERR_UNSUPPORTED when the batch needs more
+ * workspace than the scratch holds (lsa_select_workspace_bytes tells; decode
+ * batches of the 1M and 10M configurations need about 13 MiB); LSA_ERR_HIP if
+ * the scratch cannot be located.  Every call on a GPU uses that GPU's one
+ * scratch: calls that overlap on one GPU (concurrent streams, or threads)
+ * race and must be serialised by the caller.  The scratch keeps the last
+ * call's contents; the kernels clear what they need.  The device status word
+ * of a call sits in the scratch, so a mismatched index shows only as all -1
+ * rows here. */
+#define LSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lsa_select_noalloc(const lsa_index_desc* desc, const void* index, const void* queries, const int32_t* q_pos,
+                       int32_t n_tokens, int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx,
+                       float* out_scores, int32_t* out_leaves, void* stream);
+
 /* How lsa_select computes a batch of this shape (same result either way):
  *   LSA_PATH_PER_QUERY_HEAD  every query head descends and gathers on its own
  *                            (decode and small batches)

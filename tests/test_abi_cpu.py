@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(A):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = A.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -165,3 +165,20 @@ def test_flat_select_path_follows_the_batch_shape(A):
         A.PATH_PER_QUERY_HEAD
     with pytest.raises(A.LsaError):
         A.flat_select_path(d, p, 1, 7)
+
+
+def test_noalloc_select_refuses_batches_beyond_its_scratch(A):
+    """A batch whose workspace exceeds the static scratch is refused before
+    anything is enqueued (no GPU needed); decode batches of the 1M and 10M
+    configurations fit."""
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    for name in ("decode_1m", "decode_10m"):
+        wl = get_workload(name)
+        d = A.IndexDesc.of(wl)
+        p = A.SelectParams.make(wl.b, wl.k, wl.sink, wl.window)
+        assert A.select_workspace_bytes(d, p, 1, wl.n_q_heads) <= A.NOALLOC_SCRATCH_BYTES
+        need = A.select_workspace_bytes(d, p, 4096, wl.n_q_heads)
+        assert need > A.NOALLOC_SCRATCH_BYTES
+        rc = A.load().lsa_select_noalloc(ctypes.byref(d), fake, fake, fake, 4096, wl.n_q_heads, ctypes.byref(p),
+                                         fake, None, None, None)
+        assert rc == A.LSA_ERR_UNSUPPORTED and "static scratch" in A.last_error()
