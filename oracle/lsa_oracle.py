@@ -468,14 +468,16 @@ def descend(hidx: HeadIndex, fanout: tuple, qlat: np.ndarray, b: int, beam: str)
 
 
 def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectParams, flat: bool = False,
-               leaves=None) -> dict:
+               leaves=None, appended=None) -> dict:
     """The whole selection of one query head at position p.
 
     Candidates are the members of the selected leaves (all keys when ``flat``)
     that fall in C(p); each is scored s_j = q~ . k~_j; the top-k by (s desc,
     j asc) are kept (Wink Pings: after the clusters are scored, only the keys
     inside the chosen clusters are scored).  Fewer than k candidates: all of them.  ``leaves`` replaces the
-    descent by a given leaf set (the key stage alone).
+    descent by a given leaf set (the key stage alone).  ``appended`` (the
+    head's ``Appended`` keys) adds the keys that joined the selected leaves
+    after the build, at positions N, N + 1, ...
     """
     hidx = idx.heads[h]
     _, _, (lo, hi) = segments(p, prm.sink, prm.window)
@@ -492,11 +494,18 @@ def select_one(idx: OracleIndex, h: int, qlat: np.ndarray, p: int, prm: SelectPa
     j = hidx.perm[rows]
     keep = (j >= lo) & (j <= hi)
     rows, j = rows[keep], j[keep]
-    s = hidx.csr_latent[rows] @ qlat
+    lat = hidx.csr_latent[rows]
+    if appended is not None and len(appended.leaf):
+        aj = len(hidx.perm) + np.arange(len(appended.leaf), dtype=np.int64)
+        mine = np.ones(len(aj), dtype=bool) if flat else np.isin(appended.leaf, leaves)
+        mine &= (aj >= lo) & (aj <= hi)
+        j = np.concatenate([j, aj[mine]])
+        lat = np.concatenate([lat, appended.latent[mine]])
+    s = lat @ qlat
     order = np.lexsort((j, -s))[:prm.k]
     top_j, top_s = j[order], s[order]
     asc = np.argsort(top_j, kind="stable")
-    return dict(leaves=leaves, cand_idx=j, cand_scores=s, cand_scale=dot_scale(qlat, hidx.csr_latent[rows]),
+    return dict(leaves=leaves, cand_idx=j, cand_scores=s, cand_scale=dot_scale(qlat, lat),
                 top_idx=top_j[asc], top_scores=top_s[asc],
                 kth=top_s[-1] if len(j) > prm.k else -np.inf)
 
@@ -513,12 +522,14 @@ def _row(res: dict, p: int, prm: SelectParams):
 
 
 def select(idx: OracleIndex, queries: np.ndarray, q_pos: np.ndarray, prm: SelectParams,
-           flat: bool = False, pairs=None):
+           flat: bool = False, pairs=None, appended=None):
     """Output rows [sink | top-k (ascending index) | window], -1 padded, for
     every (token, query head), or only for the listed ``pairs``.
 
-    Query head hq uses KV head hq // G.  Returns (rows, scores, leaves, results)
-    where ``results[(t, hq)]`` keeps the per-query detail.
+    Query head hq uses KV head hq // G.  ``appended`` (one ``Appended`` per KV
+    head) adds keys that joined the index after its build.  Returns (rows,
+    scores, leaves, results) where ``results[(t, hq)]`` keeps the per-query
+    detail.
     """
     desc = idx.desc
     t_n, hq_n = queries.shape[0], queries.shape[1]
@@ -529,7 +540,7 @@ def select(idx: OracleIndex, queries: np.ndarray, q_pos: np.ndarray, prm: Select
         h = hq // g
         p = int(q_pos[t])
         qlat = query_latent(queries[t, hq], idx.heads[h], desc.key_dtype, desc.latent_dtype)
-        res = select_one(idx, h, qlat, p, prm, flat=flat)
+        res = select_one(idx, h, qlat, p, prm, flat=flat, appended=None if appended is None else appended[h])
         res["qlat"] = qlat
         rows[(t, hq)], scores[(t, hq)] = _row(res, p, prm)
         leaves[(t, hq)] = res["leaves"]
@@ -537,10 +548,92 @@ def select(idx: OracleIndex, queries: np.ndarray, q_pos: np.ndarray, prm: Select
     return rows, scores, leaves, results
 
 
-def flat_select(idx: OracleIndex, queries, q_pos, prm: SelectParams, pairs=None):
+def flat_select(idx: OracleIndex, queries, q_pos, prm: SelectParams, pairs=None, appended=None):
     """Full-scan indexer: every key of C(p) is a candidate (the quadratic path
     that scores every key, drawn dashed in the bayesiansapien flowchart)."""
-    return select(idx, queries, q_pos, prm, flat=True, pairs=pairs)
+    return select(idx, queries, q_pos, prm, flat=True, pairs=pairs, appended=appended)
+
+
+# ----------------------------------------------------------------------------
+# incremental upkeep: keys that arrive after the build
+# ----------------------------------------------------------------------------
+# Every decode step adds a key to the cache; the pages say the cache stays
+# full length ("Gaps" on the bayesiansapien wiki) and that decode runs inside
+# a captured loop ("Can I run LSA?" on wpnews), but nothing about how new
+# keys enter the index.  Reading: a new key joins the tree without changing
+# it.  Its latent is computed as the build computes every key's; it then
+# descends from the root, at every level to the child of the current node
+# whose stored (fp32) centroid is nearest in squared Euclidean distance among
+# the children that hold keys, ties to the lowest child id (the build's own
+# assignment rule, applied once with the centroids held fixed).  The leaf it
+# reaches holds it from then on, so a query that keeps that leaf scores it.
+# Centroids and earlier members do not move; re-clustering is a new build.
+# The i-th key appended to a KV head sits at position N + i.
+
+
+@dataclasses.dataclass
+class Appended:
+    latent: np.ndarray       # [A, d_latent] latent-dtype values, in arrival order
+    leaf: np.ndarray         # [A] leaf id each key joined
+
+
+def route_key(hidx: HeadIndex, fanout: tuple, x: np.ndarray) -> int:
+    """The leaf a latent key x reaches: at every level the nearest non-empty
+    child of the current node (float64 distances, ties to the lowest id)."""
+    node = 0
+    for lev, f in enumerate(fanout):
+        kids = node * f + np.arange(f)
+        nonempty = np.diff(hidx.offsets[lev])[kids] > 0
+        mu = hidx.centroids[lev][kids]
+        d = sq_dists(x[None, :], mu)[0]
+        d[~nonempty] = np.inf
+        node = int(kids[int(np.argmin(d))])
+    return node
+
+
+def append_keys(idx: OracleIndex, keys_new: np.ndarray, prev=None) -> list:
+    """Append keys ``keys_new`` [A, Hkv, d_head] (storage format) to every KV
+    head; ``prev`` holds the keys appended before (None: none).  Returns one
+    ``Appended`` per head, the earlier keys first."""
+    desc = idx.desc
+    out = []
+    for h, hidx in enumerate(idx.heads):
+        lat = latent_keys(keys_new[:, h, :], hidx.W, desc.key_dtype, desc.latent_dtype)
+        leaf = np.array([route_key(hidx, desc.fanout, x) for x in lat], dtype=np.int64)
+        if prev is not None:
+            lat = np.concatenate([prev[h].latent, lat])
+            leaf = np.concatenate([prev[h].leaf, leaf])
+        out.append(Appended(latent=lat, leaf=leaf))
+    return out
+
+
+def index_with_appended(idx: OracleIndex, appended: list) -> OracleIndex:
+    """The index the appended keys define: every appended key placed in its
+    leaf (after the leaf's earlier members, its position being larger), every
+    level's ranges grown to match, centroids unchanged.  Selecting on it is
+    what selecting with ``appended`` must give."""
+    desc = idx.desc
+    n0 = desc.n_keys
+    heads = []
+    for hidx, app in zip(idx.heads, appended):
+        a = len(app.leaf)
+        n_leaves = desc.nodes(desc.n_levels)
+        leaf_all = np.empty(n0 + a, dtype=np.int64)
+        leaf_all[hidx.perm] = np.repeat(np.arange(n_leaves), np.diff(hidx.offsets[-1]))
+        leaf_all[n0:] = app.leaf
+        lat_all = np.empty((n0 + a, hidx.csr_latent.shape[1]))
+        lat_all[hidx.perm] = hidx.csr_latent
+        lat_all[n0:] = app.latent
+        perm = np.argsort(leaf_all, kind="stable")
+        offs, assign = [], []
+        for lev in range(1, desc.n_levels + 1):
+            node_of = leaf_all // (n_leaves // desc.nodes(lev))
+            offs.append(np.concatenate([[0], np.cumsum(np.bincount(node_of, minlength=desc.nodes(lev)))]))
+            assign.append(node_of)
+        heads.append(HeadIndex(W=hidx.W, centroids=hidx.centroids, cscore=hidx.cscore, offsets=offs,
+                               valid=hidx.valid, perm=perm, csr_latent=lat_all[perm], assign=assign))
+    return OracleIndex(desc=dataclasses.replace(desc, n_keys=n0 + max(len(x.leaf) for x in appended)),
+                       heads=heads)
 
 
 # ----------------------------------------------------------------------------

@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     f32_to_bf16_bits,
     gen_keys,
     gen_keys_head_f32,
+    gen_keys_range,
     gen_positions,
     gen_queries,
     gen_W,

@@ -194,6 +194,17 @@ def gen_keys(wl: Workload) -> np.ndarray:
     return out
 
 
+def gen_keys_range(wl: Workload, lo: int, hi: int) -> np.ndarray:
+    """Keys [lo, hi) of every KV head, [hi - lo, Hkv, d_head] in the key
+    storage dtype, drawn as a cache of max(hi, N) keys would hold them: the
+    streams are sequential within a chunk, so positions at or past N are the
+    keys that arrive after a cache of N keys, and positions below N equal
+    gen_keys(wl)."""
+    big = wl.scaled(n_keys=max(hi, wl.n_keys))
+    out = np.stack([gen_keys_head_f32(big, h, lo, hi) for h in range(wl.n_kv_heads)], axis=1)
+    return out if wl.key_dtype == "f32" else f32_to_bf16_bits(out)
+
+
 def gen_W(wl: Workload) -> np.ndarray:
     """Latent maps [Hkv, d_head, d_latent] fp32, entries ~ N(0, 1/d_head)."""
     e = ENTROPY_BASE + wl.cache_id

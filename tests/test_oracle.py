@@ -527,3 +527,14 @@ def test_one_head_readback_matches_the_full_blob():
             assert np.array_equal(one.cscore[lev], ref.cscore[lev])
             assert np.array_equal(one.offsets[lev], ref.offsets[lev])
             assert np.array_equal(one.assign[lev], ref.assign[lev])
+
+
+def test_generator_later_keys_extend_the_cache():
+    """Keys past the cache come from the same sequential streams: a longer
+    cache's first N keys equal the cache, and its tail is gen_keys_range."""
+    wl = S.get_workload("decode_10m").scaled(n_keys=(1 << 20) - 100, n_kv_heads=2, n_centers=64)
+    base = S.gen_keys(wl)
+    longer = S.gen_keys(wl.scaled(n_keys=(1 << 20) + 300))
+    assert np.array_equal(longer[:wl.n_keys], base)
+    assert np.array_equal(S.gen_keys_range(wl, wl.n_keys, wl.n_keys + 400), longer[wl.n_keys:])
+    assert np.array_equal(S.gen_keys_range(wl, 1000, 1500), base[1000:1500])
