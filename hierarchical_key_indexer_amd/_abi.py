@@ -22,7 +22,9 @@ EXPORTS = ("lsa_index_bytes", "lsa_build_workspace_bytes", "lsa_build_index", "l
            "lsa_select_workspace_bytes", "lsa_select_path", "lsa_select", "lsa_flat_workspace_bytes",
            "lsa_flat_select_path", "lsa_flat_select", "lsa_last_error", "lsa_abi_version",
            "lsa_set_profile_events", "lsa_pca_workspace_bytes", "lsa_pca_covariance", "lsa_pca_map",
-           "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention", "lsa_select_noalloc")
+           "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention", "lsa_select_noalloc",
+           "lsa_append_pool_bytes", "lsa_append_keys", "lsa_select_appended_workspace_bytes",
+           "lsa_select_appended")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 STAGE_PROJECT, STAGE_DESCEND, STAGE_GATHER, STAGE_MERGE, STAGE_FLAT, STAGE_SAMPLE = 1, 2, 3, 4, 5, 6
 PATH_PER_QUERY_HEAD, PATH_NODE_MAJOR, PATH_ROW_TILED = 0, 1, 2
@@ -86,6 +88,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsa_flat_select_path.argtypes, lib.lsa_flat_select_path.restype = [D, S, I32, I32], I32
     lib.lsa_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
     lib.lsa_select.restype = ctypes.c_int
+    lib.lsa_append_pool_bytes.argtypes, lib.lsa_append_pool_bytes.restype = [D, I32], SZ
+    lib.lsa_append_keys.argtypes, lib.lsa_append_keys.restype = [D, VP, VP, I32, I32, VP, I32, VP], ctypes.c_int
+    lib.lsa_select_appended_workspace_bytes.argtypes = [D, S, I32, I32]
+    lib.lsa_select_appended_workspace_bytes.restype = SZ
+    lib.lsa_select_appended.argtypes = [D, VP, VP, I32, I32, VP, VP, I32, I32, S, VP, VP, VP, VP, SZ, VP]
+    lib.lsa_select_appended.restype = ctypes.c_int
     lib.lsa_select_noalloc.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, VP]
     lib.lsa_select_noalloc.restype = ctypes.c_int
     lib.lsa_flat_select.argtypes = [D, VP, VP, VP, I32, I32, S, VP, VP, VP, SZ, VP]
@@ -194,6 +202,35 @@ def lsa_select(desc, index, queries, q_pos, params, out_idx, out_scores=None, ou
     _check(load().lsa_select(ctypes.byref(desc), _ptr(index), _ptr(queries), _ptr(q_pos), t, hq,
                              ctypes.byref(params), _ptr(out_idx), _ptr(out_scores), _ptr(out_leaves),
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def append_pool_bytes(desc, capacity) -> int:
+    n = load().lsa_append_pool_bytes(ctypes.byref(desc), capacity)
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def select_appended_workspace_bytes(desc, params, n_tokens, n_q_heads) -> int:
+    n = load().lsa_select_appended_workspace_bytes(ctypes.byref(desc), ctypes.byref(params), n_tokens, n_q_heads)
+    if n == 0:
+        raise LsaError(LSA_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def lsa_append_keys(desc, index, keys, first, pool, capacity, stream=None) -> None:
+    """keys [n_new, Hkv, d] on the GPU into pool slots [first, first + n_new)."""
+    _check(load().lsa_append_keys(ctypes.byref(desc), _ptr(index), _ptr(keys), keys.shape[0], first, _ptr(pool),
+                                  capacity, _stream(stream)))
+
+
+def lsa_select_appended(desc, index, pool, capacity, n_appended, queries, q_pos, params, out_idx, out_scores=None,
+                        out_leaves=None, workspace=None, stream=None) -> None:
+    t, hq = queries.shape[0], queries.shape[1]
+    _check(load().lsa_select_appended(ctypes.byref(desc), _ptr(index), _ptr(pool), capacity, n_appended,
+                                      _ptr(queries), _ptr(q_pos), t, hq, ctypes.byref(params), _ptr(out_idx),
+                                      _ptr(out_scores), _ptr(out_leaves), _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def lsa_select_noalloc(desc, index, queries, q_pos, params, out_idx, out_scores=None, out_leaves=None,

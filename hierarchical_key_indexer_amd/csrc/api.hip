@@ -284,6 +284,75 @@ int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* q
                        workspace, workspace_bytes, stream, true);
 }
 
+// ---- incremental upkeep ---------------------------------------------------------
+
+static int check_pool(const lsa_index_desc* d, int32_t capacity) {
+  if (capacity < 1) return fail(LSA_ERR_INVALID_ARG, "capacity = %d must be >= 1", capacity);
+  if (d->n_keys + (int64_t)capacity >= (int64_t(1) << 31))
+    return fail(LSA_ERR_UNSUPPORTED, "n_keys + capacity must stay below 2^31");
+  return LSA_OK;
+}
+
+size_t lsa_append_pool_bytes(const lsa_index_desc* desc, int32_t capacity) {
+  clear_err();
+  if (check_desc(desc) != LSA_OK || check_pool(desc, capacity) != LSA_OK) return 0;
+  return lsa::pool_layout(*desc, capacity).total;
+}
+
+int lsa_append_keys(const lsa_index_desc* desc, const void* index, const void* keys, int32_t n_new, int32_t first,
+                    void* pool, int32_t capacity, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc == LSA_OK) rc = check_pool(desc, capacity);
+  if (rc != LSA_OK) return rc;
+  if (n_new < 0 || first < 0 || (int64_t)first + n_new > capacity)
+    return fail(LSA_ERR_INVALID_ARG, "slots [%d, %lld) do not fit a pool of %d", first, (long long)first + n_new,
+                capacity);
+  if (n_new == 0) return LSA_OK;
+  if (!index || !keys || !pool) return fail(LSA_ERR_INVALID_ARG, "index, keys and pool must be non-NULL");
+  char err[256] = {0};
+  rc = lsa::launch_append(*desc, index, keys, n_new, first, pool, capacity, (hipStream_t)stream, err, sizeof(err));
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
+size_t lsa_select_appended_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
+                                           int32_t n_tokens, int32_t n_q_heads) {
+  clear_err();
+  if (check_desc(desc) || check_params(desc, params, false) || check_shape(desc, n_tokens, n_q_heads, false)) return 0;
+  return lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false, true).bytes;
+}
+
+int lsa_select_appended(const lsa_index_desc* desc, const void* index, const void* pool, int32_t capacity,
+                        int32_t n_appended, const void* queries, const int32_t* q_pos, int32_t n_tokens,
+                        int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx, float* out_scores,
+                        int32_t* out_leaves, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_err();
+  int rc = check_desc(desc);
+  if (rc == LSA_OK) rc = check_params(desc, params, false);
+  if (rc == LSA_OK) rc = check_shape(desc, n_tokens, n_q_heads, false);
+  if (rc == LSA_OK) rc = check_pool(desc, capacity);
+  if (rc != LSA_OK) return rc;
+  if (n_appended < 0 || n_appended > capacity)
+    return fail(LSA_ERR_INVALID_ARG, "n_appended = %d outside [0, capacity = %d]", n_appended, capacity);
+  if (n_tokens == 0) return LSA_OK;
+  if (!index || !queries || !q_pos || !out_idx || !workspace || (n_appended > 0 && !pool))
+    return fail(LSA_ERR_INVALID_ARG, "index, queries, q_pos, out_idx, workspace and pool must be non-NULL");
+  const lsa::SelectPlan plan = lsa::plan_select(*desc, *params, n_tokens, n_q_heads, false, true);
+  if (workspace_bytes < plan.bytes)
+    return fail(LSA_ERR_BUFFER_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.bytes);
+  lsa::AppendView app;
+  app.pool = pool;
+  app.cap = capacity;
+  app.n = n_appended;
+  app.on = true;
+  char err[256] = {0};
+  rc = lsa::launch_select(*desc, *params, plan, index, queries, q_pos, n_tokens, n_q_heads, out_idx, out_scores,
+                          out_leaves, workspace, (hipStream_t)stream, false, err, sizeof(err), app);
+  if (rc != LSA_OK) return fail(rc, "%s", err);
+  return LSA_OK;
+}
+
 size_t lsa_pca_workspace_bytes(const lsa_index_desc* desc) {
   clear_err();
   if (check_desc(desc) != LSA_OK) return 0;

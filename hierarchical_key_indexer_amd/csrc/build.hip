@@ -21,6 +21,7 @@
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "select_device.h"
 
 namespace lsa {
 
@@ -222,6 +223,32 @@ struct AssignArgs {
   const FixedPoint* fx;             // scale of the member sums
 };
 
+// |mu|^2, summed in index order (one fma per element).
+template <int DL>
+__device__ __forceinline__ float centroid_norm(const float* mu) {
+  float acc = 0.f;
+  for (int j = 0; j < DL; ++j) acc = fmaf(mu[j], mu[j], acc);
+  return acc;
+}
+
+// |mu|^2 - 2 x.mu: the squared distance up to |x|^2, which is common to every
+// centroid.  The assignment of the build and the routing of appended keys
+// both use exactly this arithmetic, so they agree bit for bit.
+template <int DL>
+__device__ __forceinline__ float centroid_dist(const float* x, const float* mu, float mm) {
+  const float4* cr = (const float4*)mu;
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < DL / 4; j += 2) {
+    const float4 u = cr[j], w = cr[j + 1];
+    d0 = fmaf(x[4 * j + 0], u.x, d0); d0 = fmaf(x[4 * j + 1], u.y, d0);
+    d0 = fmaf(x[4 * j + 2], u.z, d0); d0 = fmaf(x[4 * j + 3], u.w, d0);
+    d1 = fmaf(x[4 * j + 4], w.x, d1); d1 = fmaf(x[4 * j + 5], w.y, d1);
+    d1 = fmaf(x[4 * j + 6], w.z, d1); d1 = fmaf(x[4 * j + 7], w.w, d1);
+  }
+  return fmaf(-2.f, d0 + d1, mm);
+}
+
 template <typename LT, int DL, bool ACC, bool LDS_ACC>
 __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -250,11 +277,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
     for (int i = threadIdx.x; i < nv; i += 256) lcnt[i] = 0u;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < nv; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < DL; ++j) acc = fmaf(cs[c * DL + j], cs[c * DL + j], acc);
-    cn[c] = acc;
-  }
+  for (int c = threadIdx.x; c < nv; c += 256) cn[c] = centroid_norm<DL>(cs + c * DL);
   __syncthreads();
 
   const LT* lat = (const LT*)a.lat + (size_t)h * a.lv.N * DL;
@@ -280,17 +303,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(AssignArgs a) {
     float best = __builtin_huge_valf();
     int bc = 0;
     for (int c = 0; c < nv; ++c) {
-      const float4* cr = (const float4*)(cs + c * DL);
-      float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < DL / 4; j += 2) {
-        const float4 u = cr[j], w = cr[j + 1];
-        d0 = fmaf(x[4 * j + 0], u.x, d0); d0 = fmaf(x[4 * j + 1], u.y, d0);
-        d0 = fmaf(x[4 * j + 2], u.z, d0); d0 = fmaf(x[4 * j + 3], u.w, d0);
-        d1 = fmaf(x[4 * j + 4], w.x, d1); d1 = fmaf(x[4 * j + 5], w.y, d1);
-        d1 = fmaf(x[4 * j + 6], w.z, d1); d1 = fmaf(x[4 * j + 7], w.w, d1);
-      }
-      const float d = fmaf(-2.f, d0 + d1, cn[c]);
+      const float d = centroid_dist<DL>(x, cs + c * DL, cn[c]);
       if (d < best) { best = d; bc = c; }
     }
     a.child[(size_t)h * a.lv.N + pos] = (uint8_t)bc;
@@ -451,6 +464,93 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(CsrArgs a) {
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// incremental upkeep: keys appended after the build
+// ---------------------------------------------------------------------------
+
+struct AppendArgs {
+  const void* keys;                // [n_new][Hkv][d_head] key dtype
+  int first;                       // pool slot of keys[0]
+  int d_head;
+  const float* W;                  // [Hkv][d_head][DL] (the blob's latent map)
+  const float* cent[kMaxLevels];   // [Hkv][P_l][DL] stored centroids
+  const int* off[kMaxLevels];      // [Hkv][P_l + 1] CSR ranges (non-empty children)
+  int F[kMaxLevels];
+  int64_t P[kMaxLevels];
+  int L;
+  int* pool_leaf;                  // [Hkv][cap]
+  void* pool_lat;                  // [Hkv][cap][DL]
+  int64_t cap;
+  const uint32_t* hdr;             // the blob's header and the words it must hold
+  uint32_t hx[kHeaderCheckWords];
+};
+
+// One workgroup per (appended key, KV head).  The key's latent is computed
+// as the build computes every key's (fp32 fma over d_head in index order,
+// one rounding to the latent dtype), then it descends from the root: at each
+// level the child of the current node with the smallest |mu|^2 - 2 x.mu
+// (the build's own assignment arithmetic) among the children that hold keys,
+// ties to the lowest child.  The pool slot gets the leaf and the latent; a
+// blob whose header does not match leaves the slot's leaf at -1 (never a
+// member of anything).
+template <typename KT, typename LT, int DL>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ float xk[256];
+  __shared__ __align__(16) float x[DL];
+  __shared__ u64 wmin[4];
+  const int i = blockIdx.x, h = blockIdx.y, Hkv = gridDim.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const size_t slot = (size_t)h * a.cap + a.first + i;
+  if (!header_words_match(a.hdr, a.hx)) {      // block-uniform
+    if (threadIdx.x == 0) a.pool_leaf[slot] = -1;
+    return;
+  }
+  const KT* key = (const KT*)a.keys + ((size_t)i * Hkv + h) * a.d_head;
+  for (int k = threadIdx.x; k < a.d_head; k += 256) xk[k] = KeyLoad<KT>::get(key, k);
+  __syncthreads();
+  if (threadIdx.x < DL) {
+    const float* Wh = a.W + (size_t)h * a.d_head * DL + threadIdx.x;
+    float acc = 0.f;
+    for (int k = 0; k < a.d_head; ++k) acc = fmaf(xk[k], Wh[(size_t)k * DL], acc);
+    const float v = Lat<LT>::PER16 == 8 ? round_to_bf16(acc) : acc;
+    x[threadIdx.x] = v;
+    if (Lat<LT>::PER16 == 8) ((bf16_t*)a.pool_lat)[slot * DL + threadIdx.x] = (bf16_t)(__float_as_uint(v) >> 16);
+    else ((float*)a.pool_lat)[slot * DL + threadIdx.x] = v;
+  }
+  __syncthreads();
+  int64_t node = 0;
+  for (int l = 0; l < a.L; ++l) {
+    const int F = a.F[l];
+    const int64_t kid = node * F + threadIdx.x;
+    u64 key = ~0ull;
+    if ((int)threadIdx.x < F) {
+      const int* off = a.off[l] + (size_t)h * (a.P[l] + 1);
+      if (off[kid + 1] > off[kid]) {
+        const float* mu = a.cent[l] + ((size_t)h * a.P[l] + kid) * DL;
+        const float d = centroid_dist<DL>(x, mu, centroid_norm<DL>(mu));
+        key = ((u64)order_u32(d) << 32) | (u64)threadIdx.x;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const u64 y = ((u64)(uint32_t)__shfl_xor((int)(key >> 32), o, 64) << 32) |
+                    (uint32_t)__shfl_xor((int)(uint32_t)key, o, 64);
+      key = y < key ? y : key;
+    }
+    if (lane == 0) wmin[w] = key;
+    __syncthreads();
+    u64 m = wmin[0];
+    for (int ww = 1; ww < 4; ++ww) m = wmin[ww] < m ? wmin[ww] : m;
+    __syncthreads();
+    if (m == ~0ull) {                          // no child holds keys (not for a node that holds some)
+      node = -1;
+      break;
+    }
+    node = node * F + (int64_t)(uint32_t)m;
+  }
+  if (threadIdx.x == 0) a.pool_leaf[slot] = (int)node;
 }
 
 // ---------------------------------------------------------------------------
@@ -671,6 +771,50 @@ int run_build(const lsa_index_desc& d, const void* keys, const float* W, void* i
 }  // namespace
 
 size_t build_workspace_bytes(const lsa_index_desc& d) { return carve_build(d, nullptr, nullptr); }
+
+int launch_append(const lsa_index_desc& d, const void* index, const void* keys, int32_t n_new, int32_t first,
+                  void* pool, int32_t cap, hipStream_t st, char* err, size_t errlen) {
+  if (n_new == 0) return LSA_OK;
+  const Layout L = compute_layout(d);
+  const PoolLayout PL = pool_layout(d, cap);
+  const char* blob = (const char*)index;
+  AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.keys = keys;
+  a.first = first;
+  a.d_head = d.d_head;
+  a.W = (const float*)(blob + L.W);
+  for (int l = 0; l < d.n_levels; ++l) {
+    a.cent[l] = (const float*)(blob + L.cent[l]);
+    a.off[l] = (const int*)(blob + L.offsets[l]);
+    a.F[l] = d.fanout[l];
+    a.P[l] = L.nodes[l + 1];
+  }
+  a.L = d.n_levels;
+  a.pool_leaf = (int*)((char*)pool + PL.leaf);
+  a.pool_lat = (char*)pool + PL.latent;
+  a.cap = cap;
+  const BlobHeader want = make_header(d, L);
+  a.hdr = (const uint32_t*)index;
+  for (int i = 0; i < kHeaderCheckWords; ++i) a.hx[i] = want.w[i];
+  const dim3 grid((unsigned)n_new, (unsigned)d.n_kv_heads);
+  const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
+#define LSA_APPEND(KT, LT, DLV) hipLaunchKernelGGL((append_kernel<KT, LT, DLV>), grid, dim3(256), 0, st, a)
+  if (d.d_latent == 64) {
+    if (kb && lb) LSA_APPEND(bf16_t, bf16_t, 64);
+    else if (kb) LSA_APPEND(bf16_t, float, 64);
+    else if (lb) LSA_APPEND(float, bf16_t, 64);
+    else LSA_APPEND(float, float, 64);
+  } else {
+    if (kb && lb) LSA_APPEND(bf16_t, bf16_t, 32);
+    else if (kb) LSA_APPEND(bf16_t, float, 32);
+    else if (lb) LSA_APPEND(float, bf16_t, 32);
+    else LSA_APPEND(float, float, 32);
+  }
+#undef LSA_APPEND
+  LSA_LAUNCH_CHECK();
+  return LSA_OK;
+}
 
 int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void* index, void* ws,
                  hipStream_t stream, char* err, size_t errlen) {

@@ -87,6 +87,19 @@ inline BlobHeader make_header(const lsa_index_desc& d, const Layout& L) {
 constexpr int kHeaderCheckWords = 20;
 constexpr uint32_t kHeaderCheckMask = 0xFFFFFu & ~((1u << 14) | (1u << 16) | (1u << 17));
 
+// Byte offsets of an append pool of `cap` keys per KV head (lsa.h): the leaf
+// each appended key joined, then its latent row.
+struct PoolLayout {
+  size_t leaf = 0, latent = 0, total = 0;
+};
+inline PoolLayout pool_layout(const lsa_index_desc& d, int64_t cap) {
+  PoolLayout P;
+  P.leaf = 0;
+  P.latent = align_up((size_t)(d.n_kv_heads * cap * 4));
+  P.total = align_up(P.latent + (size_t)(d.n_kv_heads * cap * d.d_latent * latent_elem_bytes(d)));
+  return P;
+}
+
 // Bump allocator over a caller workspace; with base == nullptr it only sizes.
 struct Carver {
   char* base;
@@ -104,6 +117,10 @@ struct Carver {
 size_t build_workspace_bytes(const lsa_index_desc& d);
 int launch_build(const lsa_index_desc& d, const void* keys, const float* W, void* index, void* ws,
                  hipStream_t stream, char* err, size_t errlen);
+
+// ---- incremental upkeep (build.hip) ---------------------------------------------
+int launch_append(const lsa_index_desc& d, const void* index, const void* keys, int32_t n_new, int32_t first,
+                  void* pool, int32_t cap, hipStream_t stream, char* err, size_t errlen);
 
 // ---- training-free latent map (pca.hip) ---------------------------------------
 size_t pca_workspace_bytes(const lsa_index_desc& d);
@@ -166,14 +183,25 @@ struct SelectPlan {
   int nl_cap;          // leaf-list capacity per query head
   int splits;          // workgroups per query head in the gather (1 = direct)
   int flat_splits;     // workgroups per (token, KV head) in the flat scan
+  bool appended;       // appended mode (sorted leaf ids kept for the pool's membership test)
   size_t bytes;        // workspace bytes
   PfPlan pf;           // node-major prefill path (pf.ok)
   FsPlan fs;           // row-tiled full scan (fs.ok)
 };
-SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat);
+// Keys appended after the build (lsa_select_appended): a pool of `cap` keys
+// per KV head, the first `n` of them in use.
+struct AppendView {
+  const void* pool = nullptr;
+  int64_t cap = 0;
+  int n = 0;
+  bool on = false;             // appended mode: the per-query-head path, with the pool's keys
+};
+
+SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat,
+                       bool appended = false);
 int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& plan,
                   const void* index, const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq,
                   int32_t* out_idx, float* out_scores, int32_t* out_leaves, void* ws, hipStream_t stream,
-                  bool flat, char* err, size_t errlen);
+                  bool flat, char* err, size_t errlen, const AppendView& app = AppendView());
 
 }  // namespace lsa

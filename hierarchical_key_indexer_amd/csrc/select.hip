@@ -313,6 +313,21 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
       nf = compact_ids<BLOCK>(fb, a.b, fa, wsum);
     }
   }
+  if (a.leafid) {
+    // the kept leaves in ascending id order (the per-parent frontier already
+    // is; a global beam's is in score order: each leaf's rank is the number
+    // of smaller ids, ids being distinct)
+    int* lid = a.leafid + qh * a.nl_cap;
+    for (int i = threadIdx.x; i < nf; i += BLOCK) {
+      int rank = i;
+      if (a.beam == LSA_BEAM_GLOBAL) {
+        rank = 0;
+        for (int j2 = 0; j2 < nf; ++j2) rank += fa[j2] < fa[i] ? 1 : 0;
+      }
+      lid[rank] = fa[i];
+    }
+    __syncthreads();
+  }
   // leaf list: CSR row starts and exclusive prefix of member counts
   const int* offL = a.off[a.L - 1] + (size_t)h * (a.P[a.L - 1] + 1);
   int* lrow = a.leafrow + qh * a.nl_cap;
@@ -350,7 +365,7 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
   const int t = (int)(qh / a.Hq);
   const int p = a.q_pos[t];
   u64 tau = 0ull;
-  if (p >= 0 && (int64_t)p < a.N && (int64_t)total > 4 * (int64_t)a.k) {
+  if (p >= 0 && (int64_t)p < a.Npos && (int64_t)total > 4 * (int64_t)a.k) {
     // every wave scores 64 of BLOCK evenly spaced candidates and keeps its
     // r-th best (r = expected share of 2k); tau is the median wave value
     const int64_t NS = BLOCK;
@@ -436,6 +451,7 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   u64* buf = (u64*)smem;
   int* lpre = (int*)(buf + CAP);
   int* lrow = lpre + a.nl_cap + 1;
+  int* lid = lrow + a.nl_cap;                 // appended mode: the leaves, ascending
 
   __shared__ float qs[DL];
   const int64_t qh = a.qh0 + blockIdx.y;
@@ -470,8 +486,10 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
     if (threadIdx.x < DL) qs[threadIdx.x] = qv;
     for (int i = threadIdx.x + R * BLOCK; i < np; i += BLOCK) lpre[i] = gp[i];
     for (int i = threadIdx.x + R * BLOCK; i < a.nl_cap; i += BLOCK) lrow[i] = gr[i];
+    if (a.leafid)
+      for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) lid[i] = a.leafid[qh * a.nl_cap + i];
   }
-  if (bad || p < 0 || (int64_t)p >= a.N) {
+  if (bad || p < 0 || (int64_t)p >= a.Npos) {
     if (a.S == 1)
       write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
@@ -480,10 +498,14 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
   __syncthreads();
   const int64_t total = lpre[nl];
   const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
+  // appended keys: this workgroup's share of the pool's slots
+  const int64_t plo = (int64_t)a.app_n * s / a.S, phi = (int64_t)a.app_n * (s + 1) / a.S;
   int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs, qs);
+  if (a.app_n > 0) n = pool_stream<LT, DL, M, BLOCK>(a, h, clo, chi, lid, nl, plo, phi, thr0, buf, n, &n_sh, &rs, qs);
   if (a.S == 1 && n < a.k && thr0 != 0ull) {
     // the sampled threshold let fewer than k keys through: redo without it
     n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs, qs);
+    if (a.app_n > 0) n = pool_stream<LT, DL, M, BLOCK>(a, h, clo, chi, lid, nl, plo, phi, 0ull, buf, n, &n_sh, &rs, qs);
   }
   if (a.S > 1) {
     if (n > a.k) {
@@ -643,7 +665,7 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   const int p = a.q_pos[t];
   const int bad = *a.status;
-  if (bad || p < 0 || (int64_t)p >= a.N) {
+  if (bad || p < 0 || (int64_t)p >= a.Npos) {
     write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
     return;
   }
@@ -670,13 +692,19 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
     // candidate of this query head here, without it
     int* lpre = (int*)(buf + CAP);
     int* lrow = lpre + a.nl_cap + 1;
+    int* lid = lrow + a.nl_cap;
     const int nl = a.nleaf[qh];
     for (int i = threadIdx.x; i <= nl; i += BLOCK) lpre[i] = a.leafpre[qh * (a.nl_cap + 1) + i];
     for (int i = threadIdx.x; i < nl; i += BLOCK) lrow[i] = a.leafrow[qh * a.nl_cap + i];
+    if (a.leafid)
+      for (int i = threadIdx.x; i < nl; i += BLOCK) lid[i] = a.leafid[qh * a.nl_cap + i];
     __syncthreads();
     const int h = (int)(qh % a.Hq) / a.G;
     int n = gather_stream<LT, DL, M, 4, BLOCK>(a, qh, h, a.sink, p - a.window, lpre, lrow, nl, 0, lpre[nl], 0ull,
                                                buf, &n_sh, &rs);
+    if (a.app_n > 0)
+      n = pool_stream<LT, DL, M, BLOCK>(a, h, a.sink, p - a.window, lid, nl, 0, a.app_n, 0ull, buf, n, &n_sh, &rs,
+                                        a.qlat + qh * DL);
     write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
                               a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     return;
@@ -893,6 +921,7 @@ constexpr int kFlatR = 40;                 // samples expected above a full-scan
 
 struct SelWs {
   int* status;
+  int* leafid;
   float* qlat;
   int* leafrow;
   int* leafpre;
@@ -910,10 +939,12 @@ size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const S
   w.status = c.take<int>(64);                 // byte 0 of the workspace (lsa.h)
   w.qlat = c.take<float>((size_t)(qh * d.d_latent));
   w.leafrow = w.leafpre = w.nleaf = nullptr;
+  w.leafid = nullptr;
   if (!flat) {
     w.leafrow = c.take<int>((size_t)(qh * pl.nl_cap));
     w.leafpre = c.take<int>((size_t)(qh * (pl.nl_cap + 1)));
     w.nleaf = c.take<int>((size_t)qh);
+    if (pl.appended) w.leafid = c.take<int>((size_t)(qh * pl.nl_cap));
   }
   w.tau = c.take<unsigned long long>((size_t)qh);
   const int S = flat ? pl.flat_splits : pl.splits;
@@ -935,7 +966,7 @@ void allow_lds(KERNEL* k, size_t bytes) {
 template <typename LT, int DL, int M>
 void launch_merge(SelArgs a, int64_t QH, int64_t chunk, hipStream_t st) {
   auto mk = merge_kernel<LT, DL, kMergeBlock, M>;
-  const size_t mlds = (size_t)M * kMergeBlock * 8 + ((size_t)a.nl_cap * 2 + 2) * 4;
+  const size_t mlds = (size_t)M * kMergeBlock * 8 + ((size_t)a.nl_cap * 3 + 2) * 4;
   allow_lds(mk, mlds);
   for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
     a.qh0 = q0;
@@ -956,7 +987,7 @@ template <typename KT, typename LT, int DL>
 int run_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& pl, const void* index,
                const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, bool flat, char* err,
-               size_t errlen) {
+               size_t errlen, const AppendView& app) {
   const Layout L = compute_layout(d);
   const char* blob = (const char*)index;
   SelWs w;
@@ -1000,6 +1031,16 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   a.out_scores = out_scores;
   a.qh0 = 0;
   set_header_check(a, d, L, index, w.status);
+  a.Npos = d.n_keys;
+  a.leafid = w.leafid;
+  if (app.on && app.n > 0) {
+    const PoolLayout PL = pool_layout(d, app.cap);
+    a.app_leaf = (const int*)((const char*)app.pool + PL.leaf);
+    a.app_lat = (const char*)app.pool + PL.latent;
+    a.app_cap = app.cap;
+    a.app_n = app.n;
+    a.Npos = d.n_keys + app.n;
+  }
   const int64_t QH = (int64_t)T * Hq;
 
 #define LSA_CHECK(what)                                                              \
@@ -1033,12 +1074,14 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
     constexpr int U = 8;
     const int GB = 256;
     const int KPWG = 64 / (DL * (int)sizeof(LT) / 16);
-    const int needg = p.k + (GB / 64) * KPWG * U > 2 * p.k ? p.k + (GB / 64) * KPWG * U : 2 * p.k;
+    // room for a round of appends above k (a round of the pool scan is one key per thread)
+    const int roundg = std::max((GB / 64) * KPWG * U, GB);
+    const int needg = p.k + roundg > 2 * p.k ? p.k + roundg : 2 * p.k;
     const int M = pick_m(needg, GB);
 #define LSA_GATHER(MV, BV)                                                                      \
   {                                                                                             \
     auto gk = gather_kernel<LT, DL, MV, U, BV>;                                                 \
-    const size_t glds = (size_t)MV * BV * 8 + ((size_t)pl.nl_cap * 2 + 2) * 4;                  \
+    const size_t glds = (size_t)MV * BV * 8 + ((size_t)pl.nl_cap * 3 + 2) * 4;                  \
     allow_lds(gk, glds);                                                                        \
     prof_begin(LSA_STAGE_GATHER, st);                                                           \
     for (int64_t q0 = 0; q0 < QH; q0 += chunk) {                                                \
@@ -1162,9 +1205,11 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
 
 }  // namespace
 
-SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat) {
+SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int32_t T, int32_t Hq, bool flat,
+                       bool appended) {
   SelectPlan pl;
   pl.qh = (int64_t)T * Hq;
+  pl.appended = appended && !flat;
   pl.nl_cap = p.beam == LSA_BEAM_GLOBAL ? p.b : ipow(p.b, d.n_levels);
   const Layout L = compute_layout(d);
   const double avg_leaf = (double)d.n_keys / (double)L.nodes[d.n_levels];
@@ -1191,10 +1236,10 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   pl.bytes = carve_select(d, p, pl, T, Hq, flat, nullptr, nullptr);
   memset(&pl.pf, 0, sizeof(pl.pf));
   memset(&pl.fs, 0, sizeof(pl.fs));
-  if (!flat) {
+  if (!flat && !pl.appended) {
     pl.pf = plan_prefill(d, p, T, Hq);
     if (pl.pf.ok) pl.bytes = pl.pf.bytes;
-  } else {
+  } else if (flat) {
     pl.fs = plan_flat_tiled(d, p, T, Hq);
     if (pl.fs.ok) pl.bytes = pl.fs.bytes;
   }
@@ -1204,14 +1249,14 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
 int launch_select(const lsa_index_desc& d, const lsa_select_params& p, const SelectPlan& pl, const void* index,
                   const void* queries, const int32_t* q_pos, int32_t T, int32_t Hq, int32_t* out_idx,
                   float* out_scores, int32_t* out_leaves, void* ws, hipStream_t st, bool flat, char* err,
-                  size_t errlen) {
+                  size_t errlen, const AppendView& app) {
   if (!flat && pl.pf.ok)
     return launch_prefill(d, p, pl.pf, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, err, errlen);
   if (flat && pl.fs.ok)
     return launch_flat_tiled(d, p, pl.fs, index, queries, q_pos, T, Hq, out_idx, out_scores, ws, st, err, errlen);
   const bool kb = d.key_dtype == LSA_BF16, lb = d.latent_dtype == LSA_BF16;
 #define LSA_RUN(KT, LT, DLV) \
-  return run_select<KT, LT, DLV>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen)
+  return run_select<KT, LT, DLV>(d, p, pl, index, queries, q_pos, T, Hq, out_idx, out_scores, out_leaves, ws, st, flat, err, errlen, app)
   if (d.d_latent == 64) {
     if (kb && lb) LSA_RUN(bf16_t, bf16_t, 64);
     if (kb) LSA_RUN(bf16_t, float, 64);

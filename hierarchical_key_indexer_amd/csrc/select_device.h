@@ -39,21 +39,29 @@ struct SelArgs {
   const uint32_t* hdr;         // the blob's header
   uint32_t hx[kHeaderCheckWords];   // header words the descriptor implies
   int* status;                 // the call's device status (LSA_OK / LSA_ERR_BAD_INDEX)
+  int64_t Npos;                // valid query positions: [0, Npos) (N plus the appended keys)
+  const int* app_leaf;         // [Hkv][app_cap] leaf of each appended key, -1 = none (null: no pool)
+  const void* app_lat;         // [Hkv][app_cap][DL] latent of each appended key
+  int64_t app_cap;
+  int app_n;                   // appended keys in use: positions N .. N + app_n - 1
+  int* leafid;                 // [QH][nl_cap] the selected leaves, ascending (appended mode)
 };
 
-// Wave-wide: does the blob's header hold what the call's descriptor implies
-// (magic, version, shape fields, total size, a zero build status)?  Reads the
-// first kHeaderCheckWords words of the blob and nothing else.
-__device__ __forceinline__ bool header_matches(const SelArgs& a) {
+// Wave-wide: does the blob's header hold the expected words hx (magic,
+// version, shape fields, total size, a zero build status)?  Reads the first
+// kHeaderCheckWords words of the blob and nothing else.
+__device__ __forceinline__ bool header_words_match(const uint32_t* hdr, const uint32_t* hx) {
   const int lane = lane_id();
   uint32_t want = 0u;
 #pragma unroll
   for (int i = 0; i < kHeaderCheckWords; ++i)
-    if (lane == i) want = a.hx[i];
+    if (lane == i) want = hx[i];
   const bool cmp = lane < kHeaderCheckWords && ((kHeaderCheckMask >> lane) & 1u);
-  const uint32_t got = cmp ? a.hdr[lane] : want;
+  const uint32_t got = cmp ? hdr[lane] : want;
   return __ballot(got != want) == 0ull;
 }
+
+__device__ __forceinline__ bool header_matches(const SelArgs& a) { return header_words_match(a.hdr, a.hx); }
 
 // Host: what the kernels of a call compare the blob's header with, and where
 // the call's status word lives.
@@ -268,6 +276,54 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
       if (threadIdx.x == 0) *n_sh = a.k;
       __syncthreads();
     }
+  }
+  __syncthreads();
+  return *n_sh;
+}
+
+// Appended keys: score the pool slots [s0, s1) of KV head h whose key joined
+// one of the query's leaves (lid, ascending, nl of them) and whose position
+// N + slot lies in [clo, chi], and append their rank keys above thr to buf
+// after its first n entries, compacting to the best k when it fills.  One
+// thread per slot: the 4-byte leaf ids are read for every slot, a latent row
+// only for a member (few: a query keeps a small share of the leaves).  q is
+// the query latent (fp32, visible to the block).  Needs CAP >= k + BLOCK.
+// Returns the number of keys in buf.  Block-wide.
+template <typename LT, int DL, int M, int BLOCK>
+__device__ int pool_stream(const SelArgs& a, int h, int clo, int chi, const int* lid, int nl, int64_t s0,
+                           int64_t s1, u64 thr, u64* buf, int n, int* n_sh, RadixScratch* rs, const float* q) {
+  constexpr int CAP = M * BLOCK;
+  const int* leafs = a.app_leaf + (size_t)h * a.app_cap;
+  const LT* lats = (const LT*)a.app_lat + (size_t)h * a.app_cap * DL;
+  __syncthreads();
+  if (threadIdx.x == 0) *n_sh = n;
+  for (int64_t base = s0; base < s1; base += BLOCK) {
+    __syncthreads();
+    if (*n_sh + BLOCK > CAP) {                 // block-uniform
+      const int nn = *n_sh;
+      thr = topk_compact<BLOCK, M>(buf, nn, a.k, rs);
+      if (threadIdx.x == 0) *n_sh = a.k;
+      __syncthreads();
+    }
+    const int64_t slot = base + threadIdx.x;
+    bool pr = false;
+    u64 key = 0ull;
+    if (slot < s1) {
+      const int leaf = leafs[slot];
+      const int64_t j = a.N + slot;
+      if (leaf >= 0 && nl > 0 && j >= clo && j <= chi) {
+        int lo_i = 0, hi_i = nl;               // largest lo_i with lid[lo_i] <= leaf
+        while (hi_i - lo_i > 1) {
+          const int mid = (lo_i + hi_i) >> 1;
+          if (lid[mid] <= leaf) lo_i = mid; else hi_i = mid;
+        }
+        if (lid[lo_i] == leaf) {
+          key = rank_key(row_dot<LT, DL>(lats + slot * DL, q), (int)j);
+          pr = key > thr;
+        }
+      }
+    }
+    wave_append(pr, key, buf, n_sh);
   }
   __syncthreads();
   return *n_sh;

@@ -254,6 +254,59 @@ int lsa_flat_select(const lsa_index_desc* desc, const void* index, const void* q
                     const lsa_select_params* params, int32_t* out_idx, float* out_scores,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- incremental upkeep: keys that arrive after the build --------------------------
+ * Every decode step adds a key to the cache, and the cache stays full length
+ * (page "Latent Sparse Attention: tree search over keys for 10M-token
+ * context", section "Gaps"); decode runs in a captured loop ("Latent Sparse
+ * Attention (LSA): The 72.4x and 22.7x Speedups, and What They Compare
+ * Against", section "Can I run LSA?").  The pages do not say how new keys
+ * enter the index.  Reading: a new key joins the tree without changing it.
+ * Its latent is computed as the build computes every key's; it descends from
+ * the root, at every level to the child of the current node whose stored
+ * centroid is nearest (the build's assignment arithmetic) among the children
+ * that hold keys, ties to the lowest child, and joins the leaf it reaches.
+ * Centroids and earlier keys do not move; re-clustering is a new build.  The
+ * i-th appended key of every KV head is the key at position n_keys + i.
+ *
+ * The append pool: one caller-owned device buffer of
+ * lsa_append_pool_bytes(desc, capacity) bytes, sections 256-byte aligned:
+ *     leaf    int32  [Hkv][capacity]              leaf each appended key joined
+ *                                                 (-1: the index was refused)
+ *     latent  latent [Hkv][capacity][d_latent]    its latent
+ * Slot i of a head holds the key at position n_keys + i.  The caller keeps
+ * count of the slots in use (every call appends the same tokens to every
+ * KV head).  Limits: capacity >= 1, n_keys + capacity < 2^31. */
+
+/* Bytes of an append pool of `capacity` keys per KV head; 0 if invalid. */
+size_t lsa_append_pool_bytes(const lsa_index_desc* desc, int32_t capacity);
+
+/* Append n_new keys (device [n_new][Hkv][d_head], key_dtype: the new tokens'
+ * keys) to slots [first, first + n_new) of `pool` (device, capacity keys per
+ * head), for every KV head.  Reads the index (device blob); a blob whose
+ * header does not match desc leaves the slots' leaves at -1.  Asynchronous on
+ * `stream`; allocates nothing.  Errors: LSA_ERR_INVALID_ARG (NULL pointer,
+ * slots outside [0, capacity)), LSA_ERR_UNSUPPORTED (descriptor, capacity),
+ * LSA_ERR_HIP; nothing is enqueued on a validation error. */
+int lsa_append_keys(const lsa_index_desc* desc, const void* index, const void* keys, int32_t n_new, int32_t first,
+                    void* pool, int32_t capacity, void* stream);
+
+/* Bytes of device workspace lsa_select_appended needs; 0 if invalid. */
+size_t lsa_select_appended_workspace_bytes(const lsa_index_desc* desc, const lsa_select_params* params,
+                                           int32_t n_tokens, int32_t n_q_heads);
+
+/* lsa_select over the index plus the first n_appended keys of the pool
+ * (positions n_keys .. n_keys + n_appended - 1): an appended key is a
+ * candidate of a query head iff its leaf is one the head kept and its
+ * position lies in [sink, p - window].  Query positions may be up to
+ * n_keys + n_appended - 1.  Same outputs, device status word and errors as
+ * lsa_select; n_appended outside [0, capacity] is LSA_ERR_INVALID_ARG.  Every
+ * batch runs the per-query-head kernels, which read each leaf once per query
+ * head: meant for decode between re-builds. */
+int lsa_select_appended(const lsa_index_desc* desc, const void* index, const void* pool, int32_t capacity,
+                        int32_t n_appended, const void* queries, const int32_t* q_pos, int32_t n_tokens,
+                        int32_t n_q_heads, const lsa_select_params* params, int32_t* out_idx, float* out_scores,
+                        int32_t* out_leaves, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- training-free latent map ------------------------------------------------
  * "Latent Sparse Attention (LSA): The 72.4x and 22.7x Speedups, and What They
  * Compare Against", section "How does LSA work?", lists a PCA map as the option

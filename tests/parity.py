@@ -108,9 +108,10 @@ def check_row(gpu_row, gpu_scores, res, p, prm: O.SelectParams, what=""):
 
 
 def compare_select(oidx, queries, q_pos, prm, gpu_idx, gpu_scores, gpu_leaves=None, pairs=None, flat=False,
-                   log=None):
+                   log=None, appended=None):
     """Compare GPU rows with the oracle for the given (t, hq) pairs (all by
-    default).  Returns the number of tolerated near-tie swaps."""
+    default); ``appended`` (one O.Appended per KV head) adds keys appended
+    after the build.  Returns the number of tolerated near-tie swaps."""
     desc = oidx.desc
     T, Hq = queries.shape[0], queries.shape[1]
     g = Hq // desc.n_kv_heads
@@ -126,7 +127,8 @@ def compare_select(oidx, queries, q_pos, prm, gpu_idx, gpu_scores, gpu_leaves=No
                 leaves = check_leaves(oidx.heads[h], desc.fanout, qlat, prm.b, prm.beam, gpu_leaves[t, hq])
             else:
                 leaves = None
-        res = O.select_one(oidx, h, qlat, p, prm, flat=flat, leaves=leaves)
+        res = O.select_one(oidx, h, qlat, p, prm, flat=flat, leaves=leaves,
+                           appended=None if appended is None else appended[h])
         swaps += check_row(gpu_idx[t, hq], None if gpu_scores is None else gpu_scores[t, hq], res, p, prm,
                            what=f"(t={t}, hq={hq}, p={p})")
     if log:
@@ -275,3 +277,42 @@ def check_lloyd_update(gidx, desc: O.IndexDesc, step: float, log=None, tie_rel=2
     if log:
         log(f"Lloyd update: {compared} children equal their member means, {skipped} skipped at near-ties")
     return compared, skipped
+
+
+def check_appended(oidx, keys_new, W, desc: O.IndexDesc, gpu_leaf, gpu_lat, log=None):
+    """Keys appended on the GPU (pool leaves [Hkv][A], latents [Hkv][A][dl])
+    against the oracle: latents within one ulp plus the fp32 accumulation
+    bound (as for the build), and every routing step valid: at each level
+    the child taken holds keys and its squared distance (float64, stored
+    centroids) is the smallest among the non-empty siblings up to 1e-4
+    relative (fp32 distances may swap near-ties).  Returns the number of
+    keys whose leaf differs from the oracle's own routing."""
+    diffs = 0
+    for h, hh in enumerate(oidx.heads):
+        ref = O.latent_keys(keys_new[:, h, :], W[h], desc.key_dtype, desc.latent_dtype)
+        sc = np.abs(O.stored_to_f64(keys_new[:, h, :], desc.key_dtype)) @ np.abs(W[h].astype(np.float64))
+        ulp = (np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8) if desc.latent_dtype == "bf16"
+               else np.zeros_like(ref))
+        got = gpu_lat[h]
+        assert np.all(np.abs(got - ref) <= ulp * 1.0000001 + 1e-5 * sc), f"head {h}: appended latent"
+        for i, x in enumerate(got):
+            leaf = int(gpu_leaf[h][i])
+            assert leaf >= 0, f"head {h} key {i}: not appended"
+            node, path = leaf, []
+            for lev in range(desc.n_levels - 1, -1, -1):
+                path.append((lev, node))
+                node //= desc.fanout[lev]
+            for lev, kid in reversed(path):
+                f = desc.fanout[lev]
+                par = kid // f
+                kids = par * f + np.arange(f)
+                ne = np.diff(hh.offsets[lev])[kids] > 0
+                assert ne[kid - par * f], f"head {h} key {i}: routed into an empty node"
+                d2 = ((hh.centroids[lev][kids] - x) ** 2).sum(-1)
+                best = d2[ne].min()
+                assert d2[kid - par * f] <= best * (1 + 1e-4) + 1e-6 * float(x @ x), \
+                    f"head {h} key {i} level {lev + 1}: not the nearest non-empty child"
+            diffs += leaf != O.route_key(hh, desc.fanout, x)
+    if log:
+        log(f"appended keys: latents and routes hold, {diffs} near-tie routes differ from the oracle's")
+    return diffs
