@@ -78,11 +78,11 @@ class HipEvents:
 
     def elapsed_ms(self, a, b):
         """Milliseconds between two recorded events, None if they were never
-        recorded (a stage the call did not run)."""
-        if self.hip.hipEventSynchronize(b) != 0:
-            return None
+        recorded (a stage the call did not run; the failed query's error is
+        cleared so that it does not surface in the next HIP call)."""
         ms = ctypes.c_float()
-        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        if self.hip.hipEventSynchronize(b) != 0 or self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            self.hip.hipGetLastError()
             return None
         return ms.value
 
@@ -357,7 +357,9 @@ def decode_record(wl, li, keys, hip, args, pool_n, abi):
     roof = {"bound": "hbm", "achieved": cold_bytes / (gather_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = load_traffic(wl.name, "gather")
-    roof["kernel"] = "gather_kernel"
+    fused = cold.get(abi.STAGE_MERGE) is None
+    roof["kernel"] = ("gather_split_kernel (the merge runs in each query head's last workgroup)" if fused
+                      else "gather_kernel")
     roof["algorithmic_bytes_per_launch"] = cold_bytes
     roof["kernel_ms"] = gather_ms
     roof["timing"] = (f"cold: steps rotate over {pool_n} query batches whose rows total "

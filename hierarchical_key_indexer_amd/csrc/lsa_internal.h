@@ -184,6 +184,7 @@ struct SelectPlan {
   int splits;          // workgroups per query head in the gather (1 = direct)
   int flat_splits;     // workgroups per (token, KV head) in the flat scan
   bool appended;       // appended mode (sorted leaf ids kept for the pool's membership test)
+  int g1;              // > 0: split descent with g1 workgroups per query head
   size_t bytes;        // workspace bytes
   PfPlan pf;           // node-major prefill path (pf.ok)
   FsPlan fs;           // row-tiled full scan (fs.ok)

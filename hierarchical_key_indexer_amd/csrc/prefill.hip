@@ -729,43 +729,6 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
 // per-row threshold from the samples
 // ---------------------------------------------------------------------------
 
-// Over a 256-bin histogram (lane l owns bins 4l..4l+3), the bin that holds
-// the need-th unit of weight counted from the top, and in *above the weight of
-// the bins above it; -1 if the histogram holds less than need.  Wave-wide.
-__device__ __forceinline__ int wave_find_bin(const u64* hist, u64 need, u64* above_out) {
-  const int lane = threadIdx.x & 63;
-  u64 hb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
-  const u64 sum = hb[0] + hb[1] + hb[2] + hb[3];
-  u64 incl = sum;   // over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const u64 x = __shfl_down(incl, o, 64);
-    if (lane + o < 64) incl += x;
-  }
-  const u64 above = incl - sum;
-  const bool mine = above < need && need <= incl;
-  int d = -1;
-  u64 ab = 0ull;
-  if (mine) {
-    u64 acc = above;
-    for (int i = 3; i >= 0; --i) {
-      if (acc + hb[i] >= need) {
-        d = 4 * lane + i;
-        ab = acc;
-        break;
-      }
-      acc += hb[i];
-    }
-  }
-  const u64 bal = __ballot(mine);
-  if (bal == 0ull) return -1;
-  const int src = __ffsll((long long)bal) - 1;
-  *above_out = __shfl(ab, src, 64);
-  return __shfl(d, src, 64);
-}
-
 // One wave per row.  A sample of leaf c stands for size_c / min(spl, size_c)
 // candidates (fixed point, 4 fraction bits); the threshold is the largest
 // 16-bit sample value whose weight at or above it reaches 1.5k, found with two

@@ -151,6 +151,82 @@ __device__ __forceinline__ void wave_select_top32(const uint32_t* key, int need,
   }
 }
 
+// One level of a per-parent descent with every fanout <= 64: for each parent
+// fa[i] (i < nf) the best min(b, F) children by score, ties to the lower id,
+// go to fb[i * bs ..] in child order, -1 padded.  Waves take the parents in
+// turn.  Block-wide (no barrier inside).
+template <typename LT, int DL, int NW>
+__device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, const float* q, const int* fa, int nf,
+                                            int* fb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int F = a.F[lev];
+  const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
+  const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
+  // A parent's children are one contiguous block of centroid rows: LPK
+  // lanes read a row (16 bytes each, so a load instruction covers KPW
+  // whole rows) and reduce their partial dots with DPP; each lane then
+  // takes its own child's score and the wave ranks them.  A wave loads
+  // two parents' rows before it scores either (bf16 rows, or fp32 rows at
+  // d_l = 32), so their round trips overlap.  Loads past the last child re-read the last row (its score
+  // is dropped), so every load is unconditional.
+  constexpr int E = Lat<LT>::PER16;
+  constexpr int LPK = DL / E;           // lanes per centroid row
+  constexpr int KPW = 64 / LPK;         // rows per load instruction
+  constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
+  const int bs = min(a.b, F);
+  const int lig = lane % LPK, g = lane / LPK;
+  QSlice<LT> qv;
+  qv.load(q + lig * E);
+  auto load = [&](int i, uint4* v, int& o0, int& o1) {
+    const int64_t node0 = (int64_t)fa[i] * F;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = min(r * KPW + g, F - 1);
+      v[r] = *(const uint4*)(cs + (node0 + c) * DL + lig * E);
+    }
+    const int c = min(lane, F - 1);
+    o0 = off[node0 + c];
+    o1 = off[node0 + c + 1];
+  };
+  auto pick = [&](int i, const uint4* v, int o0, int o1) {
+    float part[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
+    // child `lane` is row g' = lane % KPW of round lane / KPW, summed at lane g' * LPK
+    float sc = 0.f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float x = __shfl(part[r], (lane % KPW) * LPK, 64);
+      if (lane / KPW == r) sc = x;
+    }
+    const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
+    u64 in[1];
+    wave_select_top32<1>(&key, bs, in);
+    // kept in child order (ties went to the lower child id)
+    if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
+    for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
+  };
+  if constexpr (NR <= 8) {
+    for (int i = w; i < nf; i += 2 * NW) {
+      const bool two = i + NW < nf;
+      uint4 va[NR], vb[NR];
+      int a0, a1, b0, b1;
+      load(i, va, a0, a1);
+      load(two ? i + NW : i, vb, b0, b1);
+      pick(i, va, a0, a1);
+      if (two) pick(i + NW, vb, b0, b1);
+    }
+  } else {
+    // fp32 rows at d_l = 64: two parents' rows would not fit the registers
+    for (int i = w; i < nf; i += NW) {
+      uint4 va[NR];
+      int a0, a1;
+      load(i, va, a0, a1);
+      pick(i, va, a0, a1);
+    }
+  }
+}
+
 // SMALL: a per-parent beam and every fanout <= 64 (the only branch compiled
 // in; the general branches would raise the register count past the budget)
 template <typename KT, typename LT, int DL, int BLOCK, bool SMALL>
@@ -189,71 +265,9 @@ __global__ __launch_bounds__(BLOCK) void descend_kernel(SelArgs a) {
     const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
     const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
     if constexpr (SMALL) {
-      // A parent's children are one contiguous block of centroid rows: LPK
-      // lanes read a row (16 bytes each, so a load instruction covers KPW
-      // whole rows) and reduce their partial dots with DPP; each lane then
-      // takes its own child's score and the wave ranks them.  A wave loads
-      // two parents' rows before it scores either (bf16 rows, or fp32 rows at
-      // d_l = 32), so their round trips overlap.  Loads past the last child re-read the last row (its score
-      // is dropped), so every load is unconditional.
-      constexpr int E = Lat<LT>::PER16;
-      constexpr int LPK = DL / E;           // lanes per centroid row
-      constexpr int KPW = 64 / LPK;         // rows per load instruction
-      constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
-      const int bs = min(a.b, F);
-      const int lig = lane % LPK, g = lane / LPK;
-      QSlice<LT> qv;
-      qv.load(q + lig * E);
-      auto load = [&](int i, uint4* v, int& o0, int& o1) {
-        const int64_t node0 = (int64_t)fa[i] * F;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int c = min(r * KPW + g, F - 1);
-          v[r] = *(const uint4*)(cs + (node0 + c) * DL + lig * E);
-        }
-        const int c = min(lane, F - 1);
-        o0 = off[node0 + c];
-        o1 = off[node0 + c + 1];
-      };
-      auto pick = [&](int i, const uint4* v, int o0, int o1) {
-        float part[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
-        // child `lane` is row g' = lane % KPW of round lane / KPW, summed at lane g' * LPK
-        float sc = 0.f;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float x = __shfl(part[r], (lane % KPW) * LPK, 64);
-          if (lane / KPW == r) sc = x;
-        }
-        const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
-        u64 in[1];
-        wave_select_top32<1>(&key, bs, in);
-        // kept in child order (ties went to the lower child id)
-        if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
-        for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
-      };
-      if constexpr (NR <= 8) {
-        for (int i = w; i < nf; i += 2 * NW) {
-          const bool two = i + NW < nf;
-          uint4 va[NR], vb[NR];
-          int a0, a1, b0, b1;
-          load(i, va, a0, a1);
-          load(two ? i + NW : i, vb, b0, b1);
-          pick(i, va, a0, a1);
-          if (two) pick(i + NW, vb, b0, b1);
-        }
-      } else {
-        // fp32 rows at d_l = 64: two parents' rows would not fit the registers
-        for (int i = w; i < nf; i += NW) {
-          uint4 va[NR];
-          int a0, a1;
-          load(i, va, a0, a1);
-          pick(i, va, a0, a1);
-        }
-      }
+      small_level<LT, DL, NW>(a, lev, h, q, fa, nf, fb);
       __syncthreads();
-      nf = compact_ids<BLOCK>(fb, nf * bs, fa, wsum);
+      nf = compact_ids<BLOCK>(fb, nf * min(a.b, F), fa, wsum);
     } else if (a.beam == LSA_BEAM_PER_PARENT) {
       const int bs = min(a.b, F);
       for (int i = w; i < nf; i += NW) {
@@ -517,6 +531,299 @@ __global__ __launch_bounds__(BLOCK) void gather_kernel(SelArgs a) {
     write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
                               a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
   }
+}
+
+// ---------------------------------------------------------------------------
+// split descent: one workgroup per kept level-1 node of a query head
+// ---------------------------------------------------------------------------
+
+constexpr int kSplitBlock = 256;
+
+// Workgroup (g, query head): the query latent, the root's best children (the
+// same in every workgroup of the query head), then the descent below the g-th
+// of them.  Its leaves fill the query head's leaf slots [g sub, (g+1) sub)
+// (sub = b^(L-1), ascending ids, empty slots marked), so the slots of all the
+// workgroups list the kept leaves in ascending order.  It also scores
+// kSplitSamples candidates spread evenly over its own leaves (the gather
+// derives its threshold from them, each sample standing for its share of the
+// subtree's candidates).  Per-parent beam, fanouts <= 64.
+template <typename KT, typename LT, int DL>
+__global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
+  constexpr int BLOCK = kSplitBlock, NW = BLOCK / 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float qin[256 + kQSlices * DL];
+  __shared__ float q[DL];
+  __shared__ int wsum[NW];
+  const int sub = a.nl_cap / a.G1;
+  const int nfb = max(sub, a.G1) + 1;       // the root's kept children, a level's slots, or the prefix
+  int* fa = (int*)smem;                     // frontier: leaf ids at the end   [sub]
+  int* fb = fa + sub;                       // next frontier slots; then the prefix of leaf sizes   [nfb]
+  int* lr = fb + nfb;                       // first CSR row of each leaf   [sub]
+  const int64_t qh = a.qh0 + blockIdx.y;
+  const int g = blockIdx.x;
+  const int hq = (int)(qh % a.Hq), h = hq / a.G, t = (int)(qh / a.Hq);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (!check_index_first(a)) return;        // block-uniform; the gather reads the status
+  const int p = a.q_pos[t];
+  query_latent<KT, LT, DL>(a, qh, h, qin, q);
+  if (g == 0 && threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;   // the gather's lists (S > 1 only)
+  // level 1: the root's kept children, ascending; this workgroup takes the g-th
+  if (threadIdx.x == 0) fa[0] = 0;
+  __syncthreads();
+  small_level<LT, DL, NW>(a, 0, h, q, fa, 1, fb);
+  __syncthreads();
+  const int my = fb[g];
+  __syncthreads();
+  int nf = 0;
+  if (my >= 0) {                            // block-uniform
+    if (threadIdx.x == 0) fa[0] = my;
+    __syncthreads();
+    nf = 1;
+    for (int lev = 1; lev < a.L; ++lev) {
+      small_level<LT, DL, NW>(a, lev, h, q, fa, nf, fb);
+      __syncthreads();
+      nf = compact_ids<BLOCK>(fb, nf * min(a.b, a.F[lev]), fa, wsum);
+    }
+  }
+  // the leaf slots and the exclusive prefix of the leaves' sizes
+  const int* offL = a.off[a.L - 1] + (size_t)h * (a.P[a.L - 1] + 1);
+  int* srow = a.slot_row + qh * a.nl_cap + (int64_t)g * sub;
+  int* sn = a.slot_n + qh * a.nl_cap + (int64_t)g * sub;
+  int* sleaf = a.slot_leaf + qh * a.nl_cap + (int64_t)g * sub;
+  const int per = (sub + BLOCK - 1) / BLOCK;
+  const int i0 = min(sub, (int)threadIdx.x * per), i1 = min(sub, i0 + per);
+  int c = 0;
+  for (int i = i0; i < i1; ++i) {
+    if (i < nf) {
+      const int leaf = fa[i];
+      const int r0 = offL[leaf], r1 = offL[leaf + 1];
+      srow[i] = r0;
+      sn[i] = r1 - r0;
+      sleaf[i] = leaf;
+      lr[i] = r0;
+      c += r1 - r0;
+    } else {
+      srow[i] = -1;
+      sn[i] = 0;
+      sleaf[i] = -1;
+    }
+  }
+  int ng;
+  int run = block_exclusive_scan<BLOCK>(c, wsum, &ng);
+  for (int i = i0; i < min(i1, nf); ++i) {
+    fb[i] = run;
+    run += offL[fa[i] + 1] - offL[fa[i]];
+  }
+  if (threadIdx.x == 0) {
+    fb[nf] = ng;
+    a.smpn[qh * a.G1 + g] = ng;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // wave 0: the samples, lane l taking candidate l n_g / min(n_g, kSplitSamples)
+  constexpr int E = Lat<LT>::PER16, LPK = DL / E, KPW = 64 / LPK, NR = 64 / KPW;
+  const int ns = min(ng, kSplitSamples);
+  int row = 0, j = -1;
+  if (ns > 0) {
+    const int o = (int)((int64_t)min(lane, ns - 1) * ng / ns);
+    int lo_i = 0, hi_i = nf;                // fb[lo_i] <= o < fb[hi_i]
+    while (hi_i - lo_i > 1) {
+      const int mid = (lo_i + hi_i) >> 1;
+      if (fb[mid] <= o) lo_i = mid; else hi_i = mid;
+    }
+    row = lr[lo_i] + (o - fb[lo_i]);
+    j = a.perm[(size_t)h * a.N + row];
+  }
+  uint32_t key = 0u;
+  if (ns > 0) {
+    const int lig = lane % LPK, gg = lane / LPK;
+    QSlice<LT> qv;
+    qv.load(q + lig * E);
+    const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
+    uint4 v[NR];
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const int rw = __shfl(row, rr * KPW + gg, 64);
+      v[rr] = *(const uint4*)(latb + (size_t)rw * DL + lig * E);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const float part = group_sum_lead<LPK>(qv.dot(v[rr]));
+      const float x = __shfl(part, (lane % KPW) * LPK, 64);
+      if (lane / KPW == rr) sc = x;
+    }
+    const bool cand = lane < ns && p >= 0 && (int64_t)p < a.Npos && j >= a.sink && j <= p - a.window;
+    key = cand ? order_u32(sc) : 0u;
+  }
+  a.smp[(qh * a.G1 + g) * kSplitSamples + lane] = key;
+}
+
+// The gather of the split descent.  Its first loads take the query head's
+// leaf slots, the subtrees' samples and the query latent together; the slots
+// are compacted in LDS (row starts, prefix counts, leaf ids) and the
+// threshold is the weighted sample quantile with about 2k candidates expected
+// above it (a sample of subtree g stands for n_g / min(n_g, kSplitSamples)
+// candidates; every workgroup of the query head computes the same value).
+// The candidates are split over S workgroups as in gather_kernel (with S > 1
+// merge_kernel takes the appended lists; workgroup 0 leaves it the compacted
+// leaf list and the threshold, for its exact re-score).
+template <typename LT, int DL, int M, int U, int BLOCK>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void gather_split_kernel(SelArgs a) {
+  constexpr int CAP = M * BLOCK;
+  constexpr int NS4 = kSplitMaxB * kSplitSamples / BLOCK;   // samples per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ RadixScratch rs;
+  __shared__ int n_sh, base_sh, d_sh, nl_sh;
+  __shared__ int wsum[BLOCK / 64];
+  __shared__ int gsz[kSplitMaxB];
+  __shared__ u64 hist[256];
+  __shared__ u64 ab_sh;
+  __shared__ float qs[DL];
+  u64* buf = (u64*)smem;
+  int* lpre = (int*)(buf + CAP);            // [nl_cap + 1]
+  int* lrow = lpre + a.nl_cap + 1;          // [nl_cap]
+  int* lid = lrow + a.nl_cap;               // [nl_cap]
+  const int64_t qh = a.qh0 + blockIdx.y;
+  const int s = blockIdx.x;
+  const int t = (int)(qh / a.Hq), hq = (int)(qh % a.Hq), h = hq / a.G;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the first loads, independent of one another
+  const int p = a.q_pos[t];
+  const int bad = *a.status;
+  const int nsmp = a.G1 * kSplitSamples;
+  uint32_t sk[NS4];
+#pragma unroll
+  for (int j = 0; j < NS4; ++j) {
+    const int i = threadIdx.x + j * BLOCK;
+    sk[j] = i < nsmp ? a.smp[qh * nsmp + i] : 0u;
+  }
+  const int gn = (int)threadIdx.x < a.G1 ? a.smpn[qh * a.G1 + threadIdx.x] : 0;
+  const float qv = threadIdx.x < DL ? a.qlat[qh * DL + threadIdx.x] : 0.f;
+  for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) {
+    lpre[i] = a.slot_n[qh * a.nl_cap + i];
+    lrow[i] = a.slot_row[qh * a.nl_cap + i];
+    lid[i] = a.slot_leaf[qh * a.nl_cap + i];
+  }
+  if ((int)threadIdx.x < a.G1) gsz[threadIdx.x] = gn;
+  if (threadIdx.x < DL) qs[threadIdx.x] = qv;
+  if (bad || p < 0 || (int64_t)p >= a.Npos) {   // block-uniform
+    if (s == 0) {
+      write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
+      if (a.out_leaves)
+        for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) a.out_leaves[qh * a.nl_cap + i] = -1;
+    }
+    return;
+  }
+  __syncthreads();
+  // compact the slots in order: each thread its contiguous chunk
+  {
+    constexpr int MAXPER = 4096 / BLOCK;
+    const int per = (a.nl_cap + BLOCK - 1) / BLOCK;
+    const int i0 = min(a.nl_cap, (int)threadIdx.x * per);
+    int vn[MAXPER], vr[MAXPER], vl[MAXPER];
+    int c = 0, sz = 0;
+#pragma unroll
+    for (int j = 0; j < MAXPER; ++j) {
+      const int i = i0 + j;
+      const bool in = j < per && i < a.nl_cap;
+      vn[j] = in ? lpre[i] : 0;
+      vr[j] = in ? lrow[i] : 0;
+      vl[j] = in ? lid[i] : -1;
+      c += vn[j] > 0 ? 1 : 0;
+      sz += vn[j];
+    }
+    int nl, total;
+    int pos = block_exclusive_scan<BLOCK>(c, wsum, &nl);
+    int run = block_exclusive_scan<BLOCK>(sz, wsum, &total);   // ends with a barrier: the reads are done
+#pragma unroll
+    for (int j = 0; j < MAXPER; ++j)
+      if (vn[j] > 0) {
+        lrow[pos] = vr[j];
+        lpre[pos] = run;
+        lid[pos] = vl[j];
+        run += vn[j];
+        ++pos;
+      }
+    if (threadIdx.x == 0) {
+      lpre[nl] = total;
+      nl_sh = nl;
+    }
+  }
+  __syncthreads();
+  const int nl = nl_sh;
+  const int64_t total = lpre[nl];
+  if (s == 0) {
+    // the leaf list for the merge kernel's exact re-score, and the leaves out
+    for (int i = threadIdx.x; i <= nl; i += BLOCK) a.leafpre[qh * (a.nl_cap + 1) + i] = lpre[i];
+    for (int i = threadIdx.x; i < nl; i += BLOCK) a.leafrow[qh * a.nl_cap + i] = lrow[i];
+    if (a.leafid)
+      for (int i = threadIdx.x; i < nl; i += BLOCK) a.leafid[qh * a.nl_cap + i] = lid[i];
+    if (threadIdx.x == 0) a.nleaf[qh] = nl;
+    if (a.out_leaves)
+      for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) a.out_leaves[qh * a.nl_cap + i] = i < nl ? lid[i] : -1;
+  }
+  // threshold: weighted quantile of the samples, about 2k candidates above
+  u64 thr0 = 0ull;
+  if (total > 4 * (int64_t)a.k) {
+    const u64 target = (u64)a.k * 2u * 16u;
+    int d1 = -1, d2 = -1;
+    u64 ab1 = 0ull;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int i = threadIdx.x; i < 256; i += BLOCK) hist[i] = 0ull;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NS4; ++j) {
+        const int i = threadIdx.x + j * BLOCK;
+        if (sk[j] == 0u || (pass == 1 && (int)(sk[j] >> 24) != d1)) continue;
+        const int gi = i / kSplitSamples;
+        const int ng = gsz[gi], nsg = min(ng, kSplitSamples);
+        const u64 wt = (u64)ng * 16u / (u64)nsg;
+        atomicAdd(&hist[pass == 0 ? (sk[j] >> 24) : ((sk[j] >> 16) & 0xFFu)], wt);
+      }
+      __syncthreads();
+      if (w == 0) {
+        u64 ab = 0ull;
+        const int d = wave_find_bin(hist, pass == 0 ? target : target - ab1, &ab);
+        if (lane == 0) {
+          d_sh = d;
+          ab_sh = ab;
+        }
+      }
+      __syncthreads();
+      if (pass == 0) {
+        d1 = d_sh;
+        ab1 = ab_sh;
+      } else {
+        d2 = d_sh;
+      }
+      __syncthreads();
+      if (d1 < 0) break;                      // block-uniform: fewer than the target: take every candidate
+    }
+    if (d1 >= 0 && d2 >= 0) thr0 = (u64)(((uint32_t)d1 << 24) | ((uint32_t)d2 << 16)) << 32;
+  }
+  if (s == 0 && threadIdx.x == 0) a.tau[qh] = thr0;
+  const int clo = a.sink, chi = p - a.window;
+  const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
+  const int64_t plo = (int64_t)a.app_n * s / a.S, phi = (int64_t)a.app_n * (s + 1) / a.S;
+  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs, qs);
+  if (a.app_n > 0) n = pool_stream<LT, DL, M, BLOCK>(a, h, clo, chi, lid, nl, plo, phi, thr0, buf, n, &n_sh, &rs, qs);
+  int32_t* orow = a.out_idx + qh * a.width;
+  float* srow = a.out_scores ? a.out_scores + qh * a.k : nullptr;
+  if (a.S == 1) {
+    if (n < a.k && thr0 != 0ull) {
+      // the threshold let fewer than k keys through: redo without it
+      n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs, qs);
+      if (a.app_n > 0) n = pool_stream<LT, DL, M, BLOCK>(a, h, clo, chi, lid, nl, plo, phi, 0ull, buf, n, &n_sh, &rs, qs);
+    }
+    write_top_k_row<BLOCK, M>(buf, n, a.k, CAP, p, a.sink, a.window, orow, srow, &rs);
+    return;
+  }
+  if (n > a.k) {
+    topk_compact<BLOCK, M>(buf, n, a.k, &rs);
+    n = a.k;
+  }
+  append_part<BLOCK>(a, qh, buf, n, &base_sh);
 }
 
 // r-th largest of the nonzero keys[0..n) in LDS (0 if fewer than r): three
@@ -922,6 +1229,11 @@ constexpr int kFlatR = 40;                 // samples expected above a full-scan
 struct SelWs {
   int* status;
   int* leafid;
+  int* slot_row;
+  int* slot_n;
+  int* slot_leaf;
+  unsigned int* smp;
+  int* smpn;
   float* qlat;
   int* leafrow;
   int* leafpre;
@@ -940,13 +1252,29 @@ size_t carve_select(const lsa_index_desc& d, const lsa_select_params& p, const S
   w.qlat = c.take<float>((size_t)(qh * d.d_latent));
   w.leafrow = w.leafpre = w.nleaf = nullptr;
   w.leafid = nullptr;
-  if (!flat) {
+  w.slot_row = w.slot_n = w.slot_leaf = w.smpn = nullptr;
+  w.smp = nullptr;
+  w.tau = nullptr;
+  if (!flat && pl.g1 > 0) {
+    w.slot_row = c.take<int>((size_t)(qh * pl.nl_cap));
+    w.slot_n = c.take<int>((size_t)(qh * pl.nl_cap));
+    w.slot_leaf = c.take<int>((size_t)(qh * pl.nl_cap));
+    w.smp = c.take<unsigned int>((size_t)(qh * pl.g1 * kSplitSamples));
+    w.smpn = c.take<int>((size_t)(qh * pl.g1));
     w.leafrow = c.take<int>((size_t)(qh * pl.nl_cap));
     w.leafpre = c.take<int>((size_t)(qh * (pl.nl_cap + 1)));
     w.nleaf = c.take<int>((size_t)qh);
     if (pl.appended) w.leafid = c.take<int>((size_t)(qh * pl.nl_cap));
+    w.tau = c.take<unsigned long long>((size_t)qh);
+  } else {
+    if (!flat) {
+      w.leafrow = c.take<int>((size_t)(qh * pl.nl_cap));
+      w.leafpre = c.take<int>((size_t)(qh * (pl.nl_cap + 1)));
+      w.nleaf = c.take<int>((size_t)qh);
+      if (pl.appended) w.leafid = c.take<int>((size_t)(qh * pl.nl_cap));
+    }
+    w.tau = c.take<unsigned long long>((size_t)qh);
   }
-  w.tau = c.take<unsigned long long>((size_t)qh);
   const int S = flat ? pl.flat_splits : pl.splits;
   w.part_keys = nullptr;
   w.part_n = nullptr;
@@ -1033,6 +1361,12 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   set_header_check(a, d, L, index, w.status);
   a.Npos = d.n_keys;
   a.leafid = w.leafid;
+  a.G1 = pl.g1;
+  a.slot_row = w.slot_row;
+  a.slot_n = w.slot_n;
+  a.slot_leaf = w.slot_leaf;
+  a.smp = w.smp;
+  a.smpn = w.smpn;
   if (app.on && app.n > 0) {
     const PoolLayout PL = pool_layout(d, app.cap);
     a.app_leaf = (const int*)((const char*)app.pool + PL.leaf);
@@ -1053,6 +1387,56 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
   } while (0)
 
   const int64_t chunk = 32768;   // query heads per grid (grid.y limit)
+  if (!flat && pl.g1 > 0) {
+    // split descent, then the gather that merges in its last workgroup
+    a.S = pl.splits;
+    a.part_cap = (int64_t)a.S * p.k;
+    const int sub = pl.nl_cap / pl.g1;
+    auto dk = descend_split_kernel<KT, LT, DL>;
+    const size_t dlds = ((size_t)2 * sub + std::max(sub, pl.g1) + 1) * 4;
+    prof_begin(LSA_STAGE_DESCEND, st);
+    for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
+      a.qh0 = q0;
+      const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;
+      hipLaunchKernelGGL(dk, dim3((unsigned)pl.g1, (unsigned)nq), dim3(kSplitBlock), dlds, st, a);
+    }
+    prof_end(LSA_STAGE_DESCEND, st);
+    LSA_CHECK("descend");
+    constexpr int U = 8, GB = 256;
+    const int KPWG = 64 / (DL * (int)sizeof(LT) / 16);
+    const int roundg = std::max((GB / 64) * KPWG * U, GB);
+    const int needg = p.k + roundg > 2 * p.k ? p.k + roundg : 2 * p.k;
+    const int M = pick_m(needg, GB);
+#define LSA_GATHER_SPLIT(MV)                                                                    \
+  {                                                                                             \
+    auto gk = gather_split_kernel<LT, DL, MV, U, GB>;                                           \
+    const size_t glds = (size_t)MV * GB * 8 + ((size_t)pl.nl_cap * 3 + 2) * 4;                  \
+    allow_lds(gk, glds);                                                                        \
+    prof_begin(LSA_STAGE_GATHER, st);                                                           \
+    for (int64_t q0 = 0; q0 < QH; q0 += chunk) {                                                \
+      a.qh0 = q0;                                                                               \
+      const int64_t nq = QH - q0 < chunk ? QH - q0 : chunk;                                     \
+      hipLaunchKernelGGL(gk, dim3((unsigned)a.S, (unsigned)nq), dim3(GB), glds, st, a);         \
+    }                                                                                           \
+    prof_end(LSA_STAGE_GATHER, st);                                                             \
+  }
+    switch (M) {
+      case 1: case 2: LSA_GATHER_SPLIT(2) break;
+      case 4: LSA_GATHER_SPLIT(4) break;
+      case 8: LSA_GATHER_SPLIT(8) break;
+      case 16: LSA_GATHER_SPLIT(16) break;
+      default: LSA_GATHER_SPLIT(32) break;
+    }
+#undef LSA_GATHER_SPLIT
+    LSA_CHECK("gather");
+    if (a.S > 1) {
+      prof_begin(LSA_STAGE_MERGE, st);
+      merge_all<LT, DL>(a, p.k, QH, chunk, st);
+      prof_end(LSA_STAGE_MERGE, st);
+      LSA_CHECK("merge");
+    }
+    return LSA_OK;
+  }
   if (!flat) {
     a.S = pl.splits;
     a.part_cap = (int64_t)a.S * p.k;
@@ -1227,6 +1611,14 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
     S = S < 1 ? 1 : (S > 64 ? 64 : S);
   }
   pl.splits = S;
+  // split descent: per-parent beam, fanouts <= 64, at most kSplitMaxB kept
+  // level-1 nodes (one workgroup each); not for the node-major path
+  pl.g1 = 0;
+  if (!flat && p.beam == LSA_BEAM_PER_PARENT && p.b <= kSplitMaxB) {
+    bool ok = true;
+    for (int l = 0; l < d.n_levels; ++l) ok = ok && d.fanout[l] <= 64;
+    if (ok) pl.g1 = p.b;
+  }
   const int64_t th = (int64_t)T * d.n_kv_heads;
   int64_t sf = (256 + th - 1) / th;
   const int64_t by_rows = d.n_keys / 8192;
@@ -1238,7 +1630,10 @@ SelectPlan plan_select(const lsa_index_desc& d, const lsa_select_params& p, int3
   memset(&pl.fs, 0, sizeof(pl.fs));
   if (!flat && !pl.appended) {
     pl.pf = plan_prefill(d, p, T, Hq);
-    if (pl.pf.ok) pl.bytes = pl.pf.bytes;
+    if (pl.pf.ok) {
+      pl.bytes = pl.pf.bytes;
+      pl.g1 = 0;
+    }
   } else if (flat) {
     pl.fs = plan_flat_tiled(d, p, T, Hq);
     if (pl.fs.ok) pl.bytes = pl.fs.bytes;

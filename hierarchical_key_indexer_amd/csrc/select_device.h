@@ -45,7 +45,17 @@ struct SelArgs {
   int64_t app_cap;
   int app_n;                   // appended keys in use: positions N .. N + app_n - 1
   int* leafid;                 // [QH][nl_cap] the selected leaves, ascending (appended mode)
+  // split descent (one workgroup per kept level-1 node) and its gather
+  int G1;                      // level-1 nodes kept per query head = workgroups per query head
+  int* slot_row;               // [QH][nl_cap] first CSR row of each leaf slot
+  int* slot_n;                 // [QH][nl_cap] keys of the slot's leaf, 0 = no leaf
+  int* slot_leaf;              // [QH][nl_cap] leaf id, -1 = no leaf
+  unsigned int* smp;           // [QH][G1][kSplitSamples] sampled candidate score keys (0 = none)
+  int* smpn;                   // [QH][G1] candidates under each kept level-1 node
 };
+
+constexpr int kSplitSamples = 64;   // threshold samples per kept level-1 node
+constexpr int kSplitMaxB = 16;      // split descent: at most 16 kept level-1 nodes
 
 // Wave-wide: does the blob's header hold the expected words hx (magic,
 // version, shape fields, total size, a zero build status)?  Reads the first
@@ -327,6 +337,43 @@ __device__ int pool_stream(const SelArgs& a, int h, int clo, int chi, const int*
   }
   __syncthreads();
   return *n_sh;
+}
+
+// Over a 256-bin histogram (lane l owns bins 4l..4l+3), the bin that holds
+// the need-th unit of weight counted from the top, and in *above the weight of
+// the bins above it; -1 if the histogram holds less than need.  Wave-wide.
+__device__ __forceinline__ int wave_find_bin(const u64* hist, u64 need, u64* above_out) {
+  const int lane = threadIdx.x & 63;
+  u64 hb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
+  const u64 sum = hb[0] + hb[1] + hb[2] + hb[3];
+  u64 incl = sum;   // over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 x = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += x;
+  }
+  const u64 above = incl - sum;
+  const bool mine = above < need && need <= incl;
+  int d = -1;
+  u64 ab = 0ull;
+  if (mine) {
+    u64 acc = above;
+    for (int i = 3; i >= 0; --i) {
+      if (acc + hb[i] >= need) {
+        d = 4 * lane + i;
+        ab = acc;
+        break;
+      }
+      acc += hb[i];
+    }
+  }
+  const u64 bal = __ballot(mine);
+  if (bal == 0ull) return -1;
+  const int src = __ffsll((long long)bal) - 1;
+  *above_out = __shfl(ab, src, 64);
+  return __shfl(d, src, 64);
 }
 
 // Find, in a 4096-bin histogram of 12-bit digits, the bin that holds the

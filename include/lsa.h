@@ -23,8 +23,10 @@
  *  - Every argument is validated on the host before anything is enqueued.
  *    On any error nothing is enqueued, the status is returned and
  *    lsa_last_error() describes it.  No call aborts, exits or throws.
- *  - Status codes: lsa_status.  LSA_ERR_HIP reports a launch failure; faults
- *    inside kernels surface at the caller's next synchronisation.
+ *  - Status codes: lsa_status.  LSA_ERR_HIP reports a launch failure (read
+ *    from the thread's HIP last-error state after the launches, so an error
+ *    the caller's own earlier HIP calls left pending is reported here too);
+ *    faults inside kernels surface at the caller's next synchronisation.
  *  - Device status of a select call (lsa_select, lsa_flat_select): the host
  *    cannot read the device-resident blob without a synchronisation, so the
  *    first kernel of the call compares the blob's header (magic, version,
