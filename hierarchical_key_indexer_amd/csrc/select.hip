@@ -25,6 +25,8 @@
 //   qproj_kernel     query latents for the flat scan
 //   flat_kernel      full scan of one KV head's rows for its G query heads
 //                    (each row read once for G heads), streaming top-k each
+#include <limits.h>
+
 #include <algorithm>
 
 #include "select_device.h"
@@ -151,34 +153,28 @@ __device__ __forceinline__ void wave_select_top32(const uint32_t* key, int need,
   }
 }
 
-// One level of a per-parent descent with every fanout <= 64: for each parent
-// fa[i] (i < nf) the best min(b, F) children by score, ties to the lower id,
-// go to fb[i * bs ..] in child order, -1 padded.  Waves take the parents in
-// turn.  Block-wide (no barrier inside).
-template <typename LT, int DL, int NW>
-__device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, const float* q, const int* fa, int nf,
-                                            int* fb) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int F = a.F[lev];
-  const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
-  const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
-  // A parent's children are one contiguous block of centroid rows: LPK
-  // lanes read a row (16 bytes each, so a load instruction covers KPW
-  // whole rows) and reduce their partial dots with DPP; each lane then
-  // takes its own child's score and the wave ranks them.  A wave loads
-  // two parents' rows before it scores either (bf16 rows, or fp32 rows at
-  // d_l = 32), so their round trips overlap.  Loads past the last child re-read the last row (its score
-  // is dropped), so every load is unconditional.
-  constexpr int E = Lat<LT>::PER16;
-  constexpr int LPK = DL / E;           // lanes per centroid row
-  constexpr int KPW = 64 / LPK;         // rows per load instruction
-  constexpr int NR = 64 / KPW;          // load rounds for up to 64 children
-  const int bs = min(a.b, F);
-  const int lig = lane % LPK, g = lane / LPK;
-  QSlice<LT> qv;
-  qv.load(q + lig * E);
-  auto load = [&](int i, uint4* v, int& o0, int& o1) {
-    const int64_t node0 = (int64_t)fa[i] * F;
+// One parent's children at a level with fanout <= 64: their scoring
+// centroids are one contiguous block of rows.  LPK lanes read a row (16 bytes
+// each, so a load instruction covers KPW whole rows) and reduce their partial
+// dots with DPP; each lane then takes its own child's score and the wave
+// ranks them.  Loads past the last child re-read the last row (its score is
+// dropped), so every load is unconditional.
+template <typename LT, int DL>
+struct ChildBlock {
+  static constexpr int E = Lat<LT>::PER16;
+  static constexpr int LPK = DL / E;        // lanes per centroid row
+  static constexpr int KPW = 64 / LPK;      // rows per load instruction
+  static constexpr int NR = 64 / KPW;       // load rounds for up to 64 children
+  uint4 v[NR];
+  int o0, o1;                               // CSR range of child `lane`
+
+  // Wave-wide: issue the loads of node `parent`'s children at level lev.
+  __device__ __forceinline__ void load(const SelArgs& a, int lev, int h, int64_t parent) {
+    const int lane = threadIdx.x & 63, lig = lane % LPK, g = lane / LPK;
+    const int F = a.F[lev];
+    const LT* cs = (const LT*)a.cscore[lev] + (size_t)h * a.P[lev] * DL;
+    const int* off = a.off[lev] + (size_t)h * (a.P[lev] + 1);
+    const int64_t node0 = parent * F;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int c = min(r * KPW + g, F - 1);
@@ -187,8 +183,14 @@ __device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, co
     const int c = min(lane, F - 1);
     o0 = off[node0 + c];
     o1 = off[node0 + c + 1];
-  };
-  auto pick = [&](int i, const uint4* v, int o0, int o1) {
+  }
+
+  // Wave-wide: the parent's best bs children (ties to the lower id) into
+  // out[0..bs) in child order, -1 padded.  q: the query latent (LDS).
+  __device__ __forceinline__ void pick(const float* q, int F, int bs, int64_t parent, int* out) const {
+    const int lane = threadIdx.x & 63, lig = lane % LPK;
+    QSlice<LT> qv;
+    qv.load(q + lig * E);
     float part[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) part[r] = group_sum_lead<LPK>(qv.dot(v[r]));
@@ -202,27 +204,38 @@ __device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, co
     const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
     u64 in[1];
     wave_select_top32<1>(&key, bs, in);
-    // kept in child order (ties went to the lower child id)
-    if ((in[0] >> lane) & 1ull) fb[i * bs + (int)mbcnt64(in[0])] = fa[i] * F + lane;
-    for (int r = __popcll(in[0]) + lane; r < bs; r += 64) fb[i * bs + r] = -1;
-  };
-  if constexpr (NR <= 8) {
+    if ((in[0] >> lane) & 1ull) out[(int)mbcnt64(in[0])] = (int)(parent * F + lane);
+    for (int r = __popcll(in[0]) + lane; r < bs; r += 64) out[r] = -1;
+  }
+};
+
+// One level of a per-parent descent with every fanout <= 64: for each parent
+// fa[i] (i < nf) the best min(b, F) children go to fb[i * bs ..] in child
+// order, -1 padded.  A wave loads two parents' rows before it scores either
+// (bf16 rows, or fp32 rows at d_l = 32), so their round trips overlap.
+// Block-wide (no barrier inside).
+template <typename LT, int DL, int NW>
+__device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, const float* q, const int* fa, int nf,
+                                            int* fb) {
+  using CB = ChildBlock<LT, DL>;
+  const int w = threadIdx.x >> 6;
+  const int F = a.F[lev];
+  const int bs = min(a.b, F);
+  if constexpr (CB::NR <= 8) {
     for (int i = w; i < nf; i += 2 * NW) {
       const bool two = i + NW < nf;
-      uint4 va[NR], vb[NR];
-      int a0, a1, b0, b1;
-      load(i, va, a0, a1);
-      load(two ? i + NW : i, vb, b0, b1);
-      pick(i, va, a0, a1);
-      if (two) pick(i + NW, vb, b0, b1);
+      CB x, y;
+      x.load(a, lev, h, fa[i]);
+      y.load(a, lev, h, fa[two ? i + NW : i]);
+      x.pick(q, F, bs, fa[i], fb + i * bs);
+      if (two) y.pick(q, F, bs, fa[i + NW], fb + (i + NW) * bs);
     }
   } else {
     // fp32 rows at d_l = 64: two parents' rows would not fit the registers
     for (int i = w; i < nf; i += NW) {
-      uint4 va[NR];
-      int a0, a1;
-      load(i, va, a0, a1);
-      pick(i, va, a0, a1);
+      CB x;
+      x.load(a, lev, h, fa[i]);
+      x.pick(q, F, bs, fa[i], fb + i * bs);
     }
   }
 }
@@ -565,12 +578,14 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (!check_index_first(a)) return;        // block-uniform; the gather reads the status
   const int p = a.q_pos[t];
+  // level 1: the root's children do not depend on the query, so wave 0 loads
+  // them before the query latent (their round trip overlaps the projection's)
+  ChildBlock<LT, DL> root;
+  if (w == 0) root.load(a, 0, h, 0);
   query_latent<KT, LT, DL>(a, qh, h, qin, q);
   if (g == 0 && threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;   // the gather's lists (S > 1 only)
-  // level 1: the root's kept children, ascending; this workgroup takes the g-th
-  if (threadIdx.x == 0) fa[0] = 0;
-  __syncthreads();
-  small_level<LT, DL, NW>(a, 0, h, q, fa, 1, fb);
+  // the root's kept children, ascending; this workgroup takes the g-th
+  if (w == 0) root.pick(q, a.F[0], min(a.b, a.F[0]), 0, fb);
   __syncthreads();
   const int my = fb[g];
   __syncthreads();
@@ -603,9 +618,11 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
       lr[i] = r0;
       c += r1 - r0;
     } else {
+      // an empty slot repeats the workgroup's last leaf (none: past every
+      // id), so the slots' leaf ids stay non-decreasing across workgroups
       srow[i] = -1;
       sn[i] = 0;
-      sleaf[i] = -1;
+      sleaf[i] = nf > 0 ? fa[nf - 1] : INT_MAX;
     }
   }
   int ng;
@@ -668,145 +685,239 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
 // The candidates are split over S workgroups as in gather_kernel (with S > 1
 // merge_kernel takes the appended lists; workgroup 0 leaves it the compacted
 // leaf list and the threshold, for its exact re-score).
+// LDS scratch of block_weighted_threshold.
+struct ThrScratch {
+  uint32_t hist[4][256];       // per-wave weighted histograms
+  uint32_t lo[4], hi[4];
+  int d;
+  uint32_t above;
+};
+
+// Block-wide (256 threads): the largest tau such that the sample keys at or
+// above it weigh at least `target`.  Thread t holds NS keys (0 = none) and
+// their weights (integers: the sums are exact, so every workgroup that runs
+// this on the same samples gets the same tau).  Two passes of 8-bit digits
+// below the bits all the keys share, each a per-wave histogram in LDS (the
+// digits spread the keys, so the atomics rarely collide), summed over the
+// waves; the lower bits of tau stay 0, so the keys at or above it weigh at
+// least the target.  0 when all the samples weigh less.
+template <int NS>
+__device__ uint32_t block_weighted_threshold(const uint32_t* key, const uint32_t* wt, uint32_t target,
+                                             ThrScratch* sc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    if (key[j] != 0u) {
+      lo = min(lo, key[j]);
+      hi = max(hi, key[j]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) {
+    sc->lo[w] = lo;
+    sc->hi[w] = hi;
+  }
+  for (int i = lane; i < 256; i += 64) sc->hist[w][i] = 0u;
+  __syncthreads();
+  lo = min(min(sc->lo[0], sc->lo[1]), min(sc->lo[2], sc->lo[3]));
+  hi = max(max(sc->hi[0], sc->hi[1]), max(sc->hi[2], sc->hi[3]));
+  if (hi == 0u) return 0u;                   // block-uniform: no sample
+  const int top = lo == hi ? 0 : 32 - __clz((int)(lo ^ hi));       // bits [0, top) differ
+  uint32_t mask = top >= 32 ? 0u : ~0u << top;
+  uint32_t prefix = lo & mask;
+  uint32_t need = target;
+  for (int pass = 0, hb = top; pass < 2 && hb > 0; ++pass) {
+    const int lb = hb > 8 ? hb - 8 : 0;
+    const uint32_t dmask = (1u << (hb - lb)) - 1u;
+    if (pass > 0) {
+      for (int i = lane; i < 256; i += 64) sc->hist[w][i] = 0u;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&sc->hist[w][(key[j] >> lb) & dmask], wt[j]);
+    __syncthreads();
+    {
+      const uint32_t t = sc->hist[0][threadIdx.x] + sc->hist[1][threadIdx.x] + sc->hist[2][threadIdx.x] +
+                         sc->hist[3][threadIdx.x];
+      __syncthreads();
+      sc->hist[0][threadIdx.x] = t;
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane l owns bins 4l..4l+3; weight above a bin comes from higher lanes
+      const uint32_t h0 = sc->hist[0][4 * lane], h1 = sc->hist[0][4 * lane + 1], h2 = sc->hist[0][4 * lane + 2],
+                     h3 = sc->hist[0][4 * lane + 3];
+      const uint32_t s4 = h0 + h1 + h2 + h3;
+      uint32_t incl = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = (uint32_t)__shfl_down((int)incl, o, 64);
+        if (lane + o < 64) incl += x;
+      }
+      const uint32_t above = incl - s4;
+      if (lane == 0) sc->d = -1;
+      if (above < need && need <= incl) {
+        uint32_t acc = above;
+        int d;
+        if (acc + h3 >= need) d = 4 * lane + 3;
+        else if ((acc += h3) + h2 >= need) d = 4 * lane + 2;
+        else if ((acc += h2) + h1 >= need) d = 4 * lane + 1;
+        else { acc += h1; d = 4 * lane; }
+        sc->d = d;
+        sc->above = acc;
+      }
+    }
+    __syncthreads();
+    const int d = sc->d;
+    const uint32_t ab = sc->above;
+    __syncthreads();
+    if (d < 0) return pass == 0 ? 0u : prefix;    // block-uniform: less weight than the target
+    prefix |= (uint32_t)d << lb;
+    mask |= dmask << lb;
+    need -= ab;
+    hb = lb;
+  }
+  return prefix;
+}
+
+// The gather of the split descent.  Its first loads take the query head's
+// leaf slots, the subtrees' samples and the query latent together.  The
+// candidates are numbered in slot order (an empty slot is a leaf of no key),
+// and the threshold is the weighted sample quantile with about 2k candidates
+// expected above it: a sample of subtree g stands for
+// n_g / min(n_g, kSplitSamples) candidates.  Every workgroup of the query head
+// computes the same value.  The candidates are split over S workgroups as in
+// gather_kernel (with S > 1 merge_kernel takes the appended lists; workgroup
+// 0 leaves it the leaf list and the threshold, for its exact re-score).
 template <typename LT, int DL, int M, int U, int BLOCK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(3))) void gather_split_kernel(SelArgs a) {
   constexpr int CAP = M * BLOCK;
-  constexpr int NS4 = kSplitMaxB * kSplitSamples / BLOCK;   // samples per thread
+  constexpr int NSB = kSplitMaxB * kSplitSamples / BLOCK; // samples per thread
+  constexpr int MAXPER = 4096 / BLOCK;                    // leaf slots per thread, at most
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ RadixScratch rs;
-  __shared__ int n_sh, base_sh, d_sh, nl_sh;
+  __shared__ int n_sh, base_sh;
   __shared__ int wsum[BLOCK / 64];
+  __shared__ ThrScratch tsc;
   __shared__ int gsz[kSplitMaxB];
-  __shared__ u64 hist[256];
-  __shared__ u64 ab_sh;
   __shared__ float qs[DL];
   u64* buf = (u64*)smem;
-  int* lpre = (int*)(buf + CAP);            // [nl_cap + 1]
-  int* lrow = lpre + a.nl_cap + 1;          // [nl_cap]
-  int* lid = lrow + a.nl_cap;               // [nl_cap]
+  int* lpre = (int*)(buf + CAP);            // [nl_cap + 1] candidates before each slot
+  int* lrow = lpre + a.nl_cap + 1;          // [nl_cap] first CSR row of each slot's leaf
+  int* lid = lrow + a.nl_cap;               // [nl_cap] leaf id of each slot, non-decreasing
   const int64_t qh = a.qh0 + blockIdx.y;
   const int s = blockIdx.x;
   const int t = (int)(qh / a.Hq), hq = (int)(qh % a.Hq), h = hq / a.G;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // the first loads, independent of one another
+  const int nlc = a.nl_cap;
+  const int per = (nlc + BLOCK - 1) / BLOCK;
+  const int i0 = min(nlc, (int)threadIdx.x * per);
+  const bool want_lid = a.app_n > 0 || (s == 0 && a.out_leaves);
+  // the first loads, independent of one another: position, status, this
+  // thread's leaf slots, (wave 0) the samples and their subtree's size, the
+  // query latent
   const int p = a.q_pos[t];
   const int bad = *a.status;
-  const int nsmp = a.G1 * kSplitSamples;
-  uint32_t sk[NS4];
+  int vn[MAXPER], vr[MAXPER];
 #pragma unroll
-  for (int j = 0; j < NS4; ++j) {
+  for (int j = 0; j < MAXPER; ++j) {
+    const int i = i0 + j;
+    const bool in = j < per && i < nlc;
+    vn[j] = in ? a.slot_n[qh * nlc + i] : 0;
+    vr[j] = in ? a.slot_row[qh * nlc + i] : -1;
+  }
+  const int nsmp = a.G1 * kSplitSamples;
+  uint32_t sk[NSB];
+#pragma unroll
+  for (int j = 0; j < NSB; ++j) {
     const int i = threadIdx.x + j * BLOCK;
     sk[j] = i < nsmp ? a.smp[qh * nsmp + i] : 0u;
   }
   const int gn = (int)threadIdx.x < a.G1 ? a.smpn[qh * a.G1 + threadIdx.x] : 0;
   const float qv = threadIdx.x < DL ? a.qlat[qh * DL + threadIdx.x] : 0.f;
-  for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) {
-    lpre[i] = a.slot_n[qh * a.nl_cap + i];
-    lrow[i] = a.slot_row[qh * a.nl_cap + i];
-    lid[i] = a.slot_leaf[qh * a.nl_cap + i];
-  }
   if ((int)threadIdx.x < a.G1) gsz[threadIdx.x] = gn;
+  if (want_lid)
+    for (int i = threadIdx.x; i < nlc; i += BLOCK) lid[i] = a.slot_leaf[qh * nlc + i];
   if (threadIdx.x < DL) qs[threadIdx.x] = qv;
   if (bad || p < 0 || (int64_t)p >= a.Npos) {   // block-uniform
     if (s == 0) {
       write_invalid_row<BLOCK>(a.width, a.k, a.out_idx + qh * a.width, a.out_scores ? a.out_scores + qh * a.k : nullptr);
       if (a.out_leaves)
-        for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) a.out_leaves[qh * a.nl_cap + i] = -1;
+        for (int i = threadIdx.x; i < nlc; i += BLOCK) a.out_leaves[qh * nlc + i] = -1;
     }
     return;
   }
-  __syncthreads();
-  // compact the slots in order: each thread its contiguous chunk
-  {
-    constexpr int MAXPER = 4096 / BLOCK;
-    const int per = (a.nl_cap + BLOCK - 1) / BLOCK;
-    const int i0 = min(a.nl_cap, (int)threadIdx.x * per);
-    int vn[MAXPER], vr[MAXPER], vl[MAXPER];
-    int c = 0, sz = 0;
+  // candidates before each slot
+  int sz = 0;
 #pragma unroll
-    for (int j = 0; j < MAXPER; ++j) {
-      const int i = i0 + j;
-      const bool in = j < per && i < a.nl_cap;
-      vn[j] = in ? lpre[i] : 0;
-      vr[j] = in ? lrow[i] : 0;
-      vl[j] = in ? lid[i] : -1;
-      c += vn[j] > 0 ? 1 : 0;
-      sz += vn[j];
-    }
-    int nl, total;
-    int pos = block_exclusive_scan<BLOCK>(c, wsum, &nl);
-    int run = block_exclusive_scan<BLOCK>(sz, wsum, &total);   // ends with a barrier: the reads are done
+  for (int j = 0; j < MAXPER; ++j) sz += vn[j];
+  int total32;
+  int run = block_exclusive_scan<BLOCK>(sz, wsum, &total32);
 #pragma unroll
-    for (int j = 0; j < MAXPER; ++j)
-      if (vn[j] > 0) {
-        lrow[pos] = vr[j];
-        lpre[pos] = run;
-        lid[pos] = vl[j];
-        run += vn[j];
-        ++pos;
-      }
-    if (threadIdx.x == 0) {
-      lpre[nl] = total;
-      nl_sh = nl;
+  for (int j = 0; j < MAXPER; ++j)
+    if (j < per && i0 + j < nlc) {
+      lrow[i0 + j] = vr[j];
+      lpre[i0 + j] = run;
+      run += vn[j];
     }
-  }
+  if (threadIdx.x == 0) lpre[nlc] = total32;
+  const int64_t total = total32;
   __syncthreads();
-  const int nl = nl_sh;
-  const int64_t total = lpre[nl];
+  const int nl = nlc;
   if (s == 0) {
-    // the leaf list for the merge kernel's exact re-score, and the leaves out
-    for (int i = threadIdx.x; i <= nl; i += BLOCK) a.leafpre[qh * (a.nl_cap + 1) + i] = lpre[i];
-    for (int i = threadIdx.x; i < nl; i += BLOCK) a.leafrow[qh * a.nl_cap + i] = lrow[i];
+    // the leaf list for the merge kernel's exact re-score
+    for (int i = threadIdx.x; i <= nlc; i += BLOCK) a.leafpre[qh * (nlc + 1) + i] = lpre[i];
+    for (int i = threadIdx.x; i < nlc; i += BLOCK) a.leafrow[qh * nlc + i] = lrow[i];
     if (a.leafid)
-      for (int i = threadIdx.x; i < nl; i += BLOCK) a.leafid[qh * a.nl_cap + i] = lid[i];
-    if (threadIdx.x == 0) a.nleaf[qh] = nl;
-    if (a.out_leaves)
-      for (int i = threadIdx.x; i < a.nl_cap; i += BLOCK) a.out_leaves[qh * a.nl_cap + i] = i < nl ? lid[i] : -1;
-  }
-  // threshold: weighted quantile of the samples, about 2k candidates above
-  u64 thr0 = 0ull;
-  if (total > 4 * (int64_t)a.k) {
-    const u64 target = (u64)a.k * 2u * 16u;
-    int d1 = -1, d2 = -1;
-    u64 ab1 = 0ull;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int i = threadIdx.x; i < 256; i += BLOCK) hist[i] = 0ull;
-      __syncthreads();
+      for (int i = threadIdx.x; i < nlc; i += BLOCK) a.leafid[qh * nlc + i] = lid[i];
+    if (threadIdx.x == 0) a.nleaf[qh] = nlc;
+    if (a.out_leaves) {
+      // the kept leaves, ascending, then -1
+      int c = 0;
 #pragma unroll
-      for (int j = 0; j < NS4; ++j) {
-        const int i = threadIdx.x + j * BLOCK;
-        if (sk[j] == 0u || (pass == 1 && (int)(sk[j] >> 24) != d1)) continue;
-        const int gi = i / kSplitSamples;
-        const int ng = gsz[gi], nsg = min(ng, kSplitSamples);
-        const u64 wt = (u64)ng * 16u / (u64)nsg;
-        atomicAdd(&hist[pass == 0 ? (sk[j] >> 24) : ((sk[j] >> 16) & 0xFFu)], wt);
-      }
-      __syncthreads();
-      if (w == 0) {
-        u64 ab = 0ull;
-        const int d = wave_find_bin(hist, pass == 0 ? target : target - ab1, &ab);
-        if (lane == 0) {
-          d_sh = d;
-          ab_sh = ab;
-        }
-      }
-      __syncthreads();
-      if (pass == 0) {
-        d1 = d_sh;
-        ab1 = ab_sh;
-      } else {
-        d2 = d_sh;
-      }
-      __syncthreads();
-      if (d1 < 0) break;                      // block-uniform: fewer than the target: take every candidate
+      for (int j = 0; j < MAXPER; ++j) c += vn[j] > 0 ? 1 : 0;
+      int nv;
+      int pos = block_exclusive_scan<BLOCK>(c, wsum, &nv);
+#pragma unroll
+      for (int j = 0; j < MAXPER; ++j)
+        if (vn[j] > 0) a.out_leaves[qh * nlc + pos++] = lid[i0 + j];
+      for (int i = nv + threadIdx.x; i < nlc; i += BLOCK) a.out_leaves[qh * nlc + i] = -1;
     }
-    if (d1 >= 0 && d2 >= 0) thr0 = (u64)(((uint32_t)d1 << 24) | ((uint32_t)d2 << 16)) << 32;
   }
-  if (s == 0 && threadIdx.x == 0) a.tau[qh] = thr0;
+  // threshold: the weighted quantile of the samples with about 2k candidates
+  // above, computed by wave 0 once the first rows' loads are in flight
+  auto late = [&](u64) -> u64 {
+    uint32_t tau = 0u;
+    if (total > 4 * (int64_t)a.k) {          // block-uniform
+      // a sample of subtree g weighs n_g / min(n_g, kSplitSamples) candidates, in 1/16 units
+      uint32_t wt[NSB];
+#pragma unroll
+      for (int j = 0; j < NSB; ++j) {
+        const int g = (int)(threadIdx.x + j * BLOCK) / kSplitSamples;
+        const int ng = g < a.G1 ? gsz[g] : 0;
+        const int nsg = min(ng, kSplitSamples);
+        wt[j] = nsg > 0 ? (uint32_t)((uint64_t)ng * 16u / (uint64_t)nsg) : 0u;
+      }
+      tau = block_weighted_threshold<NSB>(sk, wt, (uint32_t)a.k * 32u, &tsc);
+    }
+    return (u64)tau << 32;
+  };
   const int clo = a.sink, chi = p - a.window;
   const int64_t lo = total * s / a.S, hi = total * (s + 1) / a.S;
   const int64_t plo = (int64_t)a.app_n * s / a.S, phi = (int64_t)a.app_n * (s + 1) / a.S;
-  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, thr0, buf, &n_sh, &rs, qs);
+  u64 thr0 = 0ull;
+  auto late_keep = [&](u64 t) -> u64 {
+    thr0 = late(t);
+    return thr0;
+  };
+  int n = gather_stream<LT, DL, M, U, BLOCK>(a, qh, h, clo, chi, lpre, lrow, nl, lo, hi, 0ull, buf, &n_sh, &rs, qs,
+                                             late_keep);
+  if (s == 0 && threadIdx.x == 0) a.tau[qh] = thr0;   // for the merge kernel's exact re-score
   if (a.app_n > 0) n = pool_stream<LT, DL, M, BLOCK>(a, h, clo, chi, lid, nl, plo, phi, thr0, buf, n, &n_sh, &rs, qs);
   int32_t* orow = a.out_idx + qh * a.width;
   float* srow = a.out_scores ? a.out_scores + qh * a.k : nullptr;

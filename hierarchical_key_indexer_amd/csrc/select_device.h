@@ -206,16 +206,23 @@ __device__ void append_part(const SelArgs& a, int64_t qh, const u64* buf, int n,
 // gather-and-score
 // ---------------------------------------------------------------------------
 
+// The threshold of a gather, known before it starts.
+struct FixedThr {
+  __device__ __forceinline__ u64 operator()(u64 thr) const { return thr; }
+};
+
 // Score candidates [lo, hi) of a query head's leaf list (CSR rows of KV head
 // h; lpre / lrow in LDS) and append the rank keys above thr to buf, keeping
 // at most the best k when the buffer fills (streaming radix-select
 // compaction).  Returns the number of keys left in buf.  The query latent is
 // read from qsrc when given (visible to the block), else from a.qlat.
-// Block-wide.
-template <typename LT, int DL, int M, int U, int BLOCK>
+// `late(thr)` gives the threshold actually used; it runs once the first rows'
+// loads are in flight (block-wide; it may synchronise the block), so a
+// threshold computed there costs no round trip of its own.  Block-wide.
+template <typename LT, int DL, int M, int U, int BLOCK, typename Late = FixedThr>
 __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int chi, const int* lpre,
                              const int* lrow, int nl, int64_t lo, int64_t hi, u64 thr, u64* buf, int* n_sh,
-                             RadixScratch* rs, const float* qsrc = nullptr) {
+                             RadixScratch* rs, const float* qsrc = nullptr, Late late = Late()) {
   constexpr int NW = BLOCK / 64;
   constexpr int CAP = M * BLOCK;
   constexpr int E = Lat<LT>::PER16;              // latent elements per lane load
@@ -261,6 +268,7 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
     }
   };
   if (rounds > 0) fetch(0, v, idx);
+  thr = late(thr);
   for (int64_t r = 0; r < rounds; ++r) {
     if (r + 1 < rounds) fetch(r + 1, vn, idxn);
     bool pr[U];
