@@ -1,8 +1,8 @@
 // Exact sparse attention over the selected keys.  The page "Latent Sparse
 // Attention (LSA): The 72.4x and 22.7x Speedups, and What They Compare
-// Against" (section "How does LSA work?", step 3) has the query attend to the
-// selected long-range keys plus the attention sink and the local window, with
-// the attention itself unchanged: softmax attention restricted to the keys
+// Against" (section "How does LSA work?", step 3): what a query reads is the
+// indexer's far keys, the sink positions and the recent window, and the
+// attention computation stays the ordinary one: softmax attention restricted to the keys
 // that an lsa_select row lists,
 //   out = sum_j softmax_j(scale * q . k_j) v_j   over the entries j >= 0,
 // an entry listed twice counting twice, an entry outside [0, N) counting as

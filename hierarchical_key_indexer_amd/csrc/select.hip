@@ -2,10 +2,9 @@
 // and the full-scan baseline.
 //
 // Steps 2 and 3 of "How does LSA work?" (page "Latent Sparse Attention (LSA):
-// The 72.4x and 22.7x Speedups, and What They Compare Against"): a query
-// scores the bucket centroids first, drills into the selected buckets, and
-// attends to the selected long-range keys plus the attention sink and a local
-// window.  The full scan is the dashed, quadratic path of the flowchart on
+// The 72.4x and 22.7x Speedups, and What They Compare Against"): the query is
+// compared with bucket centroids, only the winning buckets' keys are scored,
+// and its row lists those keys with the sink positions and the recent window.  The full scan is the dashed, quadratic path of the flowchart on
 // "Latent Sparse Attention: tree search over keys for 10M-token context".
 //
 //   descend_kernel   one workgroup per query head: the query's latent

@@ -346,9 +346,9 @@ int lsa_pca_map(const lsa_index_desc* desc, const double* cov, float* W, double*
 
 /* ---- exact sparse attention over the selected keys ------------------------------
  * "Latent Sparse Attention (LSA): The 72.4x and 22.7x Speedups, and What They
- * Compare Against", section "How does LSA work?", step 3: the query attends to
- * the selected long-range keys plus the attention sink and the local window,
- * with the attention itself unchanged.  For every (token t, query head hq):
+ * Compare Against", section "How does LSA work?", step 3: a query reads the
+ * far keys the indexer chose, the sink positions and its recent window, and
+ * the attention computation is the ordinary one.  For every (token t, query head hq):
  *   out[t][hq] = sum_j softmax_j(scale * q . k_j) v_j
  * over the entries j of row idx[t][hq] (an lsa_select output row, or any list);
  * an entry outside [0, N) is padding, an entry listed twice counts twice, and a

@@ -12,15 +12,18 @@ and What They Compare Against", wpnews.pro, section "How does LSA work?"):
 
 1. keys are clustered into buckets in a latent space, organised as a hierarchy
    (step 1) -> ``latent_keys`` + ``build_index`` (Lloyd k-means per node);
-2. a query scores the bucket centroids first and then drills into the chosen
-   buckets (step 2) -> ``descend`` + the key stage of ``select_one``;
-3. the query attends to the chosen long-range keys plus the attention sink and
-   a local window (step 3) -> ``segments`` and the output row of ``select``.
+2. selection works on clusters before keys: the query is compared with the
+   bucket centroids, and only the buckets that win are opened and their keys
+   scored (step 2) -> ``descend`` + the key stage of ``select_one``;
+3. what the query finally reads is those winning far keys, together with the
+   first (sink) positions and the positions just before it (step 3) ->
+   ``segments`` and the output row of ``select``.
 
 The same descent is drawn on "Latent Sparse Attention: tree search over keys
 for 10M-token context" (bayesiansapien wiki), TL;DR and flowchart: the query
-scores cluster centroids and descends into the best few buckets instead of a
-full key scan; the full key scan is ``flat_select``.
+compares the query with cluster centroids and walks down into a handful of the
+highest-scoring buckets, in place of scoring every key; scoring every key is
+``flat_select``.
 
 Readings taken where the pages are silent:
 per-parent beam (every kept node keeps its top-b children), inner-product
@@ -439,8 +442,8 @@ def _top_by_score(ids: np.ndarray, scores: np.ndarray, n: int) -> np.ndarray:
 
 
 def descend(hidx: HeadIndex, fanout: tuple, qlat: np.ndarray, b: int, beam: str) -> np.ndarray:
-    """Centroid scoring and descent (step 2 of "How does LSA work?"; "descends
-    into the best few buckets", bayesiansapien TL;DR).
+    """Centroid scoring and descent (step 2 of "How does LSA work?"; the
+    bayesiansapien TL;DR's tree search over a few buckets).
 
     Level by level, the children of every kept node are scored by the inner
     product q~ . mu^ with the scoring copy of their centroid; empty children
@@ -759,7 +762,7 @@ def dot_scale(qlat: np.ndarray, klat: np.ndarray) -> np.ndarray:
 # exact sparse attention over the selected keys
 # ----------------------------------------------------------------------------
 # [WPN] "How does LSA work?", step 3: the query attends to the selected
-# long-range keys plus the attention sink and the local window, and the
+# far keys the indexer chose, the sink positions and the recent window, and the
 # attention kernel itself is unchanged.  So the step after the indexer is
 # ordinary softmax attention restricted to the row's listed keys:
 #   out = sum_j softmax_j(scale * q . k_j) v_j  over the entries j of the row
