@@ -1498,7 +1498,8 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
 
   const int64_t chunk = 32768;   // query heads per grid (grid.y limit)
   if (!flat && pl.g1 > 0) {
-    // split descent, then the gather that merges in its last workgroup
+    // split descent, the gather over its leaf slots, then the merge of the
+    // gather's splits
     a.S = pl.splits;
     a.part_cap = (int64_t)a.S * p.k;
     const int sub = pl.nl_cap / pl.g1;
