@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
   constexpr int PL = 32 * RP / 64;                 // 16-byte parts per lane and 32-key tile
   // main mode: keys at or above a row's threshold are staged per wave (rank
   // key and the row's lane, 0..31) and flushed at the end of every item
-  constexpr int SST = SAMPLE ? 64 : kPfStage;
+  constexpr int SST = SAMPLE ? 1 : kPfStage;
   constexpr int SE = SST / 64;
   __shared__ __align__(16) unsigned char ktile[kPfNW][32 * DL * 2];
   __shared__ u64 skey[kPfNW][SST];
@@ -467,18 +467,143 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     const int r_in = min(ii * 32 + l32, (int)lcn[cc] - 1);
     return a.Enext[lst[cc] + r_in];
   };
-  // the next item's entries are loaded while the current item is scored
-  // (past the last item, the current item's again)
-  const int stride = a.CH * kPfNW;
-  int2 enext = make_int2(0, 0);
-  {
-    const int it0 = ch * kPfNW + w;
-    if (it0 < items) {
-      int cc, ii;
-      item_of(it0, &cc, &ii);
-      enext = entry_of(cc, ii);
+  // Key tiles: a tile is loaded coalesced (eight lanes per 128-byte key row;
+  // a lane past the leaf reads its last key, masked by position where it is
+  // scored), written to the wave's LDS tile with the 16-byte parts of row r
+  // XOR-swizzled by r % 8, and read back as an MFMA operand (lane l32 takes
+  // key l32's parts) with no bank conflicts.  The wave's LDS accesses
+  // execute in order, so one tile buffer serves every tile.
+  unsigned char* kl = ktile[w];
+  auto put_parts = [&](const u32x4* P) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int c = lane + 64 * q, r = c / RP, pt = c % RP;
+      *(u32x4*)(kl + r * RP * 16 + ((pt ^ (r & 7)) % RP) * 16) = P[q];
     }
-  }
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto get_a = [&](v8s* A) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int pt = 2 * s + half;
+      A[s] = as_v8s(*(const uint4*)(kl + l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16));
+    }
+  };
+  if constexpr (SAMPLE) {
+    // Sample pass: the leaf's first key tile is scored against the item's
+    // rows and the first spl scores of every row are kept.  The next item's
+    // entries are loaded while the current item is scored (past the last
+    // item, the current item's again).
+    const int stride = a.CH * kPfNW;
+    int2 enext = make_int2(0, 0);
+    {
+      const int it0 = ch * kPfNW + w;
+      if (it0 < items) {
+        int cc, ii;
+        item_of(it0, &cc, &ii);
+        enext = entry_of(cc, ii);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0) only
+    for (int it = ch * kPfNW + w; it < items; it += stride) {
+      int c, i;
+      item_of(it, &c, &i);
+      const int2 ecur = enext;
+      {
+        int cn, in;
+        item_of(it + stride < items ? it + stride : it, &cn, &in);
+        enext = entry_of(cn, in);
+      }
+      // this lane's row (lanes l and l + 32 share row l % 32), -1 past the
+      // end of the leaf's rows
+      const int row = i * 32 + l32 < (int)lcn[c] ? ecur.x : -1;
+      const int slot = ecur.y;
+      const int o0 = o0s[c], o1 = o1s[c];
+      // The key tile depends only on the leaf's range and the row data only
+      // on the entry: every load below is unconditional (a lane with no row
+      // reads row 0's data and drops it), so they all share one round trip.
+      u32x4 PK[PL];
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const int cq = lane + 64 * q;
+        const int krow = max(0, min(o0 + cq / RP, o1 - 1));   // in range for an empty leaf too
+        PK[q] = *(const u32x4*)(latb + (size_t)krow * DL + (cq % RP) * 8);
+      }
+      const int jr = permb[max(0, min(o0 + l32, o1 - 1))];
+      const int rq = row >= 0 ? row : 0;
+      const int pq = a.s.q_pos[rq / a.s.Hq];
+      // the rows' latents (the B operand, a missing row as zeros) come
+      // coalesced through the LDS tile as well: one key tile per item makes
+      // the row load as large as the key load
+      v8s Bq[KS];
+      {
+        u32x4 P[PL];
+#pragma unroll
+        for (int q = 0; q < PL; ++q) {
+          const int cq = lane + 64 * q;
+          const int rr = __shfl(row, cq / RP, 64);
+          P[q] = *(const u32x4*)(a.qlat16 + (size_t)(rr >= 0 ? rr : 0) * DL + (cq % RP) * 8);
+          if (rr < 0) P[q] = u32x4{0u, 0u, 0u, 0u};
+        }
+        put_parts(P);
+        get_a(Bq);
+      }
+      const int chi = (row >= 0 && pq >= 0 && (int64_t)pq < a.s.N) ? pq - a.s.window : -1;
+      if (o1 <= o0) continue;
+      put_parts(PK);
+      v8s A[KS];
+      get_a(A);
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
+      // lane holds row l32 against keys m = 8(r/4) + 4 half + r%4; key l32's
+      // position as a candidate test value (INT_MAX for a missing key or one
+      // inside the sink)
+      const int jl = (o0 + l32 < o1 && jr >= sink) ? jr : INT_MAX;
+      // registers 4g..4g+3 hold samples m0..m0+3 (m0 = 8g + 4 half): one
+      // 8-byte store per group, zero past spl or for a non-candidate
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int m0 = 8 * g + 4 * half;
+        u64 pk = 0ull;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int jm = __shfl(jl, m0 + cc, 64);
+          const u64 v = (m0 + cc < a.spl && jm <= chi) ? (u64)(order_u32(acc[4 * g + cc]) >> 16) : 0ull;
+          pk |= v << (16 * cc);
+        }
+        if (m0 < a.spl && row >= 0) *(u64*)(a.smp + ((size_t)row * a.nl + slot) * a.spl4 + m0) = pk;
+      }
+    }
+  } else {
+  // Main pass.  Every load is issued well before its use: an item's row
+  // data (row latents, threshold, position) once at its start and awaited
+  // at once, since every tile needs them; key tiles one ahead, the last tile
+  // of an item fetching the next item's first, so a tile's keys arrive while
+  // the tile before it is scored.  Entries hold rows only here.
+  const int* Erow = (const int*)a.Enext;
+  auto row_entry = [&](int cc, int ii) {
+    const int r_in = min(ii * 32 + l32, (int)lcn[cc] - 1);
+    return Erow[2 * (size_t)(lst[cc] + r_in)];
+  };
+  // key tile kt of the CSR range [lo, hi) (a lane past the range reads its
+  // last key, masked by position where it is scored; the range is never
+  // empty) and key l32's position
+  auto load_tile = [&](int lo, int hi, int kt, u32x4* P, int* jraw) {
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int c = lane + 64 * q;
+      const int krow = max(0, min(lo + 32 * kt + c / RP, hi - 1));
+      P[q] = *(const u32x4*)(latb + (size_t)krow * DL + (c % RP) * 8);
+    }
+    *jraw = permb[max(0, min(lo + 32 * kt + l32, hi - 1))];
+  };
+  const int stride = a.CH * kPfNW;
+  int it = ch * kPfNW + w;
+  if (it >= items) return;
   // Staged entries -> the rows' append lists: per-row counts in LDS, one
   // global atomic per row reserves their places.  A flush is split so that
   // the atomics' round trip overlaps the next item's loads: flush_start (the
@@ -520,133 +645,45 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     wave_lds_sync();
     pcnt = 0;
   };
-  // the first entry is in before the loop, so at the top of an item only
-  // the previous item's atomics can be outstanding
-  __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0) only
-  for (int it = ch * kPfNW + w; it < items; it += stride) {
-    int c, i;
-    item_of(it, &c, &i);
-    const int2 ecur = enext;
-    {
-      int cn, in;
-      item_of(it + stride < items ? it + stride : it, &cn, &in);
-      enext = entry_of(cn, in);
-    }
-    // this lane's row (lanes l and l + 32 share row l % 32); a lane past the
-    // end of the leaf's rows has no row: nothing reaches its threshold and
-    // it writes nothing
-    const int row = i * 32 + l32 < (int)lcn[c] ? ecur.x : -1;
-    const int slot = ecur.y;
+  int c, i;
+  item_of(it, &c, &i);
+  int ecur = row_entry(c, i);
+  u32x4 PK[PL];
+  int jr;
+  load_tile(o0s[c], o1s[c], 0, PK, &jr);
+  for (;;) {
     const int o0 = o0s[c], o1 = o1s[c];
-    // key tile kt: A operand (key l32's dims) and the key's index (INT_MAX
-    // for a missing key or one inside the sink)
-    // A key tile is loaded coalesced (eight lanes per 128-byte key row; a
-    // lane past the leaf reads its last key, masked by position below),
-    // written to the wave's LDS tile with the 16-byte parts of row r
-    // XOR-swizzled by r % 8, and read back as the MFMA operand (lane l32
-    // takes key l32's parts) with no bank conflicts.  The wave's LDS
-    // accesses execute in order, so one tile buffer serves every tile.
-    unsigned char* kl = ktile[w];
-    auto load_parts = [&](int kt, u32x4* P) {
-#pragma unroll
-      for (int q = 0; q < PL; ++q) {
-        const int c = lane + 64 * q;
-        const int krow = max(0, min(o0 + 32 * kt + c / RP, o1 - 1));   // in range for an empty leaf too
-        P[q] = *(const u32x4*)(latb + (size_t)krow * DL + (c % RP) * 8);
-      }
-    };
-    auto put_parts = [&](const u32x4* P) {
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int q = 0; q < PL; ++q) {
-        const int c = lane + 64 * q, r = c / RP, pt = c % RP;
-        *(u32x4*)(kl + r * RP * 16 + ((pt ^ (r & 7)) % RP) * 16) = P[q];
-      }
-      __builtin_amdgcn_wave_barrier();
-    };
-    auto get_a = [&](v8s* A) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int pt = 2 * s + half;
-        A[s] = as_v8s(*(const uint4*)(kl + l32 * RP * 16 + ((pt ^ (l32 & 7)) % RP) * 16));
-      }
-    };
-    // key l32's position, raw (read early) and as a candidate test value:
-    // INT_MAX for a missing key or one inside the sink
-    auto pos_raw = [&](int kt) { return permb[max(0, min(o0 + 32 * kt + l32, o1 - 1))]; };
-    auto pos_of = [&](int kt, int jraw) { return (o0 + 32 * kt + l32 < o1 && jraw >= sink) ? jraw : INT_MAX; };
-    // The first key tile depends only on the leaf's range and the row data
-    // only on the entry: every load below is unconditional (a lane with no
-    // row reads row 0's data and drops it), so they all share one round
-    // trip.
-    u32x4 PK[PL];
-    load_parts(0, PK);
-    int jr = pos_raw(0);
+    const int nkt = max(1, (o1 - o0 + 31) / 32);
+    // the next item (this one again past the last)
+    const int itn = it + stride < items ? it + stride : it;
+    int cn, in;
+    item_of(itn, &cn, &in);
+    // this lane's row (lanes l and l + 32 share row l % 32); a lane past
+    // the end of the leaf's rows has no row: nothing reaches its threshold
+    // and it writes nothing
+    const int row = i * 32 + l32 < (int)lcn[c] ? ecur : -1;
     const int rq = row >= 0 ? row : 0;
     const int pq = a.s.q_pos[rq / a.s.Hq];
-    const float tq = SAMPLE ? 0.f : a.tauf[rq];
-    // the rows' latents (the B operand, a missing row as zeros).  The sample
-    // pass scores one key tile per item, so its row load matters as much as
-    // the key load: it comes coalesced through the LDS tile as well.  The
-    // main pass loads it straight, once per item.
+    const float tq = a.tauf[rq];
+    u32x4 Bu[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) Bu[s] = *(const u32x4*)(a.qlat16 + (size_t)rq * DL + 16 * s + 8 * half);
+    const int enx = row_entry(cn, in);
+    // every tile reads the row data: they are awaited here, once
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(Bu[s]));
+    asm volatile("" ::"v"(pq), "v"(tq));
     v8s Bq[KS];
-    if constexpr (SAMPLE) {
-      u32x4 P[PL];
 #pragma unroll
-      for (int q = 0; q < PL; ++q) {
-        const int cq = lane + 64 * q;
-        const int rr = __shfl(row, cq / RP, 64);
-        P[q] = *(const u32x4*)(a.qlat16 + (size_t)(rr >= 0 ? rr : 0) * DL + (cq % RP) * 8);
-        if (rr < 0) P[q] = u32x4{0u, 0u, 0u, 0u};
-      }
-      put_parts(P);
-      get_a(Bq);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 u = *(const uint4*)(a.qlat16 + (size_t)rq * DL + 16 * s + 8 * half);
-        if (row < 0) u = make_uint4(0u, 0u, 0u, 0u);
-        Bq[s] = as_v8s(u);
-      }
-    }
+    for (int s = 0; s < KS; ++s) Bq[s] = row >= 0 ? __builtin_bit_cast(v8s, Bu[s]) : v8s{0, 0, 0, 0, 0, 0, 0, 0};
     const int chi = (row >= 0 && pq >= 0 && (int64_t)pq < a.s.N) ? pq - a.s.window : -1;
-    const float tau = (row >= 0 && !SAMPLE) ? tq : __builtin_huge_valf();
-    // results: lane holds row l32 against keys m = 8(r/4) + 4 half + r%4
-    if (SAMPLE) {
-      if (o1 <= o0) continue;
-      put_parts(PK);
-      v8s A[KS];
-      get_a(A);
-      v16f acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
-      const int jl = pos_of(0, jr);
-      // registers 4g..4g+3 hold samples m0..m0+3 (m0 = 8g + 4 half): one
-      // 8-byte store per group, zero past spl or for a non-candidate
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int m0 = 8 * g + 4 * half;
-        u64 pk = 0ull;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int jm = __shfl(jl, m0 + c, 64);
-          const u64 v = (m0 + c < a.spl && jm <= chi) ? (u64)(order_u32(acc[4 * g + c]) >> 16) : 0ull;
-          pk |= v << (16 * c);
-        }
-        if (m0 < a.spl && row >= 0) *(u64*)(a.smp + ((size_t)row * a.nl + slot) * a.spl4 + m0) = pk;
-      }
-      continue;
-    }
-    const int nkt = (o1 - o0 + 31) / 32;
+    const float tau = row >= 0 ? tq : __builtin_huge_valf();
     // the smallest causal limit of the item's rows: a tile whose keys all
     // lie in [sink, that limit] needs no per-key range test
     int chimin = row >= 0 ? chi : INT_MAX;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) chimin = min(chimin, __shfl_xor(chimin, o, 64));
-    // the previous item's appends, now that this item's loads are in flight;
-    // then this item's rows take the row slots
+    // the previous item's appends; then this item's rows take the row slots
     if (pcnt > 0) flush_finish();
     if (half == 0) srow[w][l32] = row;
     int cnt = 0;                                   // staged entries (wave-uniform)
@@ -655,13 +692,18 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       flush_finish();
       cnt = 0;
     };
-    int jrn = 0;
+    // key l32's position as a candidate test value: INT_MAX for a missing
+    // key or one inside the sink
+    auto pos_of = [&](int kt, int jraw) { return (o0 + 32 * kt + l32 < o1 && jraw >= sink) ? jraw : INT_MAX; };
+    const int o0n = o0s[cn], o1n = o1s[cn];
     for (int kt = 0; kt < nkt; ++kt) {
       put_parts(PK);
-      if (kt + 1 < nkt) {
-        load_parts(kt + 1, PK);
-        jrn = pos_raw(kt + 1);
-      }
+      // key l32's position, taken before the next tile's loads reuse its
+      // register (a copy of a register with a load in flight would wait for it)
+      const int jl = pos_of(kt, jr);
+      // the next tile: this item's, or after its last the next item's first
+      const bool more = kt + 1 < nkt;
+      load_tile(more ? o0 : o0n, more ? o1 : o1n, more ? kt + 1 : 0, PK, &jr);
       v8s A[KS];
       get_a(A);
       v16f acc;
@@ -669,8 +711,7 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], acc, 0, 0, 0);
-      const int jl = pos_of(kt, jr);
-      jr = jrn;
+      // results: lane holds row l32 against keys m = 8(r/4) + 4 half + r%4
       int js[16];
       auto positions = [&]() {
 #pragma unroll
@@ -715,14 +756,17 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
         }
       }
     }
-    // Everything this item issued (the next item's entry among it) is
-    // complete before the atomics go out: the next item's loads then wait
-    // for nothing, and the atomics' results, awaited in order behind no
-    // other access, stay in flight under those loads.
-    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0) only
+    // the atomics go out behind the next item's entry and first key tile
+    // and are awaited together with that item's row data
     if (cnt > 0) flush_start(cnt, row);             // finished in the next item
+    if (itn == it) break;
+    it = itn;
+    c = cn;
+    i = in;
+    ecur = enx;
   }
   if (pcnt > 0) flush_finish();
+  }
 }
 
 // ---------------------------------------------------------------------------
