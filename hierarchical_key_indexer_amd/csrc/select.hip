@@ -4,10 +4,18 @@
 // Steps 2 and 3 of "How does LSA work?" (page "Latent Sparse Attention (LSA):
 // The 72.4x and 22.7x Speedups, and What They Compare Against"): the query is
 // compared with bucket centroids, only the winning buckets' keys are scored,
-// and its row lists those keys with the sink positions and the recent window.  The full scan is the dashed, quadratic path of the flowchart on
-// "Latent Sparse Attention: tree search over keys for 10M-token context".
+// and its row lists those keys with the sink positions and the recent window.
+// The full scan is the dashed, quadratic path of the flowchart on "Latent
+// Sparse Attention: tree search over keys for 10M-token context".
 //
-//   descend_kernel   one workgroup per query head: the query's latent
+//   descend_split_kernel  decode shapes (per-parent beam, fanouts <= 64, at
+//                    most 16 kept level-1 nodes): one workgroup per (kept
+//                    level-1 node, query head) descends that subtree, writes
+//                    its leaves into fixed slots and scores 64 samples
+//   gather_split_kernel   the gather over those slots: candidates numbered in
+//                    slot order, the threshold a weighted quantile of the
+//                    subtrees' samples, then as gather_kernel
+//   descend_kernel   other shapes, one workgroup per query head: the query's latent
 //                    (round(q.W_h)), then level by level the children of every
 //                    kept node are scored (one lane per child) and ranked
 //                    within the wave (readlane compares); leaf list with CSR
@@ -675,15 +683,6 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   a.smp[(qh * a.G1 + g) * kSplitSamples + lane] = key;
 }
 
-// The gather of the split descent.  Its first loads take the query head's
-// leaf slots, the subtrees' samples and the query latent together; the slots
-// are compacted in LDS (row starts, prefix counts, leaf ids) and the
-// threshold is the weighted sample quantile with about 2k candidates expected
-// above it (a sample of subtree g stands for n_g / min(n_g, kSplitSamples)
-// candidates; every workgroup of the query head computes the same value).
-// The candidates are split over S workgroups as in gather_kernel (with S > 1
-// merge_kernel takes the appended lists; workgroup 0 leaves it the compacted
-// leaf list and the threshold, for its exact re-score).
 // LDS scratch of block_weighted_threshold.
 struct ThrScratch {
   uint32_t hist[4][256];       // per-wave weighted histograms
