@@ -237,7 +237,9 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
   const int64_t wlo = lo + w * wlen, whi = min(hi, wlo + wlen);
   QSlice<LT> qv;
   qv.load((qsrc ? qsrc : a.qlat + qh * DL) + lig * E);   // qsrc: the latent already in LDS
-  // first leaf of this wave's range (largest i with lpre[i] <= wlo)
+  // first leaf of this wave's range (largest i with lpre[i] <= wlo); the
+  // current leaf's candidate range [cb, nb) and first row stay in registers,
+  // so LDS is read only when a candidate crosses into a later leaf
   int cur = 0;
   {
     int lo_i = 0, hi_i = nl;
@@ -247,6 +249,7 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
     }
     cur = lo_i;
   }
+  int cb = lpre[cur], nb = lpre[cur + 1], crow = lrow[cur];
   const LT* latb = (const LT*)a.lat + (size_t)h * a.N * DL;
   const int* permb = a.perm + (size_t)h * a.N;
   const int64_t rounds = (wlen + KPW * U - 1) / (KPW * U);
@@ -260,8 +263,13 @@ __device__ int gather_stream(const SelArgs& a, int64_t qh, int h, int clo, int c
       vv[u] = make_uint4(0u, 0u, 0u, 0u);
       ii[u] = -1;
       if (o < whi) {
-        while (lpre[cur + 1] <= o) ++cur;
-        const int64_t row = lrow[cur] + (o - lpre[cur]);
+        while (nb <= o) {
+          ++cur;
+          cb = nb;
+          nb = lpre[cur + 1];
+          crow = lrow[cur];
+        }
+        const int64_t row = crow + (o - cb);
         vv[u] = *(const uint4*)(latb + row * DL + lig * E);
         ii[u] = permb[row];
       }
