@@ -60,6 +60,28 @@ __device__ int compact_ids(const int* src, int ns, int* dst, int* wsum) {
   return total;
 }
 
+// compact_ids, moving the companion values ca[i], cb[i] of every kept entry
+// along with it (into da, db).  Block-wide.
+template <int BLOCK>
+__device__ int compact_ids_with(const int* src, const int* ca, const int* cb, int ns, int* dst, int* da, int* db,
+                                int* wsum) {
+  const int per = (ns + BLOCK - 1) / BLOCK;
+  const int i0 = min(ns, (int)threadIdx.x * per), i1 = min(ns, i0 + per);
+  int c = 0;
+  for (int i = i0; i < i1; ++i) c += src[i] >= 0;
+  int total;
+  int pos = block_exclusive_scan<BLOCK>(c, wsum, &total);
+  for (int i = i0; i < i1; ++i)
+    if (src[i] >= 0) {
+      dst[pos] = src[i];
+      da[pos] = ca[i];
+      db[pos] = cb[i];
+      ++pos;
+    }
+  __syncthreads();
+  return total;
+}
+
 // Mark the `need` largest of the unique nonzero keys the wave holds (J per
 // lane): bit-serial radix select with ballots, from the top bit down, until
 // the undecided keys are exactly the ones still needed.  in[j] gets the
@@ -193,8 +215,11 @@ struct ChildBlock {
   }
 
   // Wave-wide: the parent's best bs children (ties to the lower id) into
-  // out[0..bs) in child order, -1 padded.  q: the query latent (LDS).
-  __device__ __forceinline__ void pick(const float* q, int F, int bs, int64_t parent, int* out) const {
+  // out[0..bs) in child order, -1 padded, and (when orow is given) each
+  // kept child's first CSR row and row count into orow / ocnt at the same
+  // places.  q: the query latent (LDS).
+  __device__ __forceinline__ void pick(const float* q, int F, int bs, int64_t parent, int* out,
+                                       int* orow = nullptr, int* ocnt = nullptr) const {
     const int lane = threadIdx.x & 63, lig = lane % LPK;
     QSlice<LT> qv;
     qv.load(q + lig * E);
@@ -211,7 +236,14 @@ struct ChildBlock {
     const uint32_t key = (lane < F && o1 > o0) ? order_u32(sc) : 0u;
     u64 in[1];
     wave_select_top32<1>(&key, bs, in);
-    if ((in[0] >> lane) & 1ull) out[(int)mbcnt64(in[0])] = (int)(parent * F + lane);
+    if ((in[0] >> lane) & 1ull) {
+      const int pos = (int)mbcnt64(in[0]);
+      out[pos] = (int)(parent * F + lane);
+      if (orow) {
+        orow[pos] = o0;
+        ocnt[pos] = o1 - o0;
+      }
+    }
     for (int r = __popcll(in[0]) + lane; r < bs; r += 64) out[r] = -1;
   }
 };
@@ -223,7 +255,7 @@ struct ChildBlock {
 // Block-wide (no barrier inside).
 template <typename LT, int DL, int NW>
 __device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, const float* q, const int* fa, int nf,
-                                            int* fb) {
+                                            int* fb, int* orow = nullptr, int* ocnt = nullptr) {
   using CB = ChildBlock<LT, DL>;
   const int w = threadIdx.x >> 6;
   const int F = a.F[lev];
@@ -234,15 +266,17 @@ __device__ __forceinline__ void small_level(const SelArgs& a, int lev, int h, co
       CB x, y;
       x.load(a, lev, h, fa[i]);
       y.load(a, lev, h, fa[two ? i + NW : i]);
-      x.pick(q, F, bs, fa[i], fb + i * bs);
-      if (two) y.pick(q, F, bs, fa[i + NW], fb + (i + NW) * bs);
+      x.pick(q, F, bs, fa[i], fb + i * bs, orow ? orow + i * bs : nullptr, ocnt ? ocnt + i * bs : nullptr);
+      if (two)
+        y.pick(q, F, bs, fa[i + NW], fb + (i + NW) * bs, orow ? orow + (i + NW) * bs : nullptr,
+               ocnt ? ocnt + (i + NW) * bs : nullptr);
     }
   } else {
     // fp32 rows at d_l = 64: two parents' rows would not fit the registers
     for (int i = w; i < nf; i += NW) {
       CB x;
       x.load(a, lev, h, fa[i]);
-      x.pick(q, F, bs, fa[i], fb + i * bs);
+      x.pick(q, F, bs, fa[i], fb + i * bs, orow ? orow + i * bs : nullptr, ocnt ? ocnt + i * bs : nullptr);
     }
   }
 }
@@ -578,7 +612,12 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   const int nfb = max(sub, a.G1) + 1;       // the root's kept children, a level's slots, or the prefix
   int* fa = (int*)smem;                     // frontier: leaf ids at the end   [sub]
   int* fb = fa + sub;                       // next frontier slots; then the prefix of leaf sizes   [nfb]
-  int* lr = fb + nfb;                       // first CSR row of each leaf   [sub]
+  int* lr = fb + nfb;                       // first CSR row of each frontier node (leaf)   [sub]
+  int* ln = lr + sub;                       // its row count   [sub]
+  int* fr = ln + sub;                       // first CSR row of each next-frontier slot   [nfb]
+  int* fc = fr + nfb;                       // its row count   [nfb]
+  // (a child's CSR range comes with its centroid row, so the leaves' ranges
+  // need no loads of their own)
   const int64_t qh = a.qh0 + blockIdx.y;
   const int g = blockIdx.x;
   const int hq = (int)(qh % a.Hq), h = hq / a.G, t = (int)(qh / a.Hq);
@@ -592,23 +631,27 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   query_latent<KT, LT, DL>(a, qh, h, qin, q);
   if (g == 0 && threadIdx.x == 0 && a.part_n) a.part_n[qh] = 0u;   // the gather's lists (S > 1 only)
   // the root's kept children, ascending; this workgroup takes the g-th
-  if (w == 0) root.pick(q, a.F[0], min(a.b, a.F[0]), 0, fb);
+  if (w == 0) root.pick(q, a.F[0], min(a.b, a.F[0]), 0, fb, fr, fc);
   __syncthreads();
   const int my = fb[g];
+  const int myr = fr[g], myn = fc[g];
   __syncthreads();
   int nf = 0;
   if (my >= 0) {                            // block-uniform
-    if (threadIdx.x == 0) fa[0] = my;
+    if (threadIdx.x == 0) {
+      fa[0] = my;
+      lr[0] = myr;
+      ln[0] = myn;
+    }
     __syncthreads();
     nf = 1;
     for (int lev = 1; lev < a.L; ++lev) {
-      small_level<LT, DL, NW>(a, lev, h, q, fa, nf, fb);
+      small_level<LT, DL, NW>(a, lev, h, q, fa, nf, fb, fr, fc);
       __syncthreads();
-      nf = compact_ids<BLOCK>(fb, nf * min(a.b, a.F[lev]), fa, wsum);
+      nf = compact_ids_with<BLOCK>(fb, fr, fc, nf * min(a.b, a.F[lev]), fa, lr, ln, wsum);
     }
   }
   // the leaf slots and the exclusive prefix of the leaves' sizes
-  const int* offL = a.off[a.L - 1] + (size_t)h * (a.P[a.L - 1] + 1);
   int* srow = a.slot_row + qh * a.nl_cap + (int64_t)g * sub;
   int* sn = a.slot_n + qh * a.nl_cap + (int64_t)g * sub;
   int* sleaf = a.slot_leaf + qh * a.nl_cap + (int64_t)g * sub;
@@ -617,13 +660,10 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   int c = 0;
   for (int i = i0; i < i1; ++i) {
     if (i < nf) {
-      const int leaf = fa[i];
-      const int r0 = offL[leaf], r1 = offL[leaf + 1];
-      srow[i] = r0;
-      sn[i] = r1 - r0;
-      sleaf[i] = leaf;
-      lr[i] = r0;
-      c += r1 - r0;
+      srow[i] = lr[i];
+      sn[i] = ln[i];
+      sleaf[i] = fa[i];
+      c += ln[i];
     } else {
       // an empty slot repeats the workgroup's last leaf (none: past every
       // id), so the slots' leaf ids stay non-decreasing across workgroups
@@ -636,7 +676,7 @@ __global__ __launch_bounds__(kSplitBlock) void descend_split_kernel(SelArgs a) {
   int run = block_exclusive_scan<BLOCK>(c, wsum, &ng);
   for (int i = i0; i < min(i1, nf); ++i) {
     fb[i] = run;
-    run += offL[fa[i] + 1] - offL[fa[i]];
+    run += ln[i];
   }
   if (threadIdx.x == 0) {
     fb[nf] = ng;
@@ -1503,7 +1543,7 @@ int run_select(const lsa_index_desc& d, const lsa_select_params& p, const Select
     a.part_cap = (int64_t)a.S * p.k;
     const int sub = pl.nl_cap / pl.g1;
     auto dk = descend_split_kernel<KT, LT, DL>;
-    const size_t dlds = ((size_t)2 * sub + std::max(sub, pl.g1) + 1) * 4;
+    const size_t dlds = ((size_t)3 * sub + 3 * ((size_t)std::max(sub, pl.g1) + 1)) * 4;
     prof_begin(LSA_STAGE_DESCEND, st);
     for (int64_t q0 = 0; q0 < QH; q0 += chunk) {
       a.qh0 = q0;
