@@ -375,7 +375,7 @@ struct SortScratch {
 template <int BLOCK, int M>
 __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
                                 float* scores_row, RadixScratch* sc, SortScratch& ss,
-                                const u64* src = nullptr) {
+                                const u64* src = nullptr, const u64* pre = nullptr) {
   constexpr int NW = BLOCK / 64;
   constexpr int NB = kSortBuckets;
   static_assert(NB >= 256, "the second radix histogram lives in the bucket counts");
@@ -384,7 +384,7 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const int i = threadIdx.x + j * BLOCK;
-    v[j] = (i < n) ? (src ? src[i] : buf[i]) : 0ull;
+    v[j] = (i < n) ? (pre ? pre[j] : src ? src[i] : buf[i]) : 0ull;
     if (v[j] != 0ull) {
       lo = v[j] < lo ? v[j] : lo;
       hi = v[j] > hi ? v[j] : hi;
@@ -556,12 +556,15 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
   for (int i = threadIdx.x; i < window; i += BLOCK) row[sink + k + i] = i < nw ? w0 + i : -1;
 }
 
-// The same, with the sort scratch in a static LDS block of its own.
+// The same, with the sort scratch in a static LDS block of its own.  The
+// keys come from buf, from src, or (pre) from the M keys each thread already
+// holds, key threadIdx.x + j BLOCK in pre[j].
 template <int BLOCK, int M>
 __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
-                                float* scores_row, RadixScratch* sc, const u64* src = nullptr) {
+                                float* scores_row, RadixScratch* sc, const u64* src = nullptr,
+                                const u64* pre = nullptr) {
   __shared__ SortScratch ss;
-  write_top_k_row<BLOCK, M>(buf, n, k, cap, p, sink, window, row, scores_row, sc, ss, src);
+  write_top_k_row<BLOCK, M>(buf, n, k, cap, p, sink, window, row, scores_row, sc, ss, src, pre);
 }
 
 // A row for a query whose position is outside [0, N): all -1.

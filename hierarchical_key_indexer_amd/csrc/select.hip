@@ -1116,7 +1116,13 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   u64* buf = (u64*)smem;
   const int64_t qh = a.qh0 + blockIdx.x;
   const int t = (int)(qh / a.Hq);
-  // the three loads are independent: issue them together
+  // the list's first CAP places are loaded with its count (clamped into the
+  // query head's region of the workspace, masked by the count where used)
+  const u64* src = a.part_keys + qh * a.part_cap;
+  u64 pre[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) pre[j] = src[min((int64_t)threadIdx.x + (int64_t)j * BLOCK, a.part_cap - 1)];
+  // these loads are independent as well: issue them together
   const int n_in = (int)a.part_n[qh];
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   const int p = a.q_pos[t];
@@ -1165,11 +1171,10 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
                               a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs);
     return;
   }
-  const u64* src = a.part_keys + qh * a.part_cap;
   if (n_in <= CAP) {
-    // everything fits the registers: one coalesced load and one selection
+    // everything fits the registers, loaded above: one selection
     write_top_k_row<BLOCK, M>(buf, n_in, a.k, CAP, p, a.sink, a.window, a.out_idx + qh * a.width,
-                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs, src);
+                              a.out_scores ? a.out_scores + qh * a.k : nullptr, &rs, nullptr, pre);
     return;
   }
   u64 lowest = 0ull;                         // keys below this are never needed
@@ -1452,12 +1457,13 @@ void launch_merge(SelArgs a, int64_t QH, int64_t chunk, hipStream_t st) {
   }
 }
 
-// capacity >= k + four appends' room, and >= 2k so the final sort fits
+// capacity >= k + four appends' room, and >= 2k so the final sort fits:
+// 8 keys per thread cover every k up to kMaxK
+static_assert(kMaxK + 4 * kMergeBlock <= 8 * kMergeBlock && 2 * kMaxK <= 8 * kMergeBlock, "merge capacity");
 template <typename LT, int DL>
 void merge_all(const SelArgs& a, int k, int64_t QH, int64_t chunk, hipStream_t st) {
-  const int need = k + 4 * kMergeBlock > 2 * k ? k + 4 * kMergeBlock : 2 * k;
-  if (pick_m(need, kMergeBlock) <= 8) launch_merge<LT, DL, 8>(a, QH, chunk, st);
-  else launch_merge<LT, DL, 16>(a, QH, chunk, st);
+  (void)k;
+  launch_merge<LT, DL, 8>(a, QH, chunk, st);
 }
 
 template <typename KT, typename LT, int DL>
