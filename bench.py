@@ -249,12 +249,23 @@ def attention_leg(abi, desc, wl, qd, kd, idx, reps=20):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    listed = int(((idx >= 0) & (idx < desc.n_keys)).sum().item())
-    nbytes = listed * 2 * desc.d_head * (2 if wl.key_dtype == "bf16" else 4) + idx.numel() * 4
+    valid = (idx >= 0) & (idx < desc.n_keys)
+    listed = int(valid.sum().item())
+    elt = 2 if wl.key_dtype == "bf16" else 4
+    row_bytes = listed * 2 * desc.d_head * elt + idx.numel() * 4
+    # rows of one KV head share keys (GQA, neighbouring tokens): the distinct
+    # (KV head, key) pairs are what HBM has to deliver at least
+    kvh = (torch.arange(Hq, device=idx.device) // (Hq // desc.n_kv_heads)).view(1, Hq, 1).long()
+    uniq = int(torch.unique((kvh * desc.n_keys + idx.long())[valid]).numel())
+    unique_bytes = uniq * 2 * desc.d_head * elt + idx.numel() * 4
     del vals
     return {"ms_per_call": ms, "rows": T * Hq, "keys_per_row": listed / (T * Hq), "kernel": "sparse_attention_kernel",
-            "bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "bound": "hbm", "distinct_kv_rows": uniq, "bytes": unique_bytes,
+            "achieved_GBs": unique_bytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": unique_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "per_row_bytes": row_bytes,
+            "note": "bytes: each distinct (KV head, key) K and V row once plus the index rows; per_row_bytes "
+                    "counts every row's own reads, which rows sharing keys serve from the caches"}
 
 
 def recall_rows(tree_out, flat_out, sink, k):
