@@ -367,10 +367,10 @@ def decode_record(wl, li, keys, hip, args, pool_n, abi):
     gather_ms = cold[abi.STAGE_GATHER]
     roof = {"bound": "hbm", "achieved": cold_bytes / (gather_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(wl.name, "gather")
     # decode plans split the descent over the kept level-1 nodes when the
     # per-parent beam keeps at most 16 of them and no fanout exceeds 64
     split = wl.b <= 16 and max(wl.fanout) <= 64
+    roof["traffic"] = load_traffic(wl.name, "gather_split" if split else "gather")
     roof["kernel"] = "gather_split_kernel" if split else "gather_kernel"
     roof["algorithmic_bytes_per_launch"] = cold_bytes
     roof["kernel_ms"] = gather_ms
