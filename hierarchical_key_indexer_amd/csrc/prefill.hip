@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
     atomicAdd(&a.ccnt[(size_t)h * Pe + child0 + threadIdx.x], lcnt[threadIdx.x]);
 }
 
+template <int BMAX>
 __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   __shared__ uint32_t lcnt[kPfMaxF], lbase[kPfMaxF], lfill[kPfMaxF], cst[kPfMaxF];
   if (*a.s.status != LSA_OK) return;
@@ -356,27 +357,53 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
   if (threadIdx.x < F && lcnt[threadIdx.x] != 0u) lbase[threadIdx.x] = atomicAdd(&a.cfill[cbase + threadIdx.x], lcnt[threadIdx.x]);
   __syncthreads();
   const bool last = a.lev == a.s.L - 1;
+  const int be = a.be;                           // <= BMAX: at most be children are kept
   for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
     const int r_in = ti * 64 + lane;
     if (r_in < n) {
       const int64_t pos = start + r_in;
       const int2 e = pf_entry(a, pos, h);
       u64 m = a.mask[pos];
-      int j = 0;
-      int32_t* lfr = a.lf + (size_t)e.x * a.nl;
-      while (m != 0ull) {
-        const int c = __ffsll((long long)m) - 1;
+      // the kept children in ascending order; their places in the child
+      // lists are all reserved before any is used, so the LDS atomics go
+      // out back to back
+      int cs[BMAX];
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) {
+        cs[j] = m != 0ull ? __ffsll((long long)m) - 1 : -1;
         m &= m - 1ull;
-        const uint32_t slot = (uint32_t)e.y * a.be + j;
-        const uint32_t dst = cst[c] + lbase[c] + atomicAdd(&lfill[c], 1u);
-        a.Enext[dst] = make_int2(e.x, (int)slot);
-        if (last) lfr[slot] = (int32_t)(par * F + c);
-        ++j;
       }
-      // slots left empty (fewer than be non-empty children) and their subtrees
-      for (; j < a.be; ++j) {
-        const int64_t s0 = ((int64_t)e.y * a.be + j) * a.sub;
-        for (int64_t q = 0; q < a.sub; ++q) lfr[s0 + q] = -1;
+      uint32_t dst[BMAX];
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j) dst[j] = cs[j] >= 0 ? atomicAdd(&lfill[cs[j]], 1u) : 0u;
+      int nk = 0;
+#pragma unroll
+      for (int j = 0; j < BMAX; ++j)
+        if (cs[j] >= 0) {
+          const int c = cs[j];
+          a.Enext[cst[c] + lbase[c] + dst[j]] = make_int2(e.x, e.y * be + j);
+          ++nk;
+        }
+      int32_t* lfr = a.lf + (size_t)e.x * a.nl + (size_t)e.y * be * a.sub;
+      if (last) {
+        // the leaf of each of the entry's be slots (-1 for an empty one):
+        // consecutive, so whole 16-byte stores when be is a multiple of 4
+        int lv[BMAX];
+#pragma unroll
+        for (int j = 0; j < BMAX; ++j) lv[j] = cs[j] >= 0 ? (int)(par * F + cs[j]) : -1;
+        if ((be & 3) == 0) {
+#pragma unroll
+          for (int j = 0; j < BMAX; j += 4)
+            if (j < be) *(int4*)(lfr + j) = make_int4(lv[j], lv[j + 1], lv[j + 2], lv[j + 3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < BMAX; ++j)
+            if (j < be) lfr[j] = lv[j];
+        }
+      } else {
+        // slots left empty (fewer than be non-empty children) and their subtrees
+        for (int j = nk; j < be; ++j)
+          for (int64_t q = 0; q < a.sub; ++q) lfr[(int64_t)j * a.sub + q] = -1;
       }
     }
   }
@@ -1511,7 +1538,9 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     if (d.fanout[lev] <= 32) launch_count_b<DL, 1>(a, grid, a.be, st);
     else launch_count_b<DL, 2>(a, grid, a.be, st);
     PF_CHECK("level scoring");
-    hipLaunchKernelGGL(pf_level_scatter, dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    if (a.be <= 4) hipLaunchKernelGGL(pf_level_scatter<4>, dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    else if (a.be <= 8) hipLaunchKernelGGL(pf_level_scatter<8>, dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    else hipLaunchKernelGGL(pf_level_scatter<16>, dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("level lists");
   }
   prof_end(LSA_STAGE_DESCEND, st);
