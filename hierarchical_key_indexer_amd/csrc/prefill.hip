@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int DL, int NT, int BMAX>
-__global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
+__global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) void pf_level_count(PfArgs a) {
   constexpr int KS = DL / 16;                    // k-steps of 16 latent dims
   __shared__ uint32_t lcnt[kPfMaxF];
   if (*a.s.status != LSA_OK) return;
@@ -226,8 +226,12 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
     }
     // lane holds row l32 against children 32t + 8(i/4) + 4 half + i%4
     // the lane's BMAX best scores, descending: one v_med3 per entry and score
-    // (an empty child is -inf here and key 0 below)
-    uint32_t key[NT][16];
+    // (an empty child is -inf here and key 0 below; the keys are taken from
+    // the scores again where they are compared, so they hold no registers)
+    auto key_of = [&](int t, int i) {
+      const int c = 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
+      return ((ne_mask >> c) & 1ull) ? order_u32(acc[t][i]) : 0u;
+    };
     float tf[BMAX];
 #pragma unroll
     for (int j = 0; j < BMAX; ++j) tf[j] = -__builtin_huge_valf();
@@ -237,7 +241,6 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int c = 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
         const bool nec = (ne_mask >> c) & 1ull;
-        key[t][i] = nec ? order_u32(acc[t][i]) : 0u;
         const float v = nec ? acc[t][i] : -__builtin_huge_valf();
 #pragma unroll
         for (int j = BMAX - 1; j > 0; --j) tf[j] = __builtin_amdgcn_fmed3f(tf[j - 1], tf[j], v);
@@ -272,8 +275,9 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_count(PfArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const u64 bit = 1ull << (32 * t + 8 * (i >> 2) + 4 * half + (i & 3));
-        gt |= key[t][i] > theta ? bit : 0ull;
-        eq |= key[t][i] == theta ? bit : 0ull;
+        const uint32_t kv = key_of(t, i);
+        gt |= kv > theta ? bit : 0ull;
+        eq |= kv == theta ? bit : 0ull;
       }
     gt |= shfl_xor_u64(gt, 32);
     eq |= shfl_xor_u64(eq, 32);
