@@ -809,7 +809,10 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
 // 16-bit sample value whose weight at or above it reaches 1.5k, found with two
 // 8-bit histogram passes.  A row whose leaves hold at most `cap` keys in all
 // takes every candidate (no threshold).
-template <int kTauCL>
+// NG > 0: the row's slots fit one chunk (nl <= 64 kTauCL) and its samples
+// NG groups of four (spl <= 4 NG); slots, leaf sizes and samples are then
+// loaded once and kept in registers for both histogram passes.
+template <int kTauCL, int NG>
 __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   __shared__ u64 hist[kPfNW][256];
   if (*a.s.status != LSA_OK) return;
@@ -840,6 +843,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
     for (int j = 0; j < kTauCL; ++j) sz[j] = leaf[j] >= 0 ? offL[leaf[j] + 1] - offL[leaf[j]] : 0;
   };
   int64_t tot = 0, tots = 0;                       // candidates of all / of the sampled leaves
+  int cleaf[kTauCL], csz[kTauCL];                  // NG > 0: the row's only chunk
   for (int base = 0; base < a.nl; base += 64 * kTauCL) {
     int leaf[kTauCL], sz[kTauCL];
     chunk(base, leaf, sz);
@@ -847,7 +851,23 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
     for (int j = 0; j < kTauCL; ++j) {
       tot += sz[j];
       if (leaf[j] >= 0 && sampled(leaf[j])) tots += sz[j];
+      if (NG > 0) {
+        cleaf[j] = leaf[j];
+        csz[j] = sz[j];
+      }
     }
+  }
+  // NG > 0: the samples, loaded once (as in the passes below)
+  u64 cs4[NG > 0 ? NG : 1][kTauCL];
+  if constexpr (NG > 0) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int j = 0; j < kTauCL; ++j) {
+        const int g = 4 * gi, sl = lane + 64 * j;
+        const bool use = cleaf[j] >= 0 && sampled(cleaf[j]) && g < min(csz[j], a.spl);
+        cs4[gi][j] = use ? *(const u64*)(sm + (size_t)sl * a.spl4 + g) : 0ull;
+      }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -861,7 +881,30 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
   for (int pass = 0; pass < 2; ++pass) {
     for (int b = lane; b < 256; b += 64) hist[w][b] = 0ull;
     __syncthreads();
-    if (want && (pass == 0 || d1 >= 0))
+    // one sample group: its samples' weights into the wave's histogram
+    auto add_group = [&](int g, const int* leaf, const int* sz, const u64* s4) {
+#pragma unroll
+      for (int j = 0; j < kTauCL; ++j) {
+        if (s4[j] == 0ull) continue;
+        const int se = sz[j] < a.spl ? sz[j] : a.spl;
+        // a sample stands for its share of the leaf, scaled up by the
+        // candidates of the leaves that were not sampled
+        const u64 wt = (u64)((double)sz[j] * 16.0 * (double)tot / ((double)se * (double)tots));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t v = (uint32_t)(s4[j] >> (16 * c)) & 0xFFFFu;
+          if (v == 0u || g + c >= se) continue;
+          if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
+          else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
+        }
+      }
+    };
+    if (NG > 0 && want && (pass == 0 || d1 >= 0)) {
+#pragma unroll
+      for (int gi = 0; gi < (NG > 0 ? NG : 1); ++gi)
+        if (4 * gi < a.spl) add_group(4 * gi, cleaf, csz, cs4[gi]);
+    }
+    if (NG == 0 && want && (pass == 0 || d1 >= 0))
       for (int base = 0; base < a.nl; base += 64 * kTauCL) {
         int leaf[kTauCL], sz[kTauCL];
         chunk(base, leaf, sz);
@@ -874,21 +917,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
             const bool use = leaf[j] >= 0 && sampled(leaf[j]) && g < min(sz[j], a.spl);
             s4[j] = use ? *(const u64*)(sm + (size_t)sl * a.spl4 + g) : 0ull;
           }
-#pragma unroll
-          for (int j = 0; j < kTauCL; ++j) {
-            if (s4[j] == 0ull) continue;
-            const int se = sz[j] < a.spl ? sz[j] : a.spl;
-            // a sample stands for its share of the leaf, scaled up by the
-            // candidates of the leaves that were not sampled
-            const u64 wt = (u64)((double)sz[j] * 16.0 * (double)tot / ((double)se * (double)tots));
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t v = (uint32_t)(s4[j] >> (16 * c)) & 0xFFFFu;
-              if (v == 0u || g + c >= se) continue;
-              if (pass == 0) atomicAdd(&hist[w][v >> 8], wt);
-              else if ((int)(v >> 8) == d1) atomicAdd(&hist[w][v & 0xFFu], wt);
-            }
-          }
+          add_group(g, leaf, sz, s4);
         }
       }
     __syncthreads();
@@ -1561,8 +1590,15 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     prof_begin(LSA_STAGE_SAMPLE, st);
     hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("sample pass");
-    if (a.nl >= 512) hipLaunchKernelGGL(pf_tau_kernel<8>, dim3(rgrid), dim3(kPfBlock), 0, st, a);
-    else hipLaunchKernelGGL(pf_tau_kernel<4>, dim3(rgrid), dim3(kPfBlock), 0, st, a);
+    // rows whose slots fit one chunk and whose samples fit the registers
+    // keep them there for both histogram passes
+    if (a.nl >= 512) {
+      if (a.nl <= 64 * 8 && a.spl <= 4) hipLaunchKernelGGL((pf_tau_kernel<8, 1>), dim3(rgrid), dim3(kPfBlock), 0, st, a);
+      else hipLaunchKernelGGL((pf_tau_kernel<8, 0>), dim3(rgrid), dim3(kPfBlock), 0, st, a);
+    } else {
+      // (three groups of samples kept in registers would cost half the waves)
+      hipLaunchKernelGGL((pf_tau_kernel<4, 0>), dim3(rgrid), dim3(kPfBlock), 0, st, a);
+    }
     PF_CHECK("thresholds");
     prof_end(LSA_STAGE_SAMPLE, st);
     prof_begin(LSA_STAGE_GATHER, st);
