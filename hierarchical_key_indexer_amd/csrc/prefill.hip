@@ -20,13 +20,13 @@
 //   pf_level_scatter    the rows of every kept child are written to the
 //                       child's list (the next level's groups); at the last
 //                       level also the per-row leaf slots
-//   pf_gather           leaf-major scoring: one item is (leaf, 32 rows), 32
-//                       keys of the leaf are the A operand of a 32x32x16 bf16
-//                       MFMA, the rows' latents the B operand.  Sample mode
-//                       keeps the first s scores of every (row, leaf); main
-//                       mode counts each row's keys at or above its threshold,
-//                       reserves their places with one atomic per row and
-//                       writes them
+//   pf_sample, pf_gather  leaf-major scoring: one item is (leaf, 32 rows),
+//                       32 keys of the leaf are the A operand of a 32x32x16
+//                       bf16 MFMA, the rows' latents the B operand.  The
+//                       sample pass keeps the first s scores of every (row,
+//                       leaf); the main pass counts each row's keys at or
+//                       above its threshold, reserves their places with one
+//                       atomic per row and writes them
 //   pf_tau_kernel       per row, a threshold from the weighted samples such
 //                       that about 1.5k candidates are expected above it
 //   pf_merge_kernel     per row, the exact best k of the appended keys and the
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kPfBlock) void pf_level_scatter(PfArgs a) {
 // lists.  Sample mode scores the first key tile and keeps the first spl
 // scores of every row.
 template <int DL, bool SAMPLE>
-__global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) void pf_gather(PfArgs a) {
+__device__ __forceinline__ void pf_gather_body(PfArgs a) {
   constexpr int KS = DL / 16;
   constexpr int RP = DL * 2 / 16;                  // 16-byte parts per key row
   constexpr int PL = 32 * RP / 64;                 // 16-byte parts per lane and 32-key tile
@@ -798,6 +798,19 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   if (pcnt > 0) flush_finish();
   }
+}
+
+// The two passes as kernels of their own: the sample pass holds few
+// registers and runs six waves per SIMD; the main pass holds its row data,
+// a prefetched key tile and the staging bookkeeping, and runs three.
+template <int DL>
+__global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(6))) void pf_sample(PfArgs a) {
+  pf_gather_body<DL, true>(a);
+}
+
+template <int DL>
+__global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) void pf_gather(PfArgs a) {
+  pf_gather_body<DL, false>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1588,7 +1601,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     const int64_t grid = (int64_t)d.n_kv_heads * L.nodes[lev] * a.CH;
     const unsigned rgrid = (unsigned)((R + kPfNW - 1) / kPfNW);
     prof_begin(LSA_STAGE_SAMPLE, st);
-    hipLaunchKernelGGL((pf_gather<DL, true>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    hipLaunchKernelGGL((pf_sample<DL>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("sample pass");
     // rows whose slots fit one chunk and whose samples fit the registers
     // keep them there for both histogram passes
@@ -1602,7 +1615,7 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
     PF_CHECK("thresholds");
     prof_end(LSA_STAGE_SAMPLE, st);
     prof_begin(LSA_STAGE_GATHER, st);
-    hipLaunchKernelGGL((pf_gather<DL, false>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
+    hipLaunchKernelGGL((pf_gather<DL>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
     PF_CHECK("gather");
     prof_end(LSA_STAGE_GATHER, st);
   }
