@@ -609,7 +609,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the indexer shards by KV head "
-              f"with no exchange, and multi-GPU runs are not part of this build.", flush=True)
+              f"with no exchange, and this benchmark runs on one GPU.", flush=True)
         sys.exit(2)
 
     import torch
