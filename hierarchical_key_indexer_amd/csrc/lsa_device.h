@@ -371,9 +371,13 @@ struct SortScratch {
 // row.  A bucket of more than 64 keys (a very uneven index spread) sends the
 // kept set to the bitonic sort instead.  buf[0..cap) is scratch (cap >= n,
 // cap >= 2k, a power of two).  The caller's writes to buf must be visible (a barrier before the
-// call); all threads of the block call.
-template <int BLOCK, int M>
-__device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
+// call); all threads of the block call.  DIRECT: the keys are put in order
+// in buf itself once every key knows its place, so buf needs only k + 4
+// entries (cap is not used); a bucket of more than 64 keys then writes
+// nothing of the row and returns false (block-uniform) for the caller to
+// take the row another way.  Returns true once the row is written.
+template <int BLOCK, int M, bool DIRECT = false>
+__device__ bool write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink, int window, int32_t* row,
                                 float* scores_row, RadixScratch* sc, SortScratch& ss,
                                 const u64* src = nullptr, const u64* pre = nullptr) {
   constexpr int NW = BLOCK / 64;
@@ -476,14 +480,13 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
   for (int b = threadIdx.x; b < NB; b += BLOCK) ss.cnt[b] = 0u;
   if (threadIdx.x == 0) ss.big = 0;
   __syncthreads();
-  bool keep[M];
+  // a dropped key becomes 0 (a re-keyed key never is: its low word is an
+  // order image, > 0x007FFFFF), so v[j] != 0 marks the kept keys from here on
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    keep[j] = v[j] != 0ull && (v[j] & mask) >= prefix;
-    if (keep[j]) {
-      v[j] = ((u64)(uint32_t)rank_key_index(v[j]) << 32) | (v[j] >> 32);
-      atomicAdd(&ss.cnt[bucket(v[j])], 1u);
-    }
+    const bool keep = v[j] != 0ull && (v[j] & mask) >= prefix;
+    v[j] = keep ? (((u64)(uint32_t)rank_key_index(v[j]) << 32) | (v[j] >> 32)) : 0ull;
+    if (keep) atomicAdd(&ss.cnt[bucket(v[j])], 1u);
   }
   __syncthreads();
   constexpr int PER = NB / BLOCK > 0 ? NB / BLOCK : 1;
@@ -496,7 +499,8 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
     }
   if (mx > 64) ss.big = 1;
   int nk;
-  int run = block_exclusive_scan<BLOCK>(mine, ss.wsum, &nk);
+  int run = block_exclusive_scan<BLOCK>(mine, ss.wsum, &nk);   // (its barriers publish big)
+  if (DIRECT && ss.big) return false;
   if ((int)threadIdx.x * PER < NB)
     for (int j = 0; j < PER; ++j) {
       const int c = (int)ss.cnt[threadIdx.x * PER + j];
@@ -507,8 +511,47 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
   // buf is free: every key is in registers
 #pragma unroll
   for (int j = 0; j < M; ++j)
-    if (keep[j]) buf[atomicAdd(&ss.cnt[bucket(v[j])], 1u)] = v[j];
+    if (v[j] != 0ull) buf[atomicAdd(&ss.cnt[bucket(v[j])], 1u)] = v[j];
   __syncthreads();
+  if constexpr (DIRECT) {
+    // a key's place is its bucket's start plus the smaller keys in it (as
+    // below; entries past the bucket's end are masked, buf holds k + 4);
+    // once every place is known, the keys are put in order in buf itself and
+    // the row is written from there with coalesced stores
+    const uint32_t* hw = (const uint32_t*)buf + 1;
+    int rr[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      rr[j] = -1;
+      if (v[j] != 0ull) {
+        const int b = bucket(v[j]);
+        const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
+        const uint32_t xi = (uint32_t)(v[j] >> 32);
+        int r = st;
+        for (int i = st; i < e; i += 4) {
+          const uint32_t y0 = hw[2 * i], y1 = hw[2 * i + 2], y2 = hw[2 * i + 4], y3 = hw[2 * i + 6];
+          r += (y0 < xi ? 1 : 0) + (i + 1 < e && y1 < xi ? 1 : 0) + (i + 2 < e && y2 < xi ? 1 : 0) +
+               (i + 3 < e && y3 < xi ? 1 : 0);
+        }
+        rr[j] = r;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (rr[j] >= 0) buf[rr[j]] = v[j];
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += BLOCK) {
+      if (i < nk) {
+        const u64 key = buf[i];
+        row[sink + i] = (int32_t)(key >> 32);
+        if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
+      } else {
+        row[sink + i] = -1;
+        if (scores_row) scores_row[i] = -__builtin_huge_valf();
+      }
+    }
+  } else {
   const u64* sorted = buf;
   if (ss.big) {
     bitonic_sort_asc<BLOCK>(buf, nk, cap);
@@ -520,7 +563,7 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
     u64* out = buf + cap / 2;
 #pragma unroll
     for (int j = 0; j < M; ++j)
-      if (keep[j]) {
+      if (v[j] != 0ull) {
         const int b = bucket(v[j]);
         const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
         // indices are unique, so the high words alone order the keys; four
@@ -549,11 +592,13 @@ __device__ void write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
       if (scores_row) scores_row[i] = -__builtin_huge_valf();
     }
   }
+  }
   const int ns = min(sink, p + 1);
   for (int i = threadIdx.x; i < sink; i += BLOCK) row[i] = i < ns ? i : -1;
   const int w0 = max(sink, p - window + 1);
   const int nw = p - w0 + 1;
   for (int i = threadIdx.x; i < window; i += BLOCK) row[sink + k + i] = i < nw ? w0 + i : -1;
+  return true;
 }
 
 // The same, with the sort scratch in a static LDS block of its own.  The

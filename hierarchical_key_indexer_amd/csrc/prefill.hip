@@ -50,6 +50,7 @@ namespace {
 constexpr int kPfBlock = 256;        // level and gather workgroups: 4 waves
 constexpr int kPfNW = kPfBlock / 64;
 constexpr int kPfMergeBlock = 256;
+constexpr int kPfMergeFbGrid = 1024; // workgroups of the block merge over the rows the usual-row merge left
 constexpr int kPfMinRows = 256;      // query heads per KV head for this path
 constexpr int kPfMaxB = 16;
 constexpr int kPfMaxF = 64;
@@ -85,6 +86,8 @@ struct PfArgs {
   uint16_t* smp;               // [R][nl][spl4] top 16 bits of order(score), 0 = not a candidate
   float* tauf;                 // [R] score threshold, -inf = none
   int64_t cap;                 // append capacity per row
+  uint32_t* fb_rows;           // [R] rows the usual-row merge leaves to the block merge
+  uint32_t* fb_n;              // their count (cleared by the query projection)
   // row-tiled full scan
   bool flat;                   // every key in [sink, p - window] is a candidate of every row
   int64_t ns;                  // sampled keys per KV head
@@ -157,6 +160,7 @@ __global__ __launch_bounds__(256) void pf_qproj_kernel(PfArgs a) {
   __shared__ float q[DL];
   const int64_t row = blockIdx.x;
   const int h = (int)(row % a.s.Hq) / a.s.G;
+  if (row == 0 && threadIdx.x == 0) *a.fb_n = 0u;
   if (!check_index_first(a.s)) return;       // nothing past the header is read
   query_latent<KT, bf16_t, DL>(a.s, row, h, qin, q);
   if (threadIdx.x < DL) a.qlat16[row * DL + threadIdx.x] = (uint16_t)(__float_as_uint(q[threadIdx.x]) >> 16);
@@ -947,19 +951,19 @@ __global__ __launch_bounds__(kPfBlock) void pf_tau_kernel(PfArgs a) {
 // per-row exact top-k and output
 // ---------------------------------------------------------------------------
 
+// One row by the whole workgroup, any case: the rows pf_merge_fast below
+// leaves (a re-score, more appended keys than it holds, an uneven index
+// spread).
 template <int DL, int M>
-__global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
-  constexpr int BLOCK = kPfMergeBlock, CAP = M * BLOCK, NW = BLOCK / 64;
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ RadixScratch rs;
-  __shared__ int n_sh, wsum[NW];
+__device__ __forceinline__ void pf_merge_row(const PfArgs& a, int64_t row, unsigned char* smem, RadixScratch& rs,
+                                             int& n_sh, int* wsum) {
+  constexpr int BLOCK = kPfMergeBlock, CAP = M * BLOCK;
   u64* buf = (u64*)smem;
   // one LDS block serves the leaf lists of a re-score (used while streaming
   // candidates) and then the index sort's scratch (used only afterwards)
   int* lpre = (int*)(buf + CAP);
   int* lrow = lpre + a.nl + 1;
   SortScratch& sort_ss = *(SortScratch*)(buf + CAP);
-  const int64_t row = blockIdx.x;
   const int t = (int)(row / a.s.Hq), h = (int)(row % a.s.Hq) / a.s.G;
   const int p = a.s.q_pos[t];
   if (*a.s.status != LSA_OK) {
@@ -1067,6 +1071,87 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   }
   __syncthreads();                                 // the lists are dead; the block becomes sort scratch
   write_top_k_row<BLOCK, M>(buf, n, k, CAP, p, a.s.sink, a.s.window, orow, srow, &rs, sort_ss);
+}
+
+template <int DL, int M>
+__global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ RadixScratch rs;
+  __shared__ int n_sh, wsum[kPfMergeBlock / 64];
+  const uint32_t nfb = min(*a.fb_n, (uint32_t)a.R);
+  for (uint32_t i = blockIdx.x; i < nfb; i += gridDim.x) {
+    __syncthreads();                               // the last row's LDS reads are done
+    pf_merge_row<DL, M>(a, (int64_t)a.fb_rows[i], smem, rs, n_sh, wsum);
+  }
+}
+
+
+// The usual row: its appended keys fit the registers (M per thread) and need
+// no re-score.  Same result as pf_merge_row with less than half of its LDS
+// and registers: the keys go from the list into registers, the selection
+// runs on them there, and only the k kept keys pass through LDS (bucketed by
+// index, then put in order in the same place), so seven rows fit a CU at
+// once instead of three.  A row it does not take (a
+// re-score, more keys than it holds, a bucket of more than 64 keys) goes to
+// the block merge's list before anything of its top-k part is written.
+template <int M>
+__global__ __launch_bounds__(kPfMergeBlock) void pf_merge_fast(PfArgs a) {
+  constexpr int BLOCK = kPfMergeBlock, CAP = M * BLOCK;
+  extern __shared__ __align__(16) unsigned char smem[];   // k + 4 rank keys
+  __shared__ RadixScratch rs;
+  __shared__ SortScratch ss;
+  u64* buf = (u64*)smem;
+  const int64_t row = blockIdx.x;
+  const int t = (int)(row / a.s.Hq);
+  const int k = a.s.k;
+  // independent loads, issued together
+  const int status = *a.s.status;
+  const int p = a.s.q_pos[t];
+  const int n_raw = (int)*pf_count_of(a, row);
+  const float tau = a.tauf[row];
+  int32_t* orow = a.s.out_idx + (size_t)row * a.s.width;
+  float* srow = a.s.out_scores ? a.s.out_scores + (size_t)row * k : nullptr;
+  if (status != LSA_OK) {
+    write_invalid_row<BLOCK>(a.s.width, k, orow, srow);
+    if (a.s.out_leaves)
+      for (int i = threadIdx.x; i < a.s.nl_cap; i += BLOCK) a.s.out_leaves[(size_t)row * a.s.nl_cap + i] = -1;
+    return;
+  }
+  const bool valid_p = p >= 0 && (int64_t)p < a.s.N;
+  const int n_in = valid_p ? n_raw : 0;
+  const bool rescore = valid_p && ((int64_t)n_in > a.cap || (n_in < k && tau > -__builtin_huge_valf()));
+  if (rescore || n_in > CAP) {                     // block-uniform
+    if (threadIdx.x == 0) a.fb_rows[atomicAdd(a.fb_n, 1u)] = (uint32_t)row;
+    return;
+  }
+  if (a.s.out_leaves && !a.flat && threadIdx.x < 64) {
+    // the row's leaves in slot order, then -1 (wave 0; global writes only)
+    int32_t* ol = a.s.out_leaves + (size_t)row * a.s.nl_cap;
+    const int32_t* lfr = a.lf + (size_t)row * a.nl;
+    const int lane = threadIdx.x;
+    uint32_t base = 0;
+    for (int i0 = 0; i0 < a.nl; i0 += 64) {
+      const int leaf = i0 + lane < a.nl ? lfr[i0 + lane] : -1;
+      const u64 bal = __ballot(leaf >= 0);
+      if (leaf >= 0) ol[base + mbcnt64(bal)] = leaf;
+      base += (uint32_t)__popcll(bal);
+    }
+    for (int i = (int)base + lane; i < a.s.nl_cap; i += 64) ol[i] = -1;
+  }
+  if (!valid_p) {
+    write_invalid_row<BLOCK>(a.s.width, k, orow, srow);
+    return;
+  }
+  const u64* src = a.s.part_keys + (size_t)row * a.cap;
+  u64 pre[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int i = threadIdx.x + j * BLOCK;
+    pre[j] = i < n_in ? src[i] : 0ull;
+  }
+  const bool done = write_top_k_row<BLOCK, M, true>(buf, n_in, k, 0, p, a.s.sink, a.s.window, orow, srow, &rs, ss,
+                                                    nullptr, pre);
+  if (!done && threadIdx.x == 0) a.fb_rows[atomicAdd(a.fb_n, 1u)] = (uint32_t)row;   // an uneven index spread
 }
 
 // ---------------------------------------------------------------------------
@@ -1448,6 +1533,8 @@ struct PfWs {
   float* tauf;
   u64* part_keys;
   uint32_t* part_n;
+  uint32_t* fb_rows;
+  uint32_t* fb_n;
 };
 
 size_t carve_prefill(const lsa_index_desc& d, const PfPlan& pl, int64_t R, void* base, PfWs* out) {
@@ -1472,6 +1559,8 @@ size_t carve_prefill(const lsa_index_desc& d, const PfPlan& pl, int64_t R, void*
   w.tauf = c.take<float>((size_t)R);
   w.part_keys = c.take<u64>((size_t)(R * pl.cap));
   w.part_n = c.take<uint32_t>((size_t)R);
+  w.fb_rows = c.take<uint32_t>((size_t)R);
+  w.fb_n = c.take<uint32_t>(64);
   if (out) *out = w;
   return align_up(c.used);
 }
@@ -1485,13 +1574,26 @@ void launch_count_b(const PfArgs& a, int64_t grid, int be, hipStream_t st) {
   else hipLaunchKernelGGL((pf_level_count<DL, NT, 16>), dim3((unsigned)grid), dim3(kPfBlock), 0, st, a);
 }
 
+// The merge of the usual rows, then the block merge over the rows it left.
+// The usual-row merge holds M keys per thread for the tree (the block
+// merge's buffer; rows past it are rare) and 2M for the full scan, whose
+// threshold aims at 2k appended keys (4M per thread is 2k or more).
 template <int DL, int M>
 void launch_pf_merge(const PfArgs& a, hipStream_t st) {
+  if (a.R <= 0) return;
+  if (a.flat) {
+    constexpr int MF = 2 * M;
+    hipLaunchKernelGGL(pf_merge_fast<MF>, dim3((unsigned)a.R), dim3(kPfMergeBlock), ((size_t)a.s.k + 4) * 8, st, a);
+  } else {
+    hipLaunchKernelGGL(pf_merge_fast<M>, dim3((unsigned)a.R), dim3(kPfMergeBlock), ((size_t)a.s.k + 4) * 8, st, a);
+  }
   auto mk = pf_merge_kernel<DL, M>;
   const size_t lists = ((size_t)a.nl * 2 + 2) * 4;
   const size_t lds = (size_t)M * kPfMergeBlock * 8 + (lists > sizeof(SortScratch) ? lists : sizeof(SortScratch));
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)mk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(mk, dim3((unsigned)a.R), dim3(kPfMergeBlock), lds, st, a);
+  // a grid-stride loop over the list; its length is known only on the device
+  const int64_t grid = a.R < kPfMergeFbGrid ? a.R : kPfMergeFbGrid;
+  hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(kPfMergeBlock), lds, st, a);
 }
 
 template <typename KT, int DL>
@@ -1551,6 +1653,8 @@ int run_prefill(const lsa_index_desc& d, const lsa_select_params& p, const PfPla
   a.smp = w.smp;
   a.tauf = w.tauf;
   a.cap = pl.cap;
+  a.fb_rows = w.fb_rows;
+  a.fb_n = w.fb_n;
 
 #define PF_CHECK(what)                                                               \
   do {                                                                               \
@@ -1640,6 +1744,8 @@ struct FsWs {
   float* tauf;
   u64* part_keys;
   uint32_t* part_n;
+  uint32_t* fb_rows;
+  uint32_t* fb_n;
 };
 
 size_t carve_flat_tiled(const lsa_index_desc& d, const FsPlan& pl, int64_t R, void* base, FsWs* out) {
@@ -1651,6 +1757,8 @@ size_t carve_flat_tiled(const lsa_index_desc& d, const FsPlan& pl, int64_t R, vo
   w.tauf = c.take<float>((size_t)R);
   w.part_keys = c.take<u64>((size_t)(R * pl.cap));
   w.part_n = c.take<uint32_t>((size_t)R);
+  w.fb_rows = c.take<uint32_t>((size_t)R);
+  w.fb_n = c.take<uint32_t>(64);
   if (out) *out = w;
   return align_up(c.used);
 }
@@ -1700,6 +1808,8 @@ int run_flat_tiled(const lsa_index_desc& d, const lsa_select_params& p, const Fs
   a.fs_keys = pl.keys;
   a.fs_split = pl.split;
   a.fs_rb = pl.rb;
+  a.fb_rows = w.fb_rows;
+  a.fb_n = w.fb_n;
   set_header_check(s, d, L, index, w.status);
 
 #define FS_CHECK(what)                                                               \

@@ -108,3 +108,38 @@ def test_row_tiled_full_scan_on_oracle_index(case):
     assert np.all(fi[bad] == -1) and np.all(np.isneginf(fs[bad])), "invalid positions"
     fi2, fs2, _ = gpu_select(li, queries, pos, prm, flat=True)
     assert np.array_equal(fi, fi2) and np.array_equal(fs.view(np.uint32), fs2.view(np.uint32))
+
+
+def test_best_keys_in_one_run_of_positions():
+    """Every row's best keys are near-copies of one vector stored at 3000
+    consecutive positions, and every query is that vector plus noise, so the
+    kept keys crowd into a few of the 1024 index buckets (over [0, p]) that
+    the per-wave merge sorts by: more than 64 of them share a bucket, and the
+    rows are left to the block merge.  Both large-batch paths must still
+    match the oracle on every row."""
+    from synth.workloads import f32_to_bf16_bits
+    wl = _pf(n_keys=131072, n_kv_heads=1, n_centers=256, fanout=(16, 16), b=16, k=2048, window=512,
+             n_tokens=64)
+    keys, W = gen_keys(wl), gen_W(wl)
+    rng = np.random.default_rng(20261204)
+    base = 3.0 * rng.standard_normal(wl.d_head).astype(np.float32)
+    near = base + np.float32(0.05) * rng.standard_normal((3000, wl.d_head)).astype(np.float32)
+    keys[40000:43000, 0, :] = f32_to_bf16_bits(near)
+    q = base + np.float32(0.05) * rng.standard_normal((wl.n_tokens, wl.n_q_heads, wl.d_head)).astype(np.float32)
+    queries = f32_to_bf16_bits(q.astype(np.float32))
+    pos = np.arange(wl.n_keys - wl.n_tokens, wl.n_keys, dtype=np.int32)
+    desc = O.IndexDesc.of(wl)
+    oidx = O.build_index(keys, W, desc)
+    li = _li(desc, O.index_blob(oidx))
+    prm = O.SelectParams(wl.b, wl.k, wl.sink, wl.window)
+    A = _abi()
+    log(f"[clustered best keys] N={wl.n_keys} k={wl.k} T={wl.n_tokens} G={wl.group}")
+    assert A.select_path(li.desc, _params(prm), wl.n_tokens, wl.n_q_heads) == A.PATH_NODE_MAJOR
+    assert A.flat_select_path(li.desc, _params(prm), wl.n_tokens, wl.n_q_heads) == A.PATH_ROW_TILED
+    gi, gs, gl = gpu_select(li, queries, pos, prm)
+    compare_select(oidx, queries, pos, prm, gi, gs, gl, log=log)
+    fi, fs, _ = gpu_select(li, queries, pos, prm, flat=True)
+    compare_select(oidx, queries, pos, prm, fi, fs, flat=True, log=log)
+    # the kept keys really do crowd: most of every row comes from the run
+    top = fi[:, :, wl.sink:wl.sink + wl.k]
+    assert np.mean((top >= 40000) & (top < 43000)) > 0.9
