@@ -210,11 +210,35 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
     }
   }
   __syncthreads();
-  for (int ti = ch * kPfNW + w; ti < ntiles; ti += a.CH * kPfNW) {
+  // A wave's tiles are pipelined: the list entries (rows) two tiles ahead,
+  // and where the registers allow (BMAX <= 8) the rows' latents (the B
+  // operand) one tile ahead, so a tile's operands are in registers when its
+  // turn comes.  A tile past the end has no rows.
+  constexpr bool PREQ = BMAX <= 8;
+  const int stride = a.CH * kPfNW;
+  auto row_of = [&](int tt) {
+    const int r = tt * 32 + l32;
+    return (tt < ntiles && r < n) ? pf_entry(a, start + r, h).x : -1;
+  };
+  auto latents_of = [&](int row, uint4* q) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      q[s] = make_uint4(0u, 0u, 0u, 0u);
+      if (row >= 0) q[s] = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
+    }
+  };
+  int ti = ch * kPfNW + w;
+  int row_c = row_of(ti), row_n = row_of(ti + stride);
+  uint4 qc[KS];
+  if constexpr (PREQ) latents_of(row_c, qc);
+  for (; ti < ntiles; ti += stride) {
     const int r_in = ti * 32 + l32;
     const bool valid = r_in < n;
     const int64_t pos = start + r_in;
-    const int row = valid ? pf_entry(a, pos, h).x : -1;
+    uint4 qn[KS];
+    if constexpr (PREQ) latents_of(row_n, qn);
+    else latents_of(row_c, qc);
+    const int row_nn = row_of(ti + 2 * stride);
     v16f acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -222,9 +246,7 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) u = *(const uint4*)(a.qlat16 + (size_t)row * DL + 16 * s + 8 * half);
-      const v8s Bv = as_v8s(u);
+      const v8s Bv = as_v8s(qc[s]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[t][s], Bv, acc[t], 0, 0, 0);
     }
@@ -305,6 +327,12 @@ __global__ __launch_bounds__(kPfBlock) __attribute__((amdgpu_waves_per_eu(3))) v
         m &= m - 1ull;
       }
     }
+    if constexpr (PREQ) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qc[s] = qn[s];
+    }
+    row_c = row_n;
+    row_n = row_nn;
   }
   __syncthreads();
   if (threadIdx.x < F && lcnt[threadIdx.x] != 0u)
