@@ -29,10 +29,12 @@
 //                       atomic per row and writes them
 //   pf_tau_kernel       per row, a threshold from the weighted samples such
 //                       that about 1.5k candidates are expected above it
-//   pf_merge_kernel     per row, the exact best k of the appended keys and the
-//                       output row; a row whose threshold let fewer than k keys
-//                       through (or whose list overflowed) is scored again in
-//                       full from its leaf list
+//   pf_merge_fast       per row, the exact best k of the appended keys and the
+//                       output row, for the usual row (its keys fit the
+//                       registers, no re-score); any other row goes on a list
+//   pf_merge_kernel     the rows on that list: a row whose threshold let fewer
+//                       than k keys through (or whose list overflowed) is
+//                       scored again in full from its leaf list
 #include <limits.h>
 
 #include <type_traits>
