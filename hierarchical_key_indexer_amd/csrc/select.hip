@@ -1116,14 +1116,22 @@ __global__ __launch_bounds__(BLOCK) void merge_kernel(SelArgs a) {
   u64* buf = (u64*)smem;
   const int64_t qh = a.qh0 + blockIdx.x;
   const int t = (int)(qh / a.Hq);
-  // the list's first CAP places are loaded with its count (clamped into the
-  // query head's region of the workspace, masked by the count where used)
+  // the list's first CAP / 2 places are loaded together with its count
+  // (clamped into the query head's region of the workspace, masked by the
+  // count where used), the rest once the count is known and only up to it:
+  // a list usually holds about 2k keys, and loading all CAP places made the
+  // first barrier wait for twice the bytes
   const u64* src = a.part_keys + qh * a.part_cap;
   u64 pre[M];
 #pragma unroll
-  for (int j = 0; j < M; ++j) pre[j] = src[min((int64_t)threadIdx.x + (int64_t)j * BLOCK, a.part_cap - 1)];
+  for (int j = 0; j < M / 2; ++j) pre[j] = src[min((int64_t)threadIdx.x + (int64_t)j * BLOCK, a.part_cap - 1)];
   // these loads are independent as well: issue them together
   const int n_in = (int)a.part_n[qh];
+#pragma unroll
+  for (int j = M / 2; j < M; ++j) {
+    const int64_t i = (int64_t)threadIdx.x + (int64_t)j * BLOCK;
+    pre[j] = i < n_in ? src[min(i, a.part_cap - 1)] : 0ull;
+  }
   const u64 thr0 = a.tau ? a.tau[qh] : 0ull;
   const int p = a.q_pos[t];
   const int bad = *a.status;
