@@ -1115,15 +1115,14 @@ __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_kernel(PfArgs a) {
   }
 }
 
-
 // The usual row: its appended keys fit the registers (M per thread) and need
 // no re-score.  Same result as pf_merge_row with less than half of its LDS
 // and registers: the keys go from the list into registers, the selection
 // runs on them there, and only the k kept keys pass through LDS (bucketed by
-// index, then put in order in the same place), so seven rows fit a CU at
-// once instead of three.  A row it does not take (a
-// re-score, more keys than it holds, a bucket of more than 64 keys) goes to
-// the block merge's list before anything of its top-k part is written.
+// index, then put in order in the same place), so six rows fit a CU at once
+// (with M = 16) instead of three.  A row it does not take (a re-score, more
+// keys than it holds, a bucket of more than 64 keys) goes to the block
+// merge's list before anything of its top-k part is written.
 template <int M>
 __global__ __launch_bounds__(kPfMergeBlock) void pf_merge_fast(PfArgs a) {
   constexpr int BLOCK = kPfMergeBlock, CAP = M * BLOCK;
@@ -1607,7 +1606,7 @@ void launch_count_b(const PfArgs& a, int64_t grid, int be, hipStream_t st) {
 // The merge of the usual rows, then the block merge over the rows it left.
 // The usual-row merge holds M keys per thread for the tree (the block
 // merge's buffer; rows past it are rare) and 2M for the full scan, whose
-// threshold aims at 2k appended keys (4M per thread is 2k or more).
+// threshold aims at 2k appended keys: 2M per thread hold 4k keys or more.
 template <int DL, int M>
 void launch_pf_merge(const PfArgs& a, hipStream_t st) {
   if (a.R <= 0) return;
