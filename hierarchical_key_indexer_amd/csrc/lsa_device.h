@@ -552,46 +552,46 @@ __device__ bool write_top_k_row(u64* buf, int n, int k, int cap, int p, int sink
       }
     }
   } else {
-  const u64* sorted = buf;
-  if (ss.big) {
-    bitonic_sort_asc<BLOCK>(buf, nk, cap);
-  } else {
-    // cnt[b] is now the end of bucket b and its start is the end of b - 1;
-    // a key's position is its bucket's start plus the smaller keys in it.
-    // The keys land in buf[cap/2, cap/2 + nk) in order, so the row is
-    // written with coalesced stores
-    u64* out = buf + cap / 2;
-#pragma unroll
-    for (int j = 0; j < M; ++j)
-      if (v[j] != 0ull) {
-        const int b = bucket(v[j]);
-        const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
-        // indices are unique, so the high words alone order the keys; four
-        // independent reads per step (entries past e, still inside buf since
-        // nk + 3 < cap, are masked)
-        const uint32_t xi = (uint32_t)(v[j] >> 32);
-        const uint32_t* hw = (const uint32_t*)buf + 1;
-        int r = st;
-        for (int i = st; i < e; i += 4) {
-          const uint32_t y0 = hw[2 * i], y1 = hw[2 * i + 2], y2 = hw[2 * i + 4], y3 = hw[2 * i + 6];
-          r += (y0 < xi ? 1 : 0) + (i + 1 < e && y1 < xi ? 1 : 0) + (i + 2 < e && y2 < xi ? 1 : 0) +
-               (i + 3 < e && y3 < xi ? 1 : 0);
-        }
-        out[r] = v[j];
-      }
-    __syncthreads();
-    sorted = out;
-  }
-  for (int i = threadIdx.x; i < k; i += BLOCK) {
-    if (i < nk) {
-      const u64 key = sorted[i];
-      row[sink + i] = (int32_t)(key >> 32);
-      if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
+    const u64* sorted = buf;
+    if (ss.big) {
+      bitonic_sort_asc<BLOCK>(buf, nk, cap);
     } else {
-      row[sink + i] = -1;
-      if (scores_row) scores_row[i] = -__builtin_huge_valf();
+      // cnt[b] is now the end of bucket b and its start is the end of b - 1;
+      // a key's position is its bucket's start plus the smaller keys in it.
+      // The keys land in buf[cap/2, cap/2 + nk) in order, so the row is
+      // written with coalesced stores
+      u64* out = buf + cap / 2;
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (v[j] != 0ull) {
+          const int b = bucket(v[j]);
+          const int st = b == 0 ? 0 : (int)ss.cnt[b - 1], e = (int)ss.cnt[b];
+          // indices are unique, so the high words alone order the keys; four
+          // independent reads per step (entries past e, still inside buf since
+          // nk + 3 < cap, are masked)
+          const uint32_t xi = (uint32_t)(v[j] >> 32);
+          const uint32_t* hw = (const uint32_t*)buf + 1;
+          int r = st;
+          for (int i = st; i < e; i += 4) {
+            const uint32_t y0 = hw[2 * i], y1 = hw[2 * i + 2], y2 = hw[2 * i + 4], y3 = hw[2 * i + 6];
+            r += (y0 < xi ? 1 : 0) + (i + 1 < e && y1 < xi ? 1 : 0) + (i + 2 < e && y2 < xi ? 1 : 0) +
+                 (i + 3 < e && y3 < xi ? 1 : 0);
+          }
+          out[r] = v[j];
+        }
+      __syncthreads();
+      sorted = out;
     }
-  }
+    for (int i = threadIdx.x; i < k; i += BLOCK) {
+      if (i < nk) {
+        const u64 key = sorted[i];
+        row[sink + i] = (int32_t)(key >> 32);
+        if (scores_row) scores_row[i] = order_u32_to_f32((uint32_t)key);
+      } else {
+        row[sink + i] = -1;
+        if (scores_row) scores_row[i] = -__builtin_huge_valf();
+      }
+    }
   }
   const int ns = min(sink, p + 1);
   for (int i = threadIdx.x; i < sink; i += BLOCK) row[i] = i < ns ? i : -1;
